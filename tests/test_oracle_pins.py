@@ -1,0 +1,569 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (no GPU).
+
+Each test checks the oracle against something other than itself: a library routine
+(torch / numpy format conversions), a closed form, an exact-arithmetic grid on which
+quantized attention equals textbook FP64 attention, brute-force group enumeration from
+the layout descriptions, or an invariant (power-of-two scaling, rotation norms,
+permutations). A plausible slip in the oracle (a dropped term, a wrong sign, index or
+operand) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(bits):
+    return gen.from_bf16_bits(bits)
+
+
+# ----------------------------------------------------------------------------- number formats
+def test_bf16_rounding_matches_torch():
+    g = np.random.default_rng(1)
+    x = np.concatenate([g.standard_normal(4000).astype(np.float32) * 10.0 ** g.integers(-30, 30, 4000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 3.4e38, 1e-40], np.float32)])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    got = np.array([O.bf16_round(float(v)) for v in x], np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_f16_matches_numpy():
+    g = np.random.default_rng(2)
+    x = np.concatenate([g.standard_normal(3000).astype(np.float32) * 10.0 ** g.integers(-9, 5, 3000),
+                        np.array([65504.0, 65519.0, 65520.0, 1e-8, 2.0 ** -24, 3 * 2.0 ** -25], np.float32)])
+    ref = x.astype(np.float16).view(np.uint16)
+    got = np.array([O.f32_to_f16(float(v)) for v in x], np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    for h in range(0, 65536, 97):
+        want = np.array([h], np.uint16).view(np.float16).astype(np.float64)[0]
+        v = O.f16_value(h)
+        assert (math.isnan(v) and math.isnan(want)) or v == want
+
+
+def test_e4m3_matches_torch_and_spec():
+    g = np.random.default_rng(3)
+    x = g.standard_normal(5000).astype(np.float32) * np.float32(2.0) ** g.integers(-12, 9, 5000).astype(np.float32)
+    x = x[np.abs(x) < 448.0]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.f32_to_e4m3(float(v)) for v in x], np.uint8)
+    np.testing.assert_array_equal(got, ref)
+    for b in range(256):
+        want = torch.tensor([b], dtype=torch.uint8).view(torch.float8_e4m3fn).float().item()
+        v = O.e4m3_value(b)
+        assert (math.isnan(v) and math.isnan(want)) or v == want
+    # saturation at the largest normal (the quantizer divides by amax / 448)
+    assert O.f32_to_e4m3(448.0 * (1 + 2 ** -20)) == 0x7E and O.f32_to_e4m3(-1000.0) == 0xFE
+    with open(os.path.join(GOLDEN, "e4m3_encodings.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            val, byte = line.split()
+            assert O.f32_to_e4m3(float(val)) == int(byte, 16), line
+
+
+# ----------------------------------------------------------------------------- scale layouts
+def _members(layout, T):
+    """Row groups from the layout descriptions: per block, eight scales per 32 rows (rows r, r+8, r+16,
+    r+24), four scales per 64 rows (row pairs repeating every 8 rows), four per 128 rows (32 consecutive
+    rows each)."""
+    groups = {}
+    if layout == O.LAYOUT_THREAD_Q:
+        for blk in range((T + 127) // 128 * 4):
+            for r in range(8):
+                groups[8 * blk + r] = [32 * blk + r + 8 * i for i in range(4)]
+    elif layout == O.LAYOUT_THREAD_K:
+        for blk in range((T + 63) // 64):
+            for pair in range(4):
+                groups[4 * blk + pair] = [64 * blk + 8 * m + 2 * pair + e for m in range(8) for e in range(2)]
+    elif layout == O.LAYOUT_WARP_Q:
+        for blk in range((T + 127) // 128):
+            for w in range(4):
+                groups[4 * blk + w] = list(range(128 * blk + 32 * w, 128 * blk + 32 * w + 32))
+    return groups
+
+
+@pytest.mark.parametrize("layout,block", [(O.LAYOUT_THREAD_Q, 32), (O.LAYOUT_THREAD_K, 64), (O.LAYOUT_WARP_Q, 128),
+                                          (O.LAYOUT_PER_BLOCK, 64), (O.LAYOUT_PER_BLOCK, 128), (O.LAYOUT_PER_BLOCK, 32)])
+def test_group_membership_by_enumeration(layout, block):
+    T, D = 300, 64
+    # row t holds the constant (t + 1) / 512 (exact in bf16 for t < 256 ... powers ok: compare in float)
+    vals = (np.arange(T, dtype=np.float32) + 1) / 512.0
+    x = gen.to_bf16_bits(np.broadcast_to(vals[None, :, None, None], (1, T, 1, D)))
+    xv = f32(x)[0, :, 0, 0]
+    codes, scales = O.quant_qk(x, O.Prologue(), layout, block, scale_eps=0.0)
+    if layout == O.LAYOUT_PER_BLOCK:
+        groups = {g: list(range(g * block, min(T, (g + 1) * block))) for g in range((T + block - 1) // block)}
+    else:
+        groups = _members(layout, T)
+    assert scales.shape[-1] == len(groups) == O.scale_count(T, layout, block)
+    for g, rows in groups.items():
+        rows = [t for t in rows if t < T]
+        amax = np.float32(max([xv[t] for t in rows], default=0.0))
+        assert scales[0, 0, g] == np.float32(amax / np.float32(127.0)), (g, rows)
+        for t in rows:
+            assert O.scale_index(t, layout, block) == g
+
+
+def test_thread_q_tail_groups_get_eps():
+    T, D = 40, 64
+    x = gen.normal_bf16((1, T, 2, D), gen.rng(7, 0))
+    _, scales = O.quant_qk(x, O.Prologue(), O.LAYOUT_THREAD_Q, 32, scale_eps=1e-7)
+    assert scales.shape[-1] == 32           # 40 tokens padded to 128 rows: 4 blocks x 8 scales
+    np.testing.assert_array_equal(scales[:, :, 16:], np.float32(1e-7))
+    assert np.all(scales[:, :, 8:16] > 1e-3) and np.all(scales[:, :, :8] > 1e-3)
+
+
+# ----------------------------------------------------------------------------- quantizer arithmetic
+@pytest.mark.parametrize("layout,block", [(0, 64), (1, 32), (2, 64), (3, 128)])
+def test_absmax_int8_properties(layout, block):
+    """Quantization-only mode is symmetric absmax INT8 of the bf16 rows times sm_scale."""
+    x = gen.normal_bf16((2, 200, 3, 64), gen.rng(11, layout))
+    sm = 0.3
+    codes, scales = O.quant_qk(x, O.Prologue(), layout, block, sm_scale=sm, scale_eps=0.0)
+    v = f32(x) * np.float32(sm)
+    assert np.abs(codes.astype(np.int32)).max() <= 127
+    idx = np.array([O.scale_index(t, layout, block) for t in range(200)])
+    s = scales[:, :, idx].transpose(0, 2, 1)[..., None]             # (B, T, H, 1)
+    err = np.abs(codes.astype(np.float64) * s - v)
+    assert np.all(err <= s * (0.5 + 1e-5))
+    # the largest element of every (nonempty) group reaches +-127
+    for b in range(2):
+        for h in range(3):
+            for g in np.unique(idx):
+                rows = np.nonzero(idx == g)[0]
+                assert np.abs(codes[b, rows, h].astype(np.int32)).max() == 127
+
+
+def test_half_away_from_zero_on_exact_ties():
+    D = 64
+    # scale 2^-4 exactly (amax 127 * 2^-4), values k/16 + 1/32: ties at k + 0.5
+    k = np.arange(-126, 127, dtype=np.float32)
+    vals = np.concatenate([[127 / 16.0], (k + 0.5) / 16.0])[:D * 3]
+    vals = np.resize(vals, (3 * D,)).reshape(3, D).astype(np.float32)
+    vals[0, 0] = 127 / 16.0
+    x = gen.to_bf16_bits(vals[None, :, None, :])
+    xv = f32(x)[0, :, 0, :]
+    codes, scales = O.quant_qk(x, O.Prologue(), O.LAYOUT_PER_BLOCK, 64, scale_eps=0.0)
+    assert scales[0, 0, 0] == np.float32(1 / 16.0)
+    r = xv * 16.0
+    want = np.sign(r) * np.floor(np.abs(r) + 0.5)
+    np.testing.assert_array_equal(codes[0, :, 0, :], want.astype(np.int8))
+
+
+def test_norm_matches_fp64_rmsnorm_and_power_of_two_invariance():
+    B, T, H, D = 1, 64, 2, 128
+    x = gen.normal_bf16((B, T, H, D), gen.rng(12, 0))
+    w = gen.uniform_bf16((1, D), gen.rng(12, 1))
+    pro = O.Prologue(norm=O.NORM_HEAD, weight=w, eps=1e-6)
+    y = O.prologue_rows(x, pro)
+    xv = f32(x).astype(np.float64)
+    ref = xv / np.sqrt((xv ** 2).mean(-1, keepdims=True) + 1e-6) * f32(w)[0].astype(np.float64)
+    np.testing.assert_allclose(y, ref, rtol=2 ** -8, atol=1e-6)    # bf16 output rounding
+    # eps = 0: scaling the input by 2^k leaves the normalized rows (and codes) bit-identical
+    pro0 = O.Prologue(norm=O.NORM_HEAD, weight=w, eps=0.0)
+    x2 = gen.to_bf16_bits(f32(x) * np.float32(8.0))
+    for layout, block in [(0, 64), (1, 32)]:
+        c1, s1 = O.quant_qk(x, pro0, layout, block)
+        c2, s2 = O.quant_qk(x2, pro0, layout, block)
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(s1, s2)
+    # unit weight: unit RMS up to bf16 rounding
+    ones = gen.to_bf16_bits(np.ones((1, D), np.float32))
+    y1 = O.prologue_rows(x, O.Prologue(norm=O.NORM_HEAD, weight=ones, eps=0.0))
+    np.testing.assert_allclose(np.sqrt((y1.astype(np.float64) ** 2).mean(-1)), 1.0, rtol=3e-3)
+
+
+def test_all_heads_mean_squares_and_norm():
+    B, T, H, D = 2, 20, 5, 64
+    x = gen.normal_bf16((B, T, H, D), gen.rng(13, 0))
+    ms = O.mean_sq_all_heads(x)
+    xv = f32(x).astype(np.float64)
+    np.testing.assert_allclose(ms, (xv ** 2).mean(axis=(2, 3)), rtol=1e-6)
+    w = gen.uniform_bf16((1, H * D), gen.rng(13, 1))
+    y = O.prologue_rows(x, O.Prologue(norm=O.NORM_ALL_HEADS, weight=w, eps=1e-6))
+    ref = xv / np.sqrt((xv ** 2).mean(axis=(2, 3), keepdims=True) + 1e-6) * f32(w)[0].reshape(H, D)
+    np.testing.assert_allclose(y, ref, rtol=2 ** -8, atol=1e-6)
+
+
+def test_segmented_weight_rows():
+    B, T, H, D = 1, 16, 2, 64
+    x = gen.normal_bf16((B, T, H, D), gen.rng(14, 0))
+    w = gen.uniform_bf16((2, D), gen.rng(14, 1))
+    rows = np.array([0] * 5 + [1] * 11, np.int32)
+    y = O.prologue_rows(x, O.Prologue(norm=O.NORM_HEAD, weight=w, weight_rows=rows))
+    for r, sl in ((0, slice(0, 5)), (1, slice(5, 16))):
+        yr = O.prologue_rows(x[:, sl], O.Prologue(norm=O.NORM_HEAD, weight=w[r:r + 1]))
+        np.testing.assert_array_equal(y[:, sl], yr)
+
+
+def test_rope_is_complex_rotation():
+    B, T, H, D = 1, 50, 2, 128
+    x = gen.normal_bf16((B, T, H, D), gen.rng(15, 0))
+    tb = gen.rope_table(T, D // 2, start=3)
+    z = O.prologue_rows(x, O.Prologue(rope=O.ROPE_SPLIT_HALF, table=tb)).astype(np.float64)
+    xv = f32(x).astype(np.float64)
+    P = D // 2
+    c = (xv[..., :P] + 1j * xv[..., P:]) * (tb[0, :, 0, :, 0] + 1j * tb[0, :, 0, :, 1])[None, :, None, :]
+    np.testing.assert_allclose(z[..., :P], c.real, atol=1e-5)
+    np.testing.assert_allclose(z[..., P:], c.imag, atol=1e-5)
+    # interleaved pairs (2p, 2p+1): the same rotation under the channel permutation
+    perm = np.stack([np.arange(P), np.arange(P) + P], -1).reshape(-1)
+    xi = np.ascontiguousarray(x[..., perm])
+    zi = O.prologue_rows(xi, O.Prologue(rope=O.ROPE_INTERLEAVED, table=tb))
+    np.testing.assert_array_equal(zi, z.astype(np.float32)[..., perm])
+    # the 2x2 matrix form of the table [[cos, -sin], [sin, cos]] reads the same cos / sin
+    m = np.stack([np.stack([tb[..., 0], -tb[..., 1]], -1), np.stack([tb[..., 1], tb[..., 0]], -1)], -2)
+    zm = O.prologue_rows(x, O.Prologue(rope=O.ROPE_SPLIT_HALF, table=np.ascontiguousarray(m)))
+    np.testing.assert_array_equal(zm, z.astype(np.float32))
+    # cos = 1, sin = 0 is the identity; partial rotation leaves channels >= 2 * pairs untouched
+    ident = np.ascontiguousarray(np.stack([np.ones((1, T, 1, 16)), np.zeros((1, T, 1, 16))], -1).astype(np.float32))
+    zid = O.prologue_rows(x, O.Prologue(rope=O.ROPE_SPLIT_HALF, table=ident))
+    np.testing.assert_array_equal(zid, f32(x))
+    zp = O.prologue_rows(x, O.Prologue(rope=O.ROPE_SPLIT_HALF, table=np.ascontiguousarray(tb[:, :, :, :16])))
+    np.testing.assert_array_equal(zp[..., 32:], f32(x)[..., 32:])
+    # rotation keeps pair norms
+    n0 = xv[..., :P] ** 2 + xv[..., P:] ** 2
+    n1 = z[..., :P] ** 2 + z[..., P:] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-6, atol=1e-12)
+
+
+def test_kmean_matches_fp64_mean():
+    B, T, H, D = 2, 333, 3, 64
+    x = gen.normal_bf16((B, T, H, D), gen.rng(16, 0))
+    w = gen.uniform_bf16((1, D), gen.rng(16, 1))
+    pro = O.Prologue(norm=O.NORM_HEAD, weight=w, rope=O.ROPE_SPLIT_HALF, table=gen.rope_table(T, D // 2))
+    mu = O.kmean(x, pro)
+    z = O.prologue_rows(x, pro).astype(np.float64)
+    ref = z.mean(axis=1)
+    np.testing.assert_allclose(mu, ref, rtol=1e-5, atol=1e-7)
+    # the mean subtracted by the quantizer: quantizing (x, mean) equals quantizing the centred rows
+    codes, _ = O.quant_qk(x, pro, 0, 64, mean=mu, scale_eps=0.0)
+    zc = O.prologue_rows(x, pro, mean=mu)
+    np.testing.assert_array_equal(zc, (z.astype(np.float32) - mu[:, None]).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- attention core
+def _grid_qk(g, B, S, H, D, block, int_scale):
+    """Codes with a power-of-two per-block scale: dequantized values are exact."""
+    codes = g.integers(-6, 7, size=(B, S, H, D)).astype(np.int8)
+    n = (S + block - 1) // block
+    scales = np.full((B, H, n), int_scale, np.float32)
+    return O.QK(codes, scales, O.LAYOUT_PER_BLOCK, block)
+
+
+def _ref_attention_base2(q, k, v, G):
+    """Textbook attention with base-2 scores s = qh . kh, FP64, GQA kv head h // G."""
+    qh = q.codes.astype(np.float64) * np.repeat(q.scales, q.block, axis=2)[:, :, :q.codes.shape[1]].transpose(0, 2, 1)[..., None]
+    kh = k.codes.astype(np.float64) * np.repeat(k.scales, k.block, axis=2)[:, :, :k.codes.shape[1]].transpose(0, 2, 1)[..., None]
+    B, Sq, H, D = q.codes.shape
+    out = np.zeros((B, Sq, H, D))
+    lse = np.zeros((B, H, Sq))
+    for b in range(B):
+        for h in range(H):
+            s = qh[b, :, h] @ kh[b, :, h // G].T
+            m = s.max(-1, keepdims=True)
+            p = np.exp2(s - m)
+            out[b, :, h] = (p @ v[b, :, h // G]) / p.sum(-1, keepdims=True)
+            lse[b, h] = m[:, 0] + np.log2(p.sum(-1))
+    return out, lse
+
+
+@pytest.mark.parametrize("kv_tile", [64, 128])
+def test_attention_exact_on_integer_score_grid_bf16(kv_tile):
+    """Integer scores make every p a power of two (exact in bf16) and every P.V term exact:
+    the quantized core must equal textbook FP64 attention."""
+    g = np.random.default_rng(21)
+    B, Sq, Sk, H, Hk, D = 1, 70, 200, 4, 2, 64
+    q = _grid_qk(g, B, Sq, H, D, 64, 0.25)
+    k = _grid_qk(g, B, Sk, Hk, D, 64, 0.25)          # c = 1/16, scores = dot / 16
+    q.codes[..., :] = (q.codes // 2) * 2
+    k.codes[..., :] = (k.codes // 2) * 2              # even codes: dot divisible by 4 ... scores in Z/4
+    q.scales[:] = 0.5
+    k.scales[:] = 0.5                                  # c = 1/4: s = dot/4, dot = 4 * integer
+    vb = g.integers(-8, 9, size=(B, Sk, Hk, D)).astype(np.float32) / 4
+    v = gen.to_bf16_bits(vb)
+    out, lse, allow = O.attn(q, k, v, fp8=False, kv_tile=kv_tile)
+    ref, rlse = _ref_attention_base2(q, k, f32(v).astype(np.float64), H // Hk)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_exact_on_grid_fp8():
+    g = np.random.default_rng(22)
+    B, Sq, Sk, H, D = 1, 40, 256, 2, 64
+    q = _grid_qk(g, B, Sq, H, D, 64, 0.5)
+    k = _grid_qk(g, B, Sk, H, D, 64, 0.5)
+    # q codes +-2 on 4 channels, k codes in {-2, 0, 2}, c = 1/4: integer scores in [-4, 4]
+    q.codes[:] = 0
+    for i in range(Sq):
+        for h in range(H):
+            ch = g.choice(D, 4, replace=False)
+            q.codes[0, i, h, ch] = g.choice([-2, 2], 4)
+    k.codes[:] = g.integers(-1, 2, size=k.codes.shape) * 2
+    v8 = g.integers(-7, 8, size=(B, Sk, H, D)).astype(np.float32)   # e4m3-exact integers
+    codes = np.vectorize(O.f32_to_e4m3)(v8).astype(np.uint8)
+    vs = np.full((B, H, D), 0.125, np.float32)
+    out, lse, _ = O.attn(q, k, codes, fp8=True, vs=vs, kv_tile=128)
+    ref, rlse = _ref_attention_base2(q, k, v8.astype(np.float64) * 0.125, 1)
+    # p = 2^-n is e4m3-exact while 256 p >= 2^-9, i.e. n <= 17: scores span 8
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    g = np.random.default_rng(23)
+    B, S, H, D = 1, 1, 2, 64
+    q = O.QK(g.integers(-127, 128, size=(B, 3, H, D)).astype(np.int8), np.full((B, H, 1), 0.01, np.float32), 0, 64)
+    k = O.QK(g.integers(-127, 128, size=(B, S, H, D)).astype(np.int8), np.full((B, H, 1), 0.02, np.float32), 0, 64)
+    v = gen.normal_bf16((B, S, H, D), g)
+    out, lse, _ = O.attn(q, k, v, fp8=False)
+    # one key: a one-element softmax is one up to the exponent's fused residual r = a*c - RN(a*c),
+    # |r| <= ulp(s)/2, so p = 2^r, bf16(p) == 1 and out = v / p
+    dots = np.einsum("bihd,bjhd->bhi", q.codes.astype(np.int64), k.codes.astype(np.int64))
+    smax = np.abs(dots).max() * float(np.float32(0.01) * np.float32(0.02))
+    np.testing.assert_allclose(out, np.broadcast_to(f32(v).astype(np.float64), out.shape), rtol=smax * 2.0 ** -24,
+                               atol=0)
+    np.testing.assert_allclose(lse, dots * float(np.float32(0.01) * np.float32(0.02)), rtol=1e-6)
+    # q = 0: every score is 0 -> uniform weights, out = mean of v
+    Sk = 96
+    k = O.QK(g.integers(-127, 128, size=(B, Sk, H, D)).astype(np.int8), np.full((B, H, 2), 0.02, np.float32), 0, 64)
+    v = gen.normal_bf16((B, Sk, H, D), g)
+    q0 = O.QK(np.zeros((B, 5, H, D), np.int8), np.full((B, H, 1), 0.01, np.float32), 0, 64)
+    out, lse, _ = O.attn(q0, k, v, fp8=False, kv_tile=64)
+    np.testing.assert_allclose(out, np.broadcast_to(f32(v).astype(np.float64).mean(1, keepdims=True), out.shape),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, math.log2(Sk), rtol=1e-12)
+
+
+def test_attention_close_to_dequantized_fp64_and_flip_allowance():
+    """Off the grid the only quantized-mode deviation from FP64 attention over the dequantized q, k is the
+    rounding of P to bf16: bounded by 2^-8 of the largest |v|; the flip allowance is 0 when p is exact."""
+    g = np.random.default_rng(24)
+    B, Sq, Sk, H, D = 1, 33, 300, 2, 64
+    q = O.QK(g.integers(-127, 128, size=(B, Sq, H, D)).astype(np.int8), g.uniform(0.001, 0.003, (B, H, 1)).astype(np.float32), 0, 64)
+    k = O.QK(g.integers(-127, 128, size=(B, Sk, H, D)).astype(np.int8), g.uniform(0.001, 0.003, (B, H, 5)).astype(np.float32), 0, 64)
+    v = gen.normal_bf16((B, Sk, H, D), g)
+    out, lse, allow = O.attn(q, k, v, fp8=False, kv_tile=64)
+    vv = f32(v).astype(np.float64)
+    qh = q.codes.astype(np.float64) * q.scales[:, :, 0][:, None, :, None]
+    kh = k.codes.astype(np.float64) * np.repeat(k.scales, 64, axis=2)[:, :, :Sk].transpose(0, 2, 1)[..., None]
+    for h in range(H):
+        s = qh[0, :, h] @ kh[0, :, h].T
+        p = np.exp2(s - s.max(-1, keepdims=True))
+        ref = p @ vv[0, :, h] / p.sum(-1, keepdims=True)
+        assert np.abs(out[0, :, h] - ref).max() <= 2 ** -8 * np.abs(vv).max()
+        np.testing.assert_allclose(lse[0, h], np.log2(np.exp2(s).sum(-1)), rtol=1e-6)
+    assert np.all(allow >= 0)
+    _, _, allow0 = O.attn(q, k, v, fp8=False, kv_tile=64, flip_rel=0.0)
+    assert np.all(allow0 == 0)
+
+
+def test_gqa_head_mapping():
+    g = np.random.default_rng(25)
+    B, S, H, Hk, D = 1, 16, 6, 2, 64
+    q = O.QK(g.integers(-127, 128, size=(B, 4, H, D)).astype(np.int8), np.full((B, H, 1), 0.01, np.float32), 0, 64)
+    k = O.QK(g.integers(-127, 128, size=(B, S, Hk, D)).astype(np.int8), np.full((B, Hk, 1), 0.01, np.float32), 0, 64)
+    vals = np.zeros((B, S, Hk, D), np.float32)
+    vals[:, :, 0] = 3.0
+    vals[:, :, 1] = -5.0
+    out, _, _ = O.attn(q, k, gen.to_bf16_bits(vals), fp8=False)
+    # kv head of q head h is h // (H / Hk): heads 0..2 -> 3, heads 3..5 -> -5
+    # (sum of bf16(p) over sum of p: within a bf16 rounding of the constant)
+    np.testing.assert_allclose(out[0, :, :3], 3.0, rtol=2.0 ** -8)
+    np.testing.assert_allclose(out[0, :, 3:], -5.0, rtol=2.0 ** -8)
+
+
+# ----------------------------------------------------------------------------- prefix pass + merge
+def test_prefix_merge_equals_single_pass_over_joined_keys():
+    """On an integer-score grid the two-pass merge equals one softmax over [prefix keys, projected keys],
+    the projected keys having been smoothed by mu (their pass misses q . mu; the prefix pass subtracts it)."""
+    g = np.random.default_rng(31)
+    B, Sq, Sk, P, H, D = 1, 20, 64, 96, 2, 64
+    q = O.QK(((g.integers(-3, 4, size=(B, Sq, H, D))) * 2).astype(np.int8), np.full((B, H, 1), 0.5, np.float32), 0, 64)
+    k = O.QK(((g.integers(-3, 4, size=(B, Sk, H, D))) * 2).astype(np.int8), np.full((B, H, 1), 0.5, np.float32), 0, 64)
+    mu = (g.integers(-1, 2, size=(B, H, D)) * 4).astype(np.float32)   # q . mu integer
+    vb = gen.to_bf16_bits(g.integers(-8, 9, size=(B, Sk, H, D)).astype(np.float32) / 4)
+    out_a, lse_a, _ = O.attn(q, k, vb, fp8=False, kv_tile=64)
+    pk = ((g.integers(-3, 4, size=(1, P, H, D))) * 2).astype(np.int8)
+    ks = gen.to_f16_bits(np.full((1, P, H, D // 32), 0.5, np.float32))
+    pv = g.integers(-16, 17, size=(1, P, H, D)).astype(np.int8)
+    vs = gen.to_f16_bits(np.full((1, P, H, D // 32), 0.25, np.float32))
+    pf = O.Q8Prefix(pk, ks, pv, vs)
+    out, lse, allow = O.prefix_merge(q, pf, mu, out_a.astype(np.float32), lse_a.astype(np.float32), kv_tile=64)
+    # single pass in FP64: scores q_hat . key with key = prefix (raw) or projected (k_hat + mu)
+    qh = q.codes.astype(np.float64) * 0.5
+    kh = k.codes.astype(np.float64) * 0.5 + mu[:, None].astype(np.float64)
+    keys = np.concatenate([pk.astype(np.float64) * 0.5, kh], axis=1)
+    vals = np.concatenate([pv.astype(np.float64) * 0.25, f32(vb).astype(np.float64)], axis=1)
+    for h in range(H):
+        s = qh[0, :, h] @ keys[0, :, h].T
+        p = np.exp2(s - s.max(-1, keepdims=True))
+        ref = p @ vals[0, :, h] / p.sum(-1, keepdims=True)
+        np.testing.assert_allclose(out[0, :, h], ref, rtol=1e-5, atol=1e-5)
+        off = qh[0, :, h] @ mu[0, h].astype(np.float64)
+        np.testing.assert_allclose(lse[0, h], np.log2(np.exp2(s - off[:, None]).sum(-1)), rtol=1e-5)
+    assert np.all(allow == 0)          # all p are powers of two: no flip possible
+
+
+def test_merge_is_symmetric_and_degenerate():
+    g = np.random.default_rng(32)
+    B, Sq, H, D = 1, 8, 2, 64
+    q = O.QK(g.integers(-127, 128, size=(B, Sq, H, D)).astype(np.int8), np.full((B, H, 1), 0.004, np.float32), 0, 64)
+    pk, ks = O.q8_quantize(g.standard_normal((1, 50, H, D)).astype(np.float32))
+    pv, vs = O.q8_quantize(g.standard_normal((1, 50, H, D)).astype(np.float32))
+    pf = O.Q8Prefix(pk, ks, pv, vs)
+    other = g.standard_normal((B, Sq, H, D)).astype(np.float32)
+    # an empty other pass (lse = -inf) leaves the prefix pass alone
+    out, lse, _, po, pl = O.prefix_merge(q, pf, None, other, np.full((B, H, Sq), -np.inf, np.float32), want_parts=True)
+    np.testing.assert_allclose(out, po, rtol=1e-12)
+    np.testing.assert_allclose(lse, pl, rtol=1e-12)
+    # merging with an equal-lse pass averages the two outputs
+    out2, lse2, _ = O.prefix_merge(q, pf, None, po.astype(np.float32), pl.astype(np.float32))
+    np.testing.assert_allclose(out2, po.astype(np.float32).astype(np.float64) * 0.5 + po * 0.5, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(lse2, pl + 1.0, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- q8 format
+def test_q8_quantizer():
+    g = np.random.default_rng(41)
+    x = g.standard_normal((100, 128)).astype(np.float32) * 3
+    x[0, :32] = 0.0
+    codes, sc = O.q8_quantize(x)
+    s32 = np.maximum(np.abs(x.reshape(100, 4, 32)).max(-1) / np.float32(127.0), np.float32(1e-8)).astype(np.float32)
+    np.testing.assert_array_equal(sc, s32.astype(np.float16).view(np.uint16))
+    assert np.abs(codes.astype(np.int32)).max() <= 127
+    err = np.abs(codes.reshape(100, 4, 32) * s32[..., None].astype(np.float64) - x.reshape(100, 4, 32))
+    assert np.all(err <= s32[..., None] * 0.5 * (1 + 1e-6))
+    assert np.all(np.abs(codes.reshape(100, 4, 32)).max(-1)[1:] == 127)
+    # ties round half to even: scale 1 (amax 127), values k + 0.5
+    t = np.zeros((1, 32), np.float32)
+    t[0, 0] = 127.0
+    t[0, 1:9] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 10.5, 11.5]
+    c, _ = O.q8_quantize(t)
+    assert c[0, :9].tolist() == [127, 0, 2, 2, 0, -2, -2, 10, 12]
+
+
+# ----------------------------------------------------------------------------- paged decode
+def _paged_case(g, N=3, Hq=8, Hk=2, D=64, bs=16, lens=(1, 17, 40)):
+    pages = [(L + bs - 1) // bs for L in lens]
+    NB = sum(pages) + 2
+    kc, ks = O.q8_quantize(g.standard_normal((NB, bs, Hk, D)).astype(np.float32))
+    vc, vs = O.q8_quantize(g.standard_normal((NB, bs, Hk, D)).astype(np.float32))
+    perm = g.permutation(NB)
+    bt = np.full((N, 8), -1, np.int32)
+    o = 0
+    for n, p in enumerate(pages):
+        bt[n, :p] = perm[o:o + p]
+        o += p
+    q = gen.normal_bf16((N, 1, Hq, D), g).reshape(N, Hq, D)
+    return q, kc, ks, vc, vs, bt, np.array(lens, np.int32)
+
+
+def test_paged_decode_equals_contiguous_attention():
+    """The paged decode over a block table equals unpaged attention over the gathered keys (a different
+    path of the oracle), with the q8 values exact in bf16 (power-of-two scales)."""
+    g = np.random.default_rng(51)
+    q, kc, ks, vc, vs, bt, lens = _paged_case(g)
+    ks[:] = gen.to_f16_bits(np.full(ks.shape, 2.0 ** -5, np.float32))
+    vs[:] = gen.to_f16_bits(np.full(vs.shape, 2.0 ** -4, np.float32))
+    scale = 1 / math.sqrt(64)
+    out = O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale)
+    for n, L in enumerate(lens):
+        pages = bt[n, :(L + 15) // 16]
+        kseq = (kc[pages].reshape(-1, 2, 64)[:L].astype(np.float32) * 2.0 ** -5)[None]
+        vseq = (vc[pages].reshape(-1, 2, 64)[:L].astype(np.float32) * 2.0 ** -4)[None]
+        ref = O.attn_exact(q[n][None, None], O.Prologue(), gen.to_bf16_bits(kseq), O.Prologue(), gen.to_bf16_bits(vseq))
+        np.testing.assert_allclose(out[n], ref[0, 0], rtol=1e-12, atol=1e-12)
+    # one key (L = 1): out = v
+    np.testing.assert_allclose(out[0], np.repeat(vc[bt[0, 0], 0].astype(np.float64) * 2.0 ** -4, 4, axis=0),
+                               rtol=1e-15)
+
+
+def test_paged_decode_block_permutation_invariance_and_dominant_key():
+    g = np.random.default_rng(52)
+    q, kc, ks, vc, vs, bt, lens = _paged_case(g)
+    out = O.paged_decode(q, kc, ks, vc, vs, bt, lens, 0.125)
+    NB = kc.shape[0]
+    perm = g.permutation(NB)
+    inv = np.argsort(perm)
+    bt2 = np.where(bt >= 0, inv[np.maximum(bt, 0)], -1).astype(np.int32)
+    out2 = O.paged_decode(q, kc[perm], ks[perm], vc[perm], vs[perm], bt2, lens, 0.125)
+    np.testing.assert_array_equal(out, out2)
+    # a key far above the rest takes all the weight: out equals its value exactly
+    n, pos = 2, 29
+    phys, slot = bt[n, pos // 16], pos % 16
+    q = q.copy()
+    q[n, 1:4] = q[n, 0]                # the q heads of a kv head share one query here
+    q[n, 5:8] = q[n, 4]
+    kc2 = kc.copy()
+    qv = gen.from_bf16_bits(q[n])
+    kc2[phys, slot, 0] = (np.sign(qv[0]) * 127).astype(np.int8)
+    kc2[phys, slot, 1] = (np.sign(qv[4]) * 127).astype(np.int8)
+    ks2 = ks.copy()
+    ks2[phys, slot] = gen.to_f16_bits(np.full((2, 2), 60.0, np.float32))
+    out3 = O.paged_decode(q, kc2, ks2, vc, vs, bt, lens, 0.125)
+    vexact = vc[phys, slot].astype(np.float64) * np.repeat(
+        np.array([O.f16_value(int(h)) for h in vs[phys, slot].reshape(-1)]).reshape(2, 2), 32, axis=1)
+    np.testing.assert_allclose(out3[n, :4], np.broadcast_to(vexact[0], (4, 64)), rtol=1e-12)
+    np.testing.assert_allclose(out3[n, 4:], np.broadcast_to(vexact[1], (4, 64)), rtol=1e-12)
+
+
+def test_exact_attention_shift_invariance_of_k():
+    """Subtracting a per-head constant from every key leaves attention unchanged (why k may be smoothed)."""
+    g = np.random.default_rng(53)
+    B, S, H, D = 1, 40, 2, 64
+    q = gen.normal_bf16((B, S, H, D), g)
+    kx = g.standard_normal((B, S, H, D)).astype(np.float32)
+    mu = np.round(g.standard_normal((1, 1, H, D)) * 4).astype(np.float32)
+    v = gen.normal_bf16((B, S, H, D), g)
+    k1 = gen.to_bf16_bits(np.round(kx * 8) / 8)
+    k2 = gen.to_bf16_bits(np.round(kx * 8) / 8 - mu)
+    o1 = O.attn_exact(q, O.Prologue(), k1, O.Prologue(), v)
+    o2 = O.attn_exact(q, O.Prologue(), k2, O.Prologue(), v)
+    np.testing.assert_allclose(o1, o2, rtol=1e-9, atol=1e-12)
+
+
+def test_exact_attention_matches_numpy_textbook():
+    """Binary64 attention with RMSNorm and complex-rotation RoPE written with numpy routines."""
+    g = np.random.default_rng(54)
+    B, S, H, D = 1, 48, 2, 64
+    q, k, v = (gen.normal_bf16((B, S, H, D), g) for _ in range(3))
+    w = gen.uniform_bf16((1, D), g)
+    tb = gen.rope_table(S, D // 2)
+    pro = O.Prologue(norm=O.NORM_HEAD, weight=w, eps=1e-6, rope=O.ROPE_SPLIT_HALF, table=tb)
+    out = O.attn_exact(q, pro, k, pro, v)
+
+    def prep(x):
+        xv = f32(x).astype(np.float64)
+        y = xv / np.sqrt((xv ** 2).mean(-1, keepdims=True) + 1e-6) * f32(w)[0]
+        z = (y[..., :D // 2] + 1j * y[..., D // 2:]) * (tb[0, :, 0, :, 0] + 1j * tb[0, :, 0, :, 1])[None, :, None]
+        return np.concatenate([z.real, z.imag], -1)
+
+    qx, kx, vx = prep(q), prep(k), f32(v).astype(np.float64)
+    for h in range(H):
+        s = qx[0, :, h] @ kx[0, :, h].T / math.sqrt(D)
+        p = np.exp(s - s.max(-1, keepdims=True))
+        np.testing.assert_allclose(out[0, :, h], p @ vx[0, :, h] / p.sum(-1, keepdims=True), rtol=1e-9, atol=1e-12)
+
+
+def test_quantized_pipeline_tracks_exact_attention_tiny():
+    """Norm + RoPE + k mean + INT8 q/k + bf16 P.V on the tiny workload stays within cos 0.999 of the
+    unquantized FP64 attention (the method is an approximation of it)."""
+    c = gen.CFG1
+    inp = gen.attn_inputs(c)
+    pq = O.Prologue(norm=O.NORM_HEAD, weight=inp.wq, eps=c.eps, rope=O.ROPE_SPLIT_HALF, table=inp.table)
+    pk = O.Prologue(norm=O.NORM_HEAD, weight=inp.wk, eps=c.eps, rope=O.ROPE_SPLIT_HALF, table=inp.table)
+    mu = O.kmean(inp.k, pk)
+    qc, qs = O.quant_qk(inp.q, pq, 0, 64, sm_scale=gen.sm_scale_q(c.D))
+    kc, ks = O.quant_qk(inp.k, pk, 0, 64, mean=mu)
+    out, lse, _ = O.attn(O.QK(qc, qs, 0, 64), O.QK(kc, ks, 0, 64), inp.v, fp8=False, kv_tile=64)
+    ref = O.attn_exact(inp.q, pq, inp.k, pk, inp.v)
+    cos = (out * ref).sum() / np.sqrt((out ** 2).sum() * (ref ** 2).sum())
+    assert cos > 0.999, cos
