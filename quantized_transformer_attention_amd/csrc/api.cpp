@@ -1,0 +1,244 @@
+// libsq C entry points: validate on the host (validate.cpp, no HIP call), size the
+// workspace, then hand an argument block to the kernel launchers. Nothing is
+// enqueued when validation fails.
+#include <cmath>
+#include <cstring>
+
+#include "sq_internal.h"
+
+using namespace sq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+bool all_heads_needs_ws(const sq_norm* n) { return n && n->mode == SQ_NORM_ALL_HEADS && !n->mean_sq; }
+
+int check_ws(void* ws, size_t have, size_t need, const char* what) {
+    if (need == 0) return SQ_OK;
+    if (!ws) return fail(SQ_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got NULL", what, need);
+    if (have < need) return fail(SQ_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", what, need, have);
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(SQ_ERR_ALIGN, "%s: workspace must be %zu-byte aligned", what, kAlign);
+    return SQ_OK;
+}
+
+// Runs A1 into the workspace when the all-heads norm has no precomputed statistics.
+int prepare_all_heads(const sq_rows* x, RowArgs& r, void* ws, void* stream) {
+    if (r.norm != SQ_NORM_ALL_HEADS || r.ms) return SQ_OK;
+    NormStatsArgs s{static_cast<const uint16_t*>(x->data), x->B, x->T, x->H, x->D, x->sb, x->st, x->sh,
+                    static_cast<float*>(ws), x->T, 1};
+    r.ms = s.ms;
+    r.msb = x->T;
+    r.mst = 1;
+    return launch_norm_stats(s, stream);
+}
+
+int check_prologue(const sq_rows* x, const sq_norm* n, const sq_rope* r, const char* what) {
+    int st = check_rows(x, what);
+    if (!st) st = check_norm(n, x, what);
+    if (!st) st = check_rope(r, x, what);
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sq_norm_stats(const sq_rows* x, float* mean_sq, int64_t msb, int64_t mst, void* stream) {
+    clear_error();
+    int st = check_rows(x, "sq_norm_stats");
+    if (st) return st;
+    if (x->B * x->T * x->H == 0) return SQ_OK;
+    if (!mean_sq) return fail(SQ_ERR_NULL, "sq_norm_stats: mean_sq is NULL");
+    if (msb < 0 || mst < 0) return fail(SQ_ERR_STRIDE, "sq_norm_stats: negative stride");
+    NormStatsArgs a{static_cast<const uint16_t*>(x->data), x->B, x->T, x->H, x->D, x->sb, x->st, x->sh,
+                    mean_sq, msb, mst};
+    return launch_norm_stats(a, stream);
+}
+
+size_t sq_kmean_workspace_bytes(const sq_rows* k, const sq_norm* norm) {
+    if (!k) return 0;
+    const int64_t nblk = (k->T + 63) / 64;
+    size_t bytes = round_up(sizeof(float) * static_cast<size_t>(k->B * k->H * nblk * k->D));
+    if (all_heads_needs_ws(norm)) bytes += round_up(sizeof(float) * static_cast<size_t>(k->B * k->T));
+    return bytes;
+}
+
+int sq_kmean(const sq_rows* k, const sq_norm* norm, const sq_rope* rope, float* mean, int64_t mb, int64_t mh,
+             void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    int st = check_prologue(k, norm, rope, "sq_kmean");
+    if (st) return st;
+    if (k->B * k->H == 0) return SQ_OK;
+    if (k->T == 0) return fail(SQ_ERR_SHAPE, "sq_kmean: the mean of zero tokens is undefined");
+    if (!mean) return fail(SQ_ERR_NULL, "sq_kmean: mean is NULL");
+    if (mb < 0 || mh < 0) return fail(SQ_ERR_STRIDE, "sq_kmean: negative stride");
+    st = check_ws(ws, ws_bytes, sq_kmean_workspace_bytes(k, norm), "sq_kmean");
+    if (st) return st;
+    KmeanArgs a{};
+    a.r = row_args(k, norm, rope);
+    a.nblk = (k->T + 63) / 64;
+    a.partial = static_cast<float*>(ws);
+    a.mean = mean;
+    a.mb = mb;
+    a.mh = mh;
+    void* ms_ws = static_cast<char*>(ws) + round_up(sizeof(float) * static_cast<size_t>(k->B * k->H * a.nblk * k->D));
+    st = prepare_all_heads(k, a.r, ms_ws, stream);
+    if (st) return st;
+    return launch_kmean(a, stream);
+}
+
+size_t sq_quant_qk_workspace_bytes(const sq_rows* x, const sq_norm* norm) {
+    if (!x || !all_heads_needs_ws(norm)) return 0;
+    return round_up(sizeof(float) * static_cast<size_t>(x->B * x->T));
+}
+
+int sq_quant_qk(const sq_rows* x, const sq_norm* norm, const sq_rope* rope, const float* mean, int64_t mb,
+                int64_t mh, float sm_scale, float scale_eps, sq_layout layout, int block, int8_t* codes, int64_t ob,
+                int64_t ot, int64_t oh, float* scales, int64_t ssb, int64_t ssh, void* ws, size_t ws_bytes,
+                void* stream) {
+    clear_error();
+    int st = check_prologue(x, norm, rope, "sq_quant_qk");
+    if (!st) st = check_layout(layout, block, "sq_quant_qk");
+    if (st) return st;
+    if (x->B * x->T * x->H == 0) return SQ_OK;
+    if (!codes || !scales) return fail(SQ_ERR_NULL, "sq_quant_qk: codes or scales are NULL");
+    if (ob < 0 || ot < 0 || oh < 0 || ssb < 0 || ssh < 0) return fail(SQ_ERR_STRIDE, "sq_quant_qk: negative stride");
+    if ((reinterpret_cast<uintptr_t>(codes) & 7) || ob % 8 || ot % 8 || oh % 8)
+        return fail(SQ_ERR_ALIGN, "sq_quant_qk: code rows must start on 8-byte boundaries");
+    if (mean && ((reinterpret_cast<uintptr_t>(mean) & 15) || mb % 4 || mh % 4))
+        return fail(SQ_ERR_ALIGN, "sq_quant_qk: mean rows must be 16-byte aligned");
+    if (!std::isfinite(sm_scale) || !std::isfinite(scale_eps) || scale_eps < 0.0f)
+        return fail(SQ_ERR_SHAPE, "sq_quant_qk: sm_scale and scale_eps must be finite, scale_eps >= 0");
+    st = check_ws(ws, ws_bytes, sq_quant_qk_workspace_bytes(x, norm), "sq_quant_qk");
+    if (st) return st;
+    QuantArgs a{};
+    a.r = row_args(x, norm, rope);
+    a.mean = mean;
+    a.mb = mb;
+    a.mh = mh;
+    a.sm_scale = sm_scale;
+    a.scale_eps = scale_eps;
+    a.layout = layout;
+    a.block = block;
+    a.codes = codes;
+    a.ob = ob; a.ot = ot; a.oh = oh;
+    a.scales = scales;
+    a.ssb = ssb; a.ssh = ssh;
+    a.nscale = scale_count(x->T, layout, block);
+    st = prepare_all_heads(x, a.r, ws, stream);
+    if (st) return st;
+    return launch_quant_qk(a, stream);
+}
+
+size_t sq_quant_v_fp8_workspace_bytes(const sq_rows* v) {
+    if (!v) return 0;
+    return round_up(sizeof(uint32_t) * static_cast<size_t>(v->B * v->H * v->D));
+}
+
+int sq_quant_v_fp8(const sq_rows* v, uint8_t* codes, int64_t ob, int64_t oh, int64_t od, float* vs, int64_t vsb,
+                   int64_t vsh, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    int st = check_rows(v, "sq_quant_v_fp8");
+    if (st) return st;
+    if (v->B * v->T * v->H == 0) return SQ_OK;
+    if (!codes || !vs) return fail(SQ_ERR_NULL, "sq_quant_v_fp8: codes or vs are NULL");
+    if (ob < 0 || oh < 0 || vsb < 0 || vsh < 0) return fail(SQ_ERR_STRIDE, "sq_quant_v_fp8: negative stride");
+    if (od < (v->T + 15) / 16 * 16 || od % 16)
+        return fail(SQ_ERR_STRIDE, "sq_quant_v_fp8: token stride od must be a multiple of 16 and >= T rounded up");
+    if ((reinterpret_cast<uintptr_t>(codes) & 15) || ob % 16 || oh % 16)
+        return fail(SQ_ERR_ALIGN, "sq_quant_v_fp8: channel rows must start on 16-byte boundaries");
+    st = check_ws(ws, ws_bytes, sq_quant_v_fp8_workspace_bytes(v), "sq_quant_v_fp8");
+    if (st) return st;
+    QuantVArgs a{static_cast<const uint16_t*>(v->data), v->B, v->T, v->H, v->D, v->sb, v->st, v->sh,
+                 codes, ob, oh, od, vs, vsb, vsh, static_cast<uint32_t*>(ws)};
+    return launch_quant_v_fp8(a, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_pair(const sq_qk* q, const sq_qk* k, const char* what) {
+    int st = check_qk(q, what);
+    if (!st) st = check_qk(k, what);
+    if (st) return st;
+    if (q->layout == SQ_LAYOUT_THREAD_K)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: q layout THREAD_K is a key layout", what);
+    if (k->layout == SQ_LAYOUT_THREAD_Q || k->layout == SQ_LAYOUT_WARP_Q)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: k layout must be PER_BLOCK or THREAD_K", what);
+    if (q->B != k->B || q->D != k->D) return fail(SQ_ERR_SHAPE, "%s: q and k differ in batch or head dim", what);
+    if (k->H < 1 || q->H % k->H) return fail(SQ_ERR_SHAPE, "%s: q heads %lld not a multiple of kv heads %lld", what,
+                                             (long long)q->H, (long long)k->H);
+    return SQ_OK;
+}
+
+int64_t padded_keys(int64_t S) { return (S + 127) / 128 * 128; }
+
+}  // namespace
+
+extern "C" {
+
+size_t sq_attn_workspace_bytes(const sq_qk* q, const sq_qk* k, const sq_values* v) {
+    (void)q;
+    if (!k || !v || v->dtype != SQ_BF16) return 0;
+    return round_up(sizeof(uint16_t) * static_cast<size_t>(k->B * k->H * k->D * padded_keys(k->S)));
+}
+
+int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scale, int kv_tile, float* out,
+            int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh, void* ws, size_t ws_bytes,
+            void* stream) {
+    clear_error();
+    int st = check_pair(q, k, "sq_attn");
+    if (st) return st;
+    if (q->B * q->S * q->H == 0) return SQ_OK;
+    if (k->S < 1) return fail(SQ_ERR_SHAPE, "sq_attn: no keys");
+    if (!v || !v->data) return fail(SQ_ERR_NULL, "sq_attn: values are NULL");
+    if (!out) return fail(SQ_ERR_NULL, "sq_attn: out is NULL");
+    if (ob < 0 || ot < 0 || oh < 0 || lb < 0 || lh < 0) return fail(SQ_ERR_STRIDE, "sq_attn: negative stride");
+    if (kv_tile != 64 && kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "sq_attn: kv_tile must be 64 or 128");
+    if (!(score_scale > 0.0f) || !std::isfinite(score_scale))
+        return fail(SQ_ERR_SHAPE, "sq_attn: score_scale must be finite and > 0");
+    AttnArgs a{};
+    a.q = q->codes; a.B = q->B; a.Sq = q->S; a.H = q->H; a.D = q->D;
+    a.qsb = q->sb; a.qst = q->st; a.qsh = q->sh;
+    a.qs = q->scales; a.qssb = q->ssb; a.qssh = q->ssh; a.q_layout = q->layout; a.q_block = q->block;
+    a.k = k->codes; a.Sk = k->S; a.Hk = k->H; a.ksb = k->sb; a.kst = k->st; a.ksh = k->sh;
+    a.ks = k->scales; a.kssb = k->ssb; a.kssh = k->ssh; a.k_layout = k->layout; a.k_block = k->block;
+    a.score_scale = score_scale;
+    a.kv_tile = kv_tile;
+    a.out = out; a.ob = ob; a.ot = ot; a.oh = oh;
+    a.lse = lse; a.lb = lb; a.lh = lh;
+    if (v->dtype == SQ_FP8E4M3) {
+        if (kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "sq_attn: FP8 P.V needs kv_tile 128");
+        if (v->st != 1) return fail(SQ_ERR_STRIDE, "sq_attn: FP8 values must be channel-major (st == 1)");
+        if (!v->scale) return fail(SQ_ERR_NULL, "sq_attn: FP8 values need their per-channel scales");
+        if (v->sd < (k->S + 15) / 16 * 16 || v->sd % 16 || v->sb < 0 || v->sh < 0 || v->vsb < 0 || v->vsh < 0)
+            return fail(SQ_ERR_STRIDE, "sq_attn: FP8 channel stride must be a multiple of 16 >= keys rounded up");
+        if ((reinterpret_cast<uintptr_t>(v->data) & 15) || v->sb % 16 || v->sh % 16)
+            return fail(SQ_ERR_ALIGN, "sq_attn: FP8 channel rows must start on 16-byte boundaries");
+        a.v = v->data; a.v_fp8 = 1;
+        a.vsb = v->sb; a.vsh = v->sh; a.vsd = v->sd;
+        a.vscale = v->scale; a.vssb = v->vsb; a.vssh = v->vsh;
+        return launch_attn(a, stream);
+    }
+    if (v->dtype != SQ_BF16) return fail(SQ_ERR_UNSUPPORTED, "sq_attn: values must be bf16 or FP8 e4m3");
+    if (v->sd != 1) return fail(SQ_ERR_STRIDE, "sq_attn: bf16 values must be token-major (sd == 1)");
+    if ((reinterpret_cast<uintptr_t>(v->data) & 15) || v->sb % 8 || v->st % 8 || v->sh % 8 || v->sb < 0 || v->st < 0 ||
+        v->sh < 0)
+        return fail(SQ_ERR_ALIGN, "sq_attn: bf16 value rows must start on 16-byte boundaries");
+    st = check_ws(ws, ws_bytes, sq_attn_workspace_bytes(q, k, v), "sq_attn");
+    if (st) return st;
+    const int64_t spad = padded_keys(k->S);
+    VTransposeArgs t{static_cast<const uint16_t*>(v->data), k->B, k->S, k->H, k->D, v->sb, v->st, v->sh,
+                     static_cast<uint16_t*>(ws), spad};
+    st = launch_v_transpose(t, stream);
+    if (st) return st;
+    a.v = ws; a.v_fp8 = 0;
+    a.vsb = k->H * k->D * spad; a.vsh = k->D * spad; a.vsd = spad;
+    return launch_attn(a, stream);
+}
+
+}  // extern "C"

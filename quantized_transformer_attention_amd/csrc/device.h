@@ -1,0 +1,47 @@
+// Device helpers shared by the libsq kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sq {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// 8 bf16 (one 16-byte load) -> 8 floats.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
+    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x);
+    f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z);
+    f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+}
+
+// Round to bfloat16, nearest even (v_cvt_pk_bf16_f32), back to float.
+__device__ __forceinline__ float bf16_round(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Correctly rounded v / s given y = RN(1 / s): q = RN(v y), r = v - q s exactly (fma),
+// q' = RN(q + r y). By Markstein's theorem q' = RN(v / s) when y is the correctly rounded
+// reciprocal and nothing overflows or underflows.
+__device__ __forceinline__ float div_rn(float v, float s, float y) {
+    float q = v * y;
+    float r = __builtin_fmaf(-q, s, v);
+    return __builtin_fmaf(r, y, q);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace sq

@@ -1,0 +1,167 @@
+// Internal declarations of libsq: argument blocks handed from the C entry points
+// (api.cpp) to the kernel launchers (*.hip). Host-only types; no HIP headers here,
+// so the validation layer stays free of the HIP runtime.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/sq.h"
+
+namespace sq {
+
+// Thread-local last error; returns `status` for tail calls.
+int fail(int status, const char* fmt, ...);
+void clear_error();
+
+// ---------------------------------------------------------------- row prologue
+struct RowArgs {
+    const uint16_t* x;          // bf16 rows
+    int64_t B, T, H, D, sb, st, sh;
+    int norm;                   // sq_norm_mode
+    const uint16_t* w;          // bf16 weight rows (rows, wd)
+    int64_t wd;                 // D (per head) or H*D (all heads)
+    const int32_t* wrows;       // per-token weight row or nullptr
+    const float* ms;            // all-heads mean squares (b, t) or nullptr
+    int64_t msb, mst;
+    float eps;
+    int rope;                   // sq_rope_mode
+    const float* table;
+    int64_t pairs, rb, rs, rp, rc;
+    bool rope_contig;           // rp == 2, rc == 1 and 16-byte aligned rows
+};
+
+struct QuantArgs {
+    RowArgs r;
+    const float* mean;          // (b, h) rows of D or nullptr
+    int64_t mb, mh;
+    float sm_scale, scale_eps;
+    int layout, block;
+    int8_t* codes;
+    int64_t ob, ot, oh;
+    float* scales;
+    int64_t ssb, ssh;
+    int64_t nscale;             // scales per (b, h)
+};
+
+struct KmeanArgs {
+    RowArgs r;
+    float* partial;             // (B, H, nblk, D) workspace
+    int64_t nblk;
+    float* mean;
+    int64_t mb, mh;
+};
+
+struct NormStatsArgs {
+    const uint16_t* x;
+    int64_t B, T, H, D, sb, st, sh;
+    float* ms;
+    int64_t msb, mst;
+};
+
+struct QuantVArgs {
+    const uint16_t* v;
+    int64_t B, T, H, D, sb, st, sh;
+    uint8_t* codes;             // channel-major
+    int64_t ob, oh, od;
+    float* vs;
+    int64_t vsb, vsh;
+    uint32_t* amax;             // (B, H, D) workspace
+};
+
+// ---------------------------------------------------------------- attention core
+struct AttnArgs {
+    const int8_t* q;
+    int64_t B, Sq, H, D, qsb, qst, qsh;
+    const float* qs;
+    int64_t qssb, qssh;
+    int q_layout, q_block;
+    const int8_t* k;
+    int64_t Sk, Hk, ksb, kst, ksh;
+    const float* ks;
+    int64_t kssb, kssh;
+    int k_layout, k_block;
+    const void* v;              // channel-major bf16 or fp8 (sb, sh, sd; tokens contiguous)
+    int v_fp8;
+    int64_t vsb, vsh, vsd;
+    const float* vscale;
+    int64_t vssb, vssh;
+    float score_scale;
+    int kv_tile;
+    float* out;
+    int64_t ob, ot, oh;
+    float* lse;
+    int64_t lb, lh;
+};
+
+struct VTransposeArgs {
+    const uint16_t* v;          // token-major bf16 (B, S, Hk, D)
+    int64_t B, S, H, D, sb, st, sh;
+    uint16_t* out;              // channel-major (B, H, D, Spad)
+    int64_t Spad;
+};
+
+struct PrefixArgs {
+    const int8_t* q;
+    int64_t B, Sq, H, D, qsb, qst, qsh;
+    const float* qs;
+    int64_t qssb, qssh;
+    int q_layout, q_block;
+    int64_t PB, P, Hk;
+    const int8_t* k;
+    int64_t kb, kt, kh;
+    const uint16_t* ks;
+    int64_t ksb, kst, ksh;
+    const int8_t* v;
+    int64_t vb, vt, vh;
+    const uint16_t* vs;
+    int64_t vsb, vst, vsh;
+    const float* mu;
+    int64_t mb, mh;
+    float score_scale;
+    int kv_tile;
+    float* out;
+    int64_t ob, ot, oh;
+    float* lse;
+    int64_t lb, lh;
+};
+
+struct DecodeArgs {
+    const uint16_t* q;
+    int64_t qn, qh;
+    const int8_t* kc;
+    const uint16_t* ks;
+    const int8_t* vc;
+    const uint16_t* vs;
+    int64_t num_blocks;
+    int bs, Hk, Hq, D;
+    const int32_t* bt;
+    int64_t bt_stride;
+    const int32_t* lens;
+    int N, max_len;
+    float scale;
+    float* out;
+    int64_t on, oh;
+    float* part;                // split-KV partials (N, Hq, segs, D + 2)
+    int segs, seg_tiles;        // segments per sequence and 64-key tiles per segment
+};
+
+// ---------------------------------------------------------------- launchers (*.hip)
+int launch_norm_stats(const NormStatsArgs& a, void* stream);
+int launch_kmean(const KmeanArgs& a, void* stream);
+int launch_quant_qk(const QuantArgs& a, void* stream);
+int launch_quant_v_fp8(const QuantVArgs& a, void* stream);
+int launch_v_transpose(const VTransposeArgs& a, void* stream);
+int launch_attn(const AttnArgs& a, void* stream);
+int launch_prefix(const PrefixArgs& a, void* stream);
+int launch_decode(const DecodeArgs& a, void* stream);
+
+// ---------------------------------------------------------------- validation (validate.cpp)
+int check_rows(const sq_rows* x, const char* what);
+int check_norm(const sq_norm* n, const sq_rows* x, const char* what);
+int check_rope(const sq_rope* r, const sq_rows* x, const char* what);
+int check_layout(int layout, int block, const char* what);
+int check_qk(const sq_qk* t, const char* what);
+int64_t scale_count(int64_t T, int layout, int block);
+RowArgs row_args(const sq_rows* x, const sq_norm* n, const sq_rope* r);
+
+}  // namespace sq

@@ -1,0 +1,109 @@
+"""The C-ABI library (no GPU): it loads, exports every symbol include/sq.h declares, and rejects invalid
+arguments on the host before anything is enqueued (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_transformer_attention_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "sq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = sq.lib()
+    names = declared_symbols()
+    assert len(names) >= 17
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(sq.EXPORTS)
+    assert L.sq_abi_version() == 1
+
+
+def test_status_strings():
+    L = sq.lib()
+    assert L.sq_status_string(0) == b"SQ_OK"
+    assert L.sq_status_string(-5) == b"SQ_ERR_UNSUPPORTED"
+    assert L.sq_status_string(-99) == b"SQ_ERR_UNKNOWN"
+
+
+def test_scale_counts():
+    assert sq.sq_scale_count(32760, sq.LAYOUT_THREAD_Q, 32) == 8192
+    assert sq.sq_scale_count(32760, sq.LAYOUT_THREAD_K, 64) == 2048
+    assert sq.sq_scale_count(75600, sq.LAYOUT_WARP_Q, 128) == 2364
+    assert sq.sq_scale_count(75600, sq.LAYOUT_PER_BLOCK, 64) == 1182
+    assert sq.sq_scale_count(8704, sq.LAYOUT_PER_BLOCK, 128) == 68
+    assert sq.sq_scale_count(100, sq.LAYOUT_THREAD_Q, 64) == -1
+    assert sq.sq_scale_count(100, sq.LAYOUT_PER_BLOCK, 48) == -1
+
+
+def _rows(D=128, T=10, data=0x1000, st=None):
+    return sq.sq_rows(data, 1, T, 2, D, 2 * T * D, st if st is not None else 2 * D, D)
+
+
+def _call_quant(rows, layout=0, block=64, codes=0x2000, scales=0x3000, norm=None, rope=None, sm=1.0, eps=1e-7):
+    L = sq.lib()
+    return L.sq_quant_qk(ctypes.byref(rows), ctypes.byref(norm) if norm else None,
+                         ctypes.byref(rope) if rope else None, None, 0, 0, sm, eps, layout, block, codes, 2 * 10 * 128,
+                         256, 128, scales, 2, 1, None, 0, None)
+
+
+def test_quant_validation_errors():
+    L = sq.lib()
+    assert _call_quant(_rows(D=96)) == -5
+    assert _call_quant(_rows(data=0)) == -1
+    assert _call_quant(_rows(data=0x1008)) == -4          # misaligned row base
+    assert _call_quant(_rows(st=260)) == -4               # stride not a multiple of 8 elements
+    assert _call_quant(_rows(), layout=1, block=64) == -5  # THREAD_Q needs block 32
+    assert _call_quant(_rows(), codes=0) == -1
+    assert _call_quant(_rows(), codes=0x2004) == -4
+    assert _call_quant(_rows(), eps=-1.0) == -2
+    bad_norm = sq.sq_norm(sq.NORM_HEAD, 0, None, None, 0, 0, 1e-6)
+    assert _call_quant(_rows(), norm=bad_norm) == -1
+    rope = sq.sq_rope(sq.ROPE_SPLIT_HALF, 0x4000, 12, 0, 128, 2, 1)  # pairs % 8 != 0
+    assert _call_quant(_rows(), rope=rope) == -5
+    rope = sq.sq_rope(sq.ROPE_SPLIT_HALF, 0x4000, 80, 0, 128, 2, 1)  # pairs > D / 2
+    assert _call_quant(_rows(), rope=rope) == -2
+    # an all-heads norm without precomputed statistics needs a workspace
+    norm = sq.sq_norm(sq.NORM_ALL_HEADS, 0x5000, None, None, 0, 0, 1e-6)
+    assert _call_quant(_rows(), norm=norm) == -6
+    assert b"workspace" in L.sq_last_error()
+    # empty input is a valid no-op
+    assert _call_quant(_rows(T=0)) == 0
+
+
+def _qk(layout=0, block=64, S=10, H=2, D=128, codes=0x1000):
+    return sq.sq_qk(codes, 1, S, H, D, S * H * D, H * D, D, 0x2000, H * 4, 4, layout, block)
+
+
+def test_attn_validation_errors():
+    L = sq.lib()
+    v = sq.sq_values(0x3000, sq.SQ_BF16, 10 * 2 * 128, 2 * 128, 128, 1, None, 0, 0)
+
+    def call(q, k, vv=v, tile=64, out=0x4000, scale=1.0, ws=None, wsb=0):
+        return L.sq_attn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vv), scale, tile, out, 0, 0, 0, None, 0, 0,
+                         ws, wsb, None)
+
+    assert call(_qk(layout=2), _qk()) == -5                # THREAD_K is a key layout
+    assert call(_qk(), _qk(layout=1, block=32)) == -5      # THREAD_Q is a query layout
+    assert call(_qk(H=3), _qk(H=2)) == -2                  # heads not a multiple of kv heads
+    assert call(_qk(D=64), _qk()) == -2                   # head dims differ
+    assert call(_qk(), _qk(), tile=32) == -5
+    assert call(_qk(), _qk(), out=0) == -1
+    assert call(_qk(), _qk(), scale=0.0) == -2
+    assert call(_qk(), _qk(S=0)) == -2                     # no keys
+    assert call(_qk(), _qk()) == -6                        # bf16 values are staged in a workspace
+    v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 16, None, 0, 0)
+    assert call(_qk(), _qk(), vv=v8, tile=128) == -1       # FP8 needs its scales
+    v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 16, 0x5000, 0, 0)
+    assert call(_qk(), _qk(), vv=v8, tile=64) == -5        # FP8 P.V runs 128-key tiles
+    v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 8, 0x5000, 0, 0)
+    assert call(_qk(), _qk(), vv=v8, tile=128) == -3       # channel stride below the key count
+    assert call(_qk(S=0), _qk()) == 0                      # no queries: no-op

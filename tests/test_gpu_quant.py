@@ -1,0 +1,163 @@
+"""GPU parity of the prologue and quantizers against the CPU oracle: bit-exact INT8 codes, FP32 scales,
+all-heads mean squares, k means and FP8 V codes, on ragged small cases and at the workloads' full sizes."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as O
+import quantized_transformer_attention_amd as sq
+from tests._util import DEV, dev, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _pro(norm, rope, w, table, wrows=None, eps=1e-6):
+    return O.Prologue(norm=norm, weight=w, weight_rows=wrows, eps=eps, rope=rope, table=table)
+
+
+def _gpu_specs(norm, rope, w, table, wrows=None, eps=1e-6):
+    n = sq.Norm(norm, dev_bf16(w), dev(wrows) if wrows is not None else None, None, eps) if norm else None
+    r = sq.Rope(rope, dev(table)) if rope else None
+    return n, r
+
+
+def _case(B, T, H, D, seed, outliers=0):
+    g = gen.rng(seed, 0)
+    x = gen.normal_bf16((B, T, H, D), g, outliers)
+    return x
+
+
+LAYOUTS = [(0, 32), (0, 64), (0, 128), (1, 32), (2, 64), (3, 128)]
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("norm", [O.NORM_NONE, O.NORM_HEAD, O.NORM_ALL_HEADS])
+@pytest.mark.parametrize("rope", [O.ROPE_NONE, O.ROPE_SPLIT_HALF, O.ROPE_INTERLEAVED])
+def test_quant_bit_exact_ragged(D, norm, rope):
+    B, T, H = 2, 333, 3
+    print("quant D=%d norm=%d rope=%d" % (D, norm, rope), flush=True)
+    x = _case(B, T, H, D, 100 + D + 10 * norm + rope)
+    wd = H * D if norm == O.NORM_ALL_HEADS else D
+    w = gen.uniform_bf16((2, wd), gen.rng(7, 1))
+    wrows = (np.arange(T) >= 100).astype(np.int32)
+    table = gen.rope_table(T, D // 2 if rope == O.ROPE_SPLIT_HALF else D // 2 - 3, start=5)
+    pro = _pro(norm, rope, w, table, wrows)
+    mu = O.kmean(x, pro)
+    n, r = _gpu_specs(norm, rope, w, table, wrows)
+    xd = dev_bf16(x)
+    mu_gpu = sq.sq_kmean(xd, n, r)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(mu_gpu).view(np.uint32), mu.view(np.uint32))
+    for layout, block in LAYOUTS:
+        for mean, sm in ((None, 0.1275), (mu, 1.0)):
+            codes, scales = O.quant_qk(x, pro, layout, block, mean=mean, sm_scale=sm, scale_eps=1e-7)
+            res = sq.sq_quant_qk(xd, n, r, dev(mean) if mean is not None else None, sm, 1e-7, layout, block)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(res.scales).view(np.uint32), scales.view(np.uint32),
+                                          err_msg="scales layout %d block %d" % (layout, block))
+            np.testing.assert_array_equal(host(res.codes), codes, err_msg="codes layout %d block %d" % (layout, block))
+
+
+def test_norm_stats_bit_exact():
+    for D, H in ((128, 40), (64, 7)):
+        x = _case(2, 77, H, D, 200 + D, outliers=9)
+        ms = O.mean_sq_all_heads(x)
+        got = sq.sq_norm_stats(dev_bf16(x))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(got).view(np.uint32), ms.view(np.uint32))
+
+
+def test_quant_edge_cases():
+    D = 128
+    # one token; all-zero rows with scale_eps = 0 (scale 0 -> codes 0); strided input (a head slice)
+    x = _case(1, 1, 2, D, 300)
+    for layout, block in LAYOUTS:
+        codes, scales = O.quant_qk(x, O.Prologue(), layout, block)
+        res = sq.sq_quant_qk(dev_bf16(x), layout=layout, block=block)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(res.codes), codes)
+        np.testing.assert_array_equal(host(res.scales).view(np.uint32), scales.view(np.uint32))
+    z = np.zeros((1, 70, 2, D), np.uint16)
+    codes, scales = O.quant_qk(z, O.Prologue(), 0, 64, scale_eps=0.0)
+    res = sq.sq_quant_qk(dev_bf16(z), layout=0, block=64, scale_eps=0.0)
+    torch.cuda.synchronize()
+    assert np.all(host(res.codes) == 0) and np.all(codes == 0)
+    np.testing.assert_array_equal(host(res.scales), scales)
+    big = _case(1, 130, 6, D, 301)
+    xd = dev_bf16(big)[:, :, 1:5]            # strided view: heads 1..4 of 6
+    codes, scales = O.quant_qk(np.ascontiguousarray(big[:, :, 1:5]), O.Prologue(), 1, 32)
+    res = sq.sq_quant_qk(xd, layout=1, block=32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(res.codes), codes)
+    np.testing.assert_array_equal(host(res.scales).view(np.uint32), scales.view(np.uint32))
+
+
+def test_v_fp8_bit_exact():
+    for D, T in ((128, 300), (64, 129), (128, 1)):
+        v = _case(1, T, 3, D, 400 + T, outliers=5)
+        codes, vs = O.quant_v_fp8(v)
+        c_gpu, vs_gpu = sq.sq_quant_v_fp8(dev_bf16(v))
+        torch.cuda.synchronize()
+        cg = host(c_gpu)                                   # (B, H, D, Tpad)
+        np.testing.assert_array_equal(host(vs_gpu).view(np.uint32), vs.view(np.uint32))
+        np.testing.assert_array_equal(cg[..., :T], codes.transpose(0, 2, 3, 1))
+        assert np.all(cg[..., T:] == 0)
+
+
+def test_cfg2_video_quantizers_full_size():
+    """Video workload at full size (1 x 32760 x 40 x 128, 1% outlier channels): all-heads norm + RoPE,
+    THREAD_Q q, k mean + THREAD_K k, V to FP8, bit-exact on every element."""
+    c = gen.CFG2
+    inp = gen.attn_inputs(c)
+    print("cfg2 inputs ready", flush=True)
+    pq = _pro(O.NORM_ALL_HEADS, O.ROPE_SPLIT_HALF, inp.wq, inp.table, eps=c.eps)
+    pk = _pro(O.NORM_ALL_HEADS, O.ROPE_SPLIT_HALF, inp.wk, inp.table, eps=c.eps)
+    nq, r = _gpu_specs(O.NORM_ALL_HEADS, O.ROPE_SPLIT_HALF, inp.wq, inp.table, eps=c.eps)
+    nk, _ = _gpu_specs(O.NORM_ALL_HEADS, O.ROPE_SPLIT_HALF, inp.wk, inp.table, eps=c.eps)
+    qd, kd, vd = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    ms = sq.sq_norm_stats(kd)
+    mu_gpu = sq.sq_kmean(kd, nk, r)
+    qq = sq.sq_quant_qk(qd, nq, r, None, gen.sm_scale_q(c.D), 1e-7, O.LAYOUT_THREAD_Q, 32)
+    kq = sq.sq_quant_qk(kd, nk, r, mu_gpu, 1.0, 1e-7, O.LAYOUT_THREAD_K, 64)
+    v8, vs = sq.sq_quant_v_fp8(vd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ms).view(np.uint32), O.mean_sq_all_heads(inp.k).view(np.uint32))
+    mu = O.kmean(inp.k, pk)
+    np.testing.assert_array_equal(host(mu_gpu).view(np.uint32), mu.view(np.uint32))
+    print("cfg2 k mean ok", flush=True)
+    codes, scales = O.quant_qk(inp.q, pq, O.LAYOUT_THREAD_Q, 32, sm_scale=gen.sm_scale_q(c.D))
+    np.testing.assert_array_equal(host(qq.scales).view(np.uint32), scales.view(np.uint32))
+    np.testing.assert_array_equal(host(qq.codes), codes)
+    codes, scales = O.quant_qk(inp.k, pk, O.LAYOUT_THREAD_K, 64, mean=mu)
+    np.testing.assert_array_equal(host(kq.scales).view(np.uint32), scales.view(np.uint32))
+    np.testing.assert_array_equal(host(kq.codes), codes)
+    vc, vsc = O.quant_v_fp8(inp.v)
+    np.testing.assert_array_equal(host(vs).view(np.uint32), vsc.view(np.uint32))
+    np.testing.assert_array_equal(host(v8)[..., :c.Sk], vc.transpose(0, 2, 3, 1))
+
+
+def test_cfg4_quantizer_full_size_sampled_heads():
+    """Quantizer workload at full size (2 x 75600 x 40 x 128), every layout, checked on sampled heads
+    (the per-head norm makes heads independent; the oracle runs on the sampled head slices)."""
+    c = gen.CFG4
+    x, w, table = gen.quant_inputs(c)
+    print("cfg4 inputs ready", flush=True)
+    pro = _pro(O.NORM_HEAD, O.ROPE_SPLIT_HALF, w, table, eps=c.eps)
+    n, r = _gpu_specs(O.NORM_HEAD, O.ROPE_SPLIT_HALF, w, table, eps=c.eps)
+    xd = dev_bf16(x)
+    heads = [0, 17, 39]
+    xs = np.ascontiguousarray(x[:, :, heads])
+    mu_gpu = sq.sq_kmean(xd, n, r)
+    torch.cuda.synchronize()
+    mu = O.kmean(xs, pro)
+    np.testing.assert_array_equal(host(mu_gpu)[:, heads].view(np.uint32), mu.view(np.uint32))
+    smq = gen.sm_scale_q(c.D)
+    for layout, block, mean, sm in ((0, 128, None, smq), (1, 32, None, smq), (3, 128, None, smq), (0, 64, mu, 1.0),
+                                    (2, 64, mu, 1.0)):
+        res = sq.sq_quant_qk(xd, n, r, mu_gpu if mean is not None else None, sm, 1e-7, layout, block)
+        torch.cuda.synchronize()
+        codes, scales = O.quant_qk(xs, pro, layout, block, mean=mean, sm_scale=sm)
+        np.testing.assert_array_equal(host(res.scales)[:, heads].view(np.uint32), scales.view(np.uint32))
+        np.testing.assert_array_equal(host(res.codes)[:, :, heads], codes)
+        print("cfg4 layout %d ok" % layout, flush=True)
