@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized attention path on one MI355X (gfx950).
+
+A step is one pass of the whole path over one batch of seeded synthetic input, every
+stage in the library's HIP kernels:
+  video (default; the workload the TFLOPS metric is quoted on): B=1, H=40, D=128,
+    Sq=Sk=32760, 1% outlier channels x20 -> all-heads mean squares of q and k, k mean,
+    fused norm + RoPE + INT8 quantization of q (THREAD_Q) and k (THREAD_K, k mean
+    subtracted), V to FP8 per channel, attention core with FP8 P.V;
+  joint: the video recipe's projected pass at H=24, 8704 tokens (PER_BLOCK q 128 / k 64,
+    bf16 P.V) plus the 4096-token q8 prefix pass merged by log-sum-exp;
+  quantizer: k mean + the five quantizer runs of a 2 x 75600 x 40 x 128 tensor;
+  decode: paged GQA decode of 64 sequences over a q8 cache.
+value = the workload's algorithmic work / the step time (TFLOPS = 4 B H Sq Sk D for the
+attention workloads; GB/s of algorithmic bytes for the quantizer and decode).
+
+Prints ONE JSON line. roofline: the dominant kernel's algorithmic rate, from HIP events
+around its launches on the stream it runs on, against MI355X's published peak; traffic
+from the committed rocprofv3 counter summary when it was taken on the current kernel
+source. cpu_baseline: the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS_INT8 = 5000.0        # dense INT8 (and FP8) MFMA, POP/s -> TFLOP/s units
+PEAK_TFLOPS_BF16 = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "quantized_transformer_attention_amd", "csrc")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video", choices=["video", "joint", "quantizer", "decode", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
+    return ap.parse_args()
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, files, units_per_launch: float):
+    """HBM bytes per launch from the committed counter summary, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_sha") != source_sha(files) or e.get("units") != units_per_launch:
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream every library call enqueues on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def __call__(self, name, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+        return r
+
+    def avg_ms(self, name):
+        p = self.pairs.get(name, [])
+        return sum(s.elapsed_time(e) for s, e in p) / len(p) if p else float("nan")
+
+    def reset(self):
+        self.pairs = {}
+
+
+# ---------------------------------------------------------------------------------------------- workloads
+def video_like(args, torch, sq, gen, c, timer):
+    """Build the video-style pipeline (also the joint workload's projected pass)."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    inp = gen.attn_inputs(c)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qd, kd, vd = bf(inp.q), bf(inp.k), bf(inp.v)
+    table = torch.from_numpy(inp.table).to(dev)
+    wr = torch.from_numpy(inp.weight_rows).to(dev) if inp.weight_rows is not None else None
+    all_heads = c.norm == "all_heads"
+    mode = sq.NORM_ALL_HEADS if all_heads else sq.NORM_HEAD
+    wq, wk = bf(inp.wq), bf(inp.wk)
+    rope = sq.Rope(sq.ROPE_SPLIT_HALF, table)
+    ql, qb = gen.LAYOUT[c.q_layout], c.q_block
+    kl, kb = gen.LAYOUT[c.k_layout], c.k_block
+    smq = gen.sm_scale_q(c.D)
+    wsp = {n: sq.Workspace(dev) for n in ("kmean", "q", "k", "v", "attn")}
+    elems = c.B * c.Sq * c.H * c.D
+
+    def step():
+        if all_heads:
+            msq = timer("norm_stats_q", lambda: sq.sq_norm_stats(qd))
+            msk = timer("norm_stats_k", lambda: sq.sq_norm_stats(kd))
+        else:
+            msq = msk = None
+        nq = sq.Norm(mode, wq, wr, msq, c.eps)
+        nk = sq.Norm(mode, wk, wr, msk, c.eps)
+        mu = timer("kmean", lambda: sq.sq_kmean(kd, nk, rope, workspace=wsp["kmean"]))
+        q = timer("quant_q", lambda: sq.sq_quant_qk(qd, nq, rope, None, smq, 1e-7, ql, qb, workspace=wsp["q"]))
+        k = timer("quant_k", lambda: sq.sq_quant_qk(kd, nk, rope, mu, 1.0, 1e-7, kl, kb, workspace=wsp["k"]))
+        if c.pv == "fp8":
+            v8, vs = timer("quant_v", lambda: sq.sq_quant_v_fp8(vd, workspace=wsp["v"]))
+            out, lse = timer("attn", lambda: sq.sq_attn(q, k, v8, vs, 1.0, c.kv_tile, workspace=wsp["attn"]))
+        else:
+            out, lse = timer("attn", lambda: sq.sq_attn(q, k, vd, None, 1.0, c.kv_tile, workspace=wsp["attn"]))
+        return q, mu, out, lse
+
+    bytes_ = {
+        "norm_stats_q": elems * 2 + c.B * c.Sq * 4, "norm_stats_k": elems * 2 + c.B * c.Sk * 4,
+        "kmean": elems * 2, "quant_q": elems * 3, "quant_k": elems * 3, "quant_v": elems * 5,
+    }
+    return step, bytes_
+
+
+def run_video(args, torch, sq, gen, timer):
+    c = gen.CFG2
+    step, bytes_ = video_like(args, torch, sq, gen, c, timer)
+    flops = c.flops()
+    res = time_steps(args, torch, step, timer)
+    attn_ms = timer.avg_ms("attn")
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    files = ["attn.hip", "device.h", "sq_internal.h"]
+    line = {
+        "metric": "quantized-attention TFLOPS (4*B*H*Sq*Sk*d) and % of gfx950 INT8 MFMA peak",
+        "value": flops / (res["ms"] * 1e-3) / 1e12, "unit": "TFLOPS",
+        "dtype": "i8",
+        "config": {"workload": "video self-attention B=1 H=40 Sq=Sk=32760 d=128, THREAD_Q/THREAD_K INT8, FP8 P.V",
+                   "B": c.B, "H": c.H, "Sq": c.Sq, "Sk": c.Sk, "head_dim": c.D, "kv_tile": c.kv_tile},
+        "roofline": {"bound": "mfma", "kernel": "k_attn", "achieved": achieved, "peak": PEAK_TFLOPS_INT8,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS_INT8,
+                     "traffic": traffic_for("k_attn_video", files, flops),
+                     "avg_launch_ms": attn_ms, "flops_per_launch": flops},
+        "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
+        "stages_gbs": {n: b / (timer.avg_ms(n) * 1e-3) / 1e9 for n, b in bytes_.items()},
+        "core_pct_of_int8_peak": 100.0 * achieved / PEAK_TFLOPS_INT8,
+    }
+    return res, line
+
+
+def run_joint(args, torch, sq, gen, timer):
+    import numpy as np
+
+    c = gen.CFG3
+    step_proj, bytes_ = video_like(args, torch, sq, gen, c, timer)
+    dev = torch.device("cuda:0")
+    g = gen.rng(c.seed, gen.S_EXTRA)
+    kc, ks = gen.q8_like((1, c.prefix, c.Hk, c.D), g)
+    vc, vs = gen.q8_like((1, c.prefix, c.Hk, c.D), g)
+    f16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.float16).to(dev)
+    pre = sq.Q8Prefix(torch.from_numpy(kc).to(dev), f16(ks), torch.from_numpy(vc).to(dev), f16(vs))
+
+    def step():
+        q, mu, out, lse = step_proj()
+        timer("prefix", lambda: sq.sq_attn_prefix_lse_merge(q, pre, mu, out, lse, 1.0, c.kv_tile))
+
+    f_proj = c.flops()
+    f_pre = 4.0 * c.B * c.H * c.Sq * c.prefix * c.D
+    res = time_steps(args, torch, step, timer)
+    attn_ms, pre_ms = timer.avg_ms("attn"), timer.avg_ms("prefix")
+    achieved = f_proj / (attn_ms * 1e-3) / 1e12
+    line = {
+        "metric": "quantized-attention TFLOPS (4*B*H*Sq*Sk*d) and % of gfx950 INT8 MFMA peak",
+        "value": (f_proj + f_pre) / (res["ms"] * 1e-3) / 1e12, "unit": "TFLOPS", "dtype": "i8",
+        "config": {"workload": "joint text+image attention, 512 + 8192 projected tokens + 4096-token q8 prefix, "
+                               "H=24 d=128, bf16 P.V", "B": c.B, "H": c.H, "Sq": c.Sq, "Sk": c.Sk, "prefix": c.prefix,
+                   "head_dim": c.D, "kv_tile": c.kv_tile},
+        "roofline": {"bound": "mfma", "kernel": "k_attn", "achieved": achieved, "peak": PEAK_TFLOPS_INT8,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS_INT8, "traffic": None,
+                     "avg_launch_ms": attn_ms, "flops_per_launch": f_proj},
+        "prefix_pass": {"avg_ms": pre_ms, "tflops": f_pre / (pre_ms * 1e-3) / 1e12},
+        "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
+    }
+    return res, line
+
+
+def run_quantizer(args, torch, sq, gen, timer):
+    import numpy as np
+    c = gen.CFG4
+    dev = torch.device("cuda:0")
+    x, w, table = gen.quant_inputs(c)
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    del x
+    norm = sq.Norm(sq.NORM_HEAD, torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev), None, None, c.eps)
+    rope = sq.Rope(sq.ROPE_SPLIT_HALF, torch.from_numpy(table).to(dev))
+    smq = gen.sm_scale_q(c.D)
+    ws = sq.Workspace(dev)
+    runs = [("quant_q_per_block128", None, smq, 0, 128), ("quant_q_thread_q", None, smq, 1, 32),
+            ("quant_q_warp_q", None, smq, 3, 128), ("quant_k_per_block64", "mu", 1.0, 0, 64),
+            ("quant_k_thread_k", "mu", 1.0, 2, 64)]
+
+    def step():
+        mu = timer("kmean", lambda: sq.sq_kmean(xd, norm, rope, workspace=ws))
+        for name, m, sm, lay, blk in runs:
+            timer(name, lambda: sq.sq_quant_qk(xd, norm, rope, mu if m else None, sm, 1e-7, lay, blk))
+
+    elems = c.B * c.T * c.H * c.D
+    table_bytes = table.nbytes
+    bytes_ = {"kmean": elems * 2}
+    for name, *_ in runs:
+        bytes_[name] = elems * 3 + table_bytes
+    total = sum(bytes_.values())
+    res = time_steps(args, torch, step, timer)
+    qn = "quant_q_per_block128"
+    q_ms = timer.avg_ms(qn)
+    achieved = bytes_[qn] / (q_ms * 1e-3) / 1e9
+    line = {
+        "metric": "fused q/k quantizer GB/s (algorithmic bytes) and % of HBM peak",
+        "value": total / (res["ms"] * 1e-3) / 1e9, "unit": "GB/s", "dtype": "bf16->i8",
+        "config": {"workload": "quantizer B=2 T=75600 H=40 d=128: k mean + q PER_BLOCK(128), THREAD_Q, WARP_Q + "
+                               "k PER_BLOCK(64), THREAD_K", "B": c.B, "T": c.T, "H": c.H, "head_dim": c.D},
+        "roofline": {"bound": "hbm", "kernel": "k_quant_qk", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": q_ms,
+                     "bytes_per_launch": bytes_[qn]},
+        "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
+        "stages_gbs": {n: b / (timer.avg_ms(n) * 1e-3) / 1e9 for n, b in bytes_.items()},
+    }
+    return res, line
+
+
+def run_decode(args, torch, sq, gen, timer):
+    import numpy as np
+    c = gen.CFG5
+    dev = torch.device("cuda:0")
+    lens, bt, NB = gen.decode_layout(c)
+    g = gen.rng(c.seed, gen.S_EXTRA)
+    kc, ks = gen.q8_like((NB, c.bs, c.Hk, c.D), g)
+    vc, vs = gen.q8_like((NB, c.bs, c.Hk, c.D), g)
+    f16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.float16).to(dev)
+    kd, ksd, vd, vsd = torch.from_numpy(kc).to(dev), f16(ks), torch.from_numpy(vc).to(dev), f16(vs)
+    del kc, vc
+    q = torch.from_numpy(gen.decode_query(c).view(np.int16)).view(torch.bfloat16).to(dev)
+    btd, ld = torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev)
+    ws = sq.Workspace(dev)
+    out = torch.empty((c.N, c.Hq, c.D), dtype=torch.float32, device=dev)
+
+    def step():
+        timer("decode", lambda: sq.sq_paged_decode(q, kd, ksd, vd, vsd, btd, ld, c.lmax, c.scale, out=out,
+                                                   workspace=ws))
+
+    nbytes = int(lens.sum()) * c.Hk * (2 * c.D + 2 * 2 * (c.D // 32)) + q.numel() * 2 + out.numel() * 4
+    res = time_steps(args, torch, step, timer)
+    d_ms = timer.avg_ms("decode")
+    achieved = nbytes / (d_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged q8 decode GB/s (algorithmic bytes) and % of HBM peak",
+        "value": nbytes / (res["ms"] * 1e-3) / 1e9, "unit": "GB/s", "dtype": "i8",
+        "config": {"workload": "paged GQA decode, 64 sequences L~U(512,16384), 32 q / 8 kv heads, d=128, block 16, "
+                               "q8 cache", "num_seqs": c.N, "Hq": c.Hq, "Hk": c.Hk, "head_dim": c.D,
+                   "sum_len": int(lens.sum())},
+        "roofline": {"bound": "hbm", "kernel": "k_decode_split+k_decode_reduce", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "avg_launch_ms": d_ms, "bytes_per_launch": nbytes},
+    }
+    return res, line
+
+
+def time_steps(args, torch, step, timer):
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.reset()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return {"ms": (t1 - t0) * 1e3 / args.steps}
+
+
+# ---------------------------------------------------------------------------------------------- CPU baseline
+def cpu_baseline_video(args):
+    """The oracle's quantized attention core on sampled query rows (all 40 heads, all 32760 keys) of the video
+    workload's shapes: seeded INT8 codes and scales in THREAD_Q / THREAD_K layouts and FP8 values."""
+    import numpy as np
+
+    import gen
+    import oracle as O
+    c = gen.CFG2
+    g = np.random.default_rng(c.seed)
+    qc = g.integers(-127, 128, size=(1, c.Sq, c.H, c.D), dtype=np.int8)
+    kc = g.integers(-127, 128, size=(1, c.Sk, c.H, c.D), dtype=np.int8)
+    qs = g.uniform(1e-3, 4e-3, size=(1, c.H, O.scale_count(c.Sq, 1, 32))).astype(np.float32)
+    ks = g.uniform(1e-3, 4e-3, size=(1, c.H, O.scale_count(c.Sk, 2, 64))).astype(np.float32)
+    v8 = g.integers(0, 0x7f, size=(1, c.Sk, c.H, c.D), dtype=np.uint8) | (g.integers(0, 2, size=(1, c.Sk, c.H, c.D),
+                                                                                       dtype=np.uint8) << 7)
+    vs = np.full((1, c.H, c.D), 0.01, np.float32)
+    q, k = O.QK(qc, qs, 1, 32), O.QK(kc, ks, 2, 64)
+    rows_done, t_used, chunk = 0, 0.0, 8
+    while t_used < args.cpu_seconds and rows_done < c.Sq:
+        rows = np.arange(rows_done, rows_done + chunk, dtype=np.int64)
+        t0 = time.perf_counter()
+        O.attn(q, k, v8, True, vs, kv_tile=c.kv_tile, rows=rows, want_allow=False)
+        t_used += time.perf_counter() - t0
+        rows_done += chunk
+    flops = 4.0 * rows_done * c.H * c.Sk * c.D
+    return {"value": flops / t_used / 1e12, "unit": "TFLOPS", "cores": O.num_threads(), "kind": "oracle",
+            "sample": "quantized core (INT8 Q.K^T, FP32 softmax, FP8 P.V) on %d query rows x 40 heads x 32760 keys "
+                      "of the video workload, %.1f s" % (rows_done, t_used)}
+
+
+# ---------------------------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.exit("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus)
+    import torch
+
+    import gen
+    import quantized_transformer_attention_amd as sq
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    sq.lib()
+    timer = Timer(torch)
+    runners = {"video": run_video, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode}
+    if args.workload not in runners:
+        sys.exit("workload %s is not benchmarked yet" % args.workload)
+    print("bench: workload %s, warmup %d, steps %d" % (args.workload, args.warmup, args.steps), file=sys.stderr,
+          flush=True)
+    res, line = runners[args.workload](args, torch, sq, gen, timer)
+    out = {"metric": line.pop("metric"), "value": line.pop("value"), "unit": line.pop("unit"), "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": line.pop("dtype"), "data": "synthetic (seeded)",
+           "config": line.pop("config")}
+    out.update(line)
+    if not args.no_cpu_baseline and args.workload == "video":
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_video(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

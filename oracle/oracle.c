@@ -420,6 +420,12 @@ void orc_quant_v_fp8(const uint16_t* v, int64_t B, int64_t T, int64_t H, int64_t
  * hardware is within a few ulps, not correctly rounded) changes Pt, the largest
  * change |dPt| * |Vt_jc| joins a flip allowance, rescaled and normalized like
  * acc. The GPU result may differ from out by at most tolerance + allow.
+ * FP8 P.V adds a second allowance for the reduced-precision sum of an FP8 dot
+ * product (reading: an FP8 matrix unit may add a run of 8 consecutive products
+ * aligned to the largest of them, keeping 13 bits below its leading bit, as the
+ * 8-bit products carry at most 8 significant bits). Keys j = 8m .. 8m+7 form a
+ * run; with E the exponent of the run's largest |Pt Vt| and u = 2^(E - 13), a
+ * product that is not a multiple of u may lose up to min(|Pt Vt|, u).
  * ---------------------------------------------------------------------------- */
 typedef struct {
     int64_t B, S, H, D;       /* codes (B, S, H, D) */
@@ -431,6 +437,22 @@ typedef struct {
 static double pt_value(double p, int fp8) {
     float pf = (float)p;
     return fp8 ? e4m3_value(f32_e4m3(pf * 256.0f)) : (double)bf16_round(pf);
+}
+
+/* Bound of what a run of products loses when it is summed on a grid of 2^(E - 13),
+ * E the exponent of the run's largest magnitude (see the FP8 allowance above). */
+static double run_truncation_bound(const double* prod, int64_t n) {
+    double mx = 0.0, lost = 0.0;
+    for (int64_t j = 0; j < n; ++j) mx = fmax(mx, fabs(prod[j]));
+    if (mx == 0.0) return 0.0;
+    int E;
+    frexp(mx, &E);                          /* mx = f 2^E, f in [0.5, 1): leading bit 2^(E-1) */
+    const double u = ldexp(1.0, E - 1 - 13);
+    for (int64_t j = 0; j < n; ++j) {
+        double a = fabs(prod[j]);
+        if (fmod(a, u) != 0.0) lost += fmin(a, u);
+    }
+    return lost;
 }
 
 static double pt_flip(float p, int fp8, double flip_rel) {
@@ -459,6 +481,7 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                 double acc[512], al[512];
                 float* a = (float*)malloc(sizeof(float) * (size_t)kv_tile);
                 float* c = (float*)malloc(sizeof(float) * (size_t)kv_tile);
+                double* ptv = (double*)malloc(sizeof(double) * (size_t)kv_tile);
                 for (int64_t d = 0; d < D; ++d) acc[d] = al[d] = 0.0;
                 float m = -INFINITY;
                 double l = 0.0;
@@ -488,12 +511,26 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                         l += (double)p;
                         double pt = pt_value(p, fp8);
                         double fl = allow ? pt_flip(p, fp8, flip_rel) : 0.0;
+                        ptv[jj] = pt;
                         for (int64_t d = 0; d < D; ++d) {
                             int64_t vi = ((b * Sk + j) * Hk + hk) * D + d;
                             double vt = fp8 ? e4m3_value(((const uint8_t*)v)[vi]) : (double)bf16_f32(((const uint16_t*)v)[vi]);
                             acc[d] += pt * vt;
                             al[d] += fl * fabs(vt);
                         }
+                    }
+                    if (allow && fp8) {
+                        /* runs of 8 keys from key indices 8m (tiles start at multiples of 8) */
+                        for (int64_t d = 0; d < D; ++d)
+                            for (int64_t r0 = 0; r0 < n; r0 += 8) {
+                                double prod[8];
+                                int64_t rn = n - r0 < 8 ? n - r0 : 8;
+                                for (int64_t u = 0; u < rn; ++u) {
+                                    int64_t vi = ((b * Sk + j0 + r0 + u) * Hk + hk) * D + d;
+                                    prod[u] = ptv[r0 + u] * e4m3_value(((const uint8_t*)v)[vi]);
+                                }
+                                al[d] += run_truncation_bound(prod, rn);
+                            }
                     }
                     m = mn;
                 }
@@ -505,6 +542,7 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                 lse[(b * H + h) * nrows + ri] = (double)m + log2(l);
                 free(a);
                 free(c);
+                free(ptv);
             }
 }
 

@@ -133,6 +133,21 @@ def _ws(nbytes: int, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
+class Workspace:
+    """A reusable device workspace (grown on demand) for repeated calls, e.g. timing loops."""
+
+    def __init__(self, device):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf, self.buf.numel()
+
+
 def _rows(x: torch.Tensor) -> sq_rows:
     assert x.dtype == torch.bfloat16 and x.dim() == 4 and x.stride(3) == 1, "rows: bf16 (B, T, H, D), channels contiguous"
     B, T, H, D = x.shape
@@ -188,7 +203,8 @@ def sq_norm_stats(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def sq_kmean(k: torch.Tensor, norm: Optional[Norm] = None, rope: Optional[Rope] = None) -> torch.Tensor:
+def sq_kmean(k: torch.Tensor, norm: Optional[Norm] = None, rope: Optional[Rope] = None,
+             workspace: Optional[Workspace] = None) -> torch.Tensor:
     """Mean over tokens of the normalized, rotated k rows, FP32 (B, H, D)."""
     B, T, H, D = k.shape
     out = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
@@ -196,7 +212,8 @@ def sq_kmean(k: torch.Tensor, norm: Optional[Norm] = None, rope: Optional[Rope] 
     nc = norm.c() if norm is not None else None
     rc = rope.c() if rope is not None else None
     L = lib()
-    ws, nb = _ws(L.sq_kmean_workspace_bytes(ctypes.byref(r), ctypes.byref(nc) if nc else None), k.device)
+    need = L.sq_kmean_workspace_bytes(ctypes.byref(r), ctypes.byref(nc) if nc else None)
+    ws, nb = workspace.get(need) if workspace is not None else _ws(need, k.device)
     _check(L.sq_kmean(ctypes.byref(r), ctypes.byref(nc) if nc else None, ctypes.byref(rc) if rc else None, _ptr(out),
                       out.stride(0), out.stride(1), _ptr(ws), nb, _stream(k.device)))
     return out
@@ -219,7 +236,7 @@ class QK:
 
 def sq_quant_qk(x: torch.Tensor, norm: Optional[Norm] = None, rope: Optional[Rope] = None,
                 mean: Optional[torch.Tensor] = None, sm_scale: float = 1.0, scale_eps: float = 1e-7,
-                layout: int = LAYOUT_PER_BLOCK, block: int = 64) -> QK:
+                layout: int = LAYOUT_PER_BLOCK, block: int = 64, workspace: Optional[Workspace] = None) -> QK:
     """Fused norm + RoPE + mean + INT8 quantization of bf16 rows (B, T, H, D)."""
     B, T, H, D = x.shape
     n = sq_scale_count(T, layout, block)
@@ -231,7 +248,8 @@ def sq_quant_qk(x: torch.Tensor, norm: Optional[Norm] = None, rope: Optional[Rop
     nc = norm.c() if norm is not None else None
     rc = rope.c() if rope is not None else None
     L = lib()
-    ws, nb = _ws(L.sq_quant_qk_workspace_bytes(ctypes.byref(r), ctypes.byref(nc) if nc else None), x.device)
+    need = L.sq_quant_qk_workspace_bytes(ctypes.byref(r), ctypes.byref(nc) if nc else None)
+    ws, nb = workspace.get(need) if workspace is not None else _ws(need, x.device)
     _check(L.sq_quant_qk(ctypes.byref(r), ctypes.byref(nc) if nc else None, ctypes.byref(rc) if rc else None,
                          _ptr(mean), mean.stride(0) if mean is not None else 0,
                          mean.stride(1) if mean is not None else 0, sm_scale, scale_eps, layout, block, _ptr(codes),
@@ -240,7 +258,7 @@ def sq_quant_qk(x: torch.Tensor, norm: Optional[Norm] = None, rope: Optional[Rop
     return QK(codes, scales, layout, block)
 
 
-def sq_quant_v_fp8(v: torch.Tensor, token_stride: Optional[int] = None):
+def sq_quant_v_fp8(v: torch.Tensor, token_stride: Optional[int] = None, workspace: Optional[Workspace] = None):
     """bf16 V (B, T, H, D) -> FP8 e4m3fn codes channel-major (B, H, D, Tpad) as uint8, FP32 scales (B, H, D)."""
     B, T, H, D = v.shape
     tp = token_stride if token_stride is not None else (T + 127) // 128 * 128
@@ -248,7 +266,8 @@ def sq_quant_v_fp8(v: torch.Tensor, token_stride: Optional[int] = None):
     vs = torch.empty((B, H, D), dtype=torch.float32, device=v.device)
     r = _rows(v)
     L = lib()
-    ws, nb = _ws(L.sq_quant_v_fp8_workspace_bytes(ctypes.byref(r)), v.device)
+    need = L.sq_quant_v_fp8_workspace_bytes(ctypes.byref(r))
+    ws, nb = workspace.get(need) if workspace is not None else _ws(need, v.device)
     _check(L.sq_quant_v_fp8(ctypes.byref(r), _ptr(codes), codes.stride(0), codes.stride(1), codes.stride(2), _ptr(vs),
                             vs.stride(0), vs.stride(1), _ptr(ws), nb, _stream(v.device)))
     return codes, vs
@@ -262,21 +281,6 @@ def _values(v: torch.Tensor, v_scale: Optional[torch.Tensor]) -> sq_values:
     # channel-major (B, H, D, Tpad): element (b, s, h, c) at b*sb + h*sh + c*sd + s
     return sq_values(v.data_ptr(), SQ_FP8E4M3, v.stride(0), 1, v.stride(1), v.stride(2), v_scale.data_ptr(),
                      v_scale.stride(0), v_scale.stride(1))
-
-
-class Workspace:
-    """A reusable device workspace (grown on demand) for repeated calls, e.g. timing loops."""
-
-    def __init__(self, device):
-        self.device = device
-        self.buf = None
-
-    def get(self, nbytes: int):
-        if nbytes == 0:
-            return None, 0
-        if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        return self.buf, self.buf.numel()
 
 
 def sq_attn(q: QK, k: QK, v: torch.Tensor, v_scale: Optional[torch.Tensor] = None, score_scale: float = 1.0,

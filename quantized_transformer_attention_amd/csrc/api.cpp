@@ -242,3 +242,120 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------- C. q8 prefix pass + merge
+extern "C" {
+
+size_t sq_attn_prefix_lse_merge_workspace_bytes(const sq_qk* q, const sq_q8prefix* prefix) {
+    (void)q;
+    (void)prefix;
+    return 0;
+}
+
+int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const float* k_mean, int64_t mb, int64_t mh,
+                             float score_scale, int kv_tile, float* out, int64_t ob, int64_t ot, int64_t oh,
+                             float* lse, int64_t lb, int64_t lh, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    clear_error();
+    const char* what = "sq_attn_prefix_lse_merge";
+    int st = check_qk(q, what);
+    if (st) return st;
+    if (q->layout == SQ_LAYOUT_THREAD_K) return fail(SQ_ERR_UNSUPPORTED, "%s: q layout THREAD_K is a key layout", what);
+    if (!prefix) return fail(SQ_ERR_NULL, "%s: prefix descriptor is NULL", what);
+    const sq_q8prefix& p = *prefix;
+    if (p.B < 0 || p.P < 0 || p.Hk < 1) return fail(SQ_ERR_SHAPE, "%s: bad prefix sizes", what);
+    if (p.D != q->D) return fail(SQ_ERR_SHAPE, "%s: prefix head dim %lld differs from q's %lld", what,
+                                 (long long)p.D, (long long)q->D);
+    if (q->H % p.Hk) return fail(SQ_ERR_SHAPE, "%s: q heads %lld not a multiple of prefix kv heads %lld", what,
+                                 (long long)q->H, (long long)p.Hk);
+    if (p.B != 1 && p.B != q->B) return fail(SQ_ERR_SHAPE, "%s: prefix batch must be 1 or q's batch", what);
+    if (q->B * q->S * q->H == 0 || p.P == 0) return SQ_OK;
+    if (!p.k || !p.v || !p.k_scale || !p.v_scale) return fail(SQ_ERR_NULL, "%s: prefix tensors are NULL", what);
+    if (!out || !lse) return fail(SQ_ERR_NULL, "%s: out and lse (the projected pass) are required", what);
+    if ((reinterpret_cast<uintptr_t>(p.k) & 15) || (reinterpret_cast<uintptr_t>(p.v) & 15) || p.kb % 16 ||
+        p.kt % 16 || p.kh % 16 || p.vb % 16 || p.vt % 16 || p.vh % 16)
+        return fail(SQ_ERR_ALIGN, "%s: prefix code rows must start on 16-byte boundaries", what);
+    if ((reinterpret_cast<uintptr_t>(p.k_scale) & 1) || (reinterpret_cast<uintptr_t>(p.v_scale) & 1))
+        return fail(SQ_ERR_ALIGN, "%s: FP16 scales must be 2-byte aligned", what);
+    if (p.kb < 0 || p.kt < 0 || p.kh < 0 || p.vb < 0 || p.vt < 0 || p.vh < 0 || p.ksb < 0 || p.kst < 0 ||
+        p.ksh < 0 || p.vsb < 0 || p.vst < 0 || p.vsh < 0 || ob < 0 || ot < 0 || oh < 0 || lb < 0 || lh < 0)
+        return fail(SQ_ERR_STRIDE, "%s: negative stride", what);
+    if (k_mean && ((reinterpret_cast<uintptr_t>(k_mean) & 15) || mb % 4 || mh % 4 || mb < 0 || mh < 0))
+        return fail(SQ_ERR_ALIGN, "%s: k_mean rows must be 16-byte aligned", what);
+    if (kv_tile != 64 && kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: kv_tile must be 64 or 128", what);
+    if (!(score_scale > 0.0f) || !std::isfinite(score_scale))
+        return fail(SQ_ERR_SHAPE, "%s: score_scale must be finite and > 0", what);
+    PrefixArgs a{};
+    a.q = q->codes; a.B = q->B; a.Sq = q->S; a.H = q->H; a.D = q->D;
+    a.qsb = q->sb; a.qst = q->st; a.qsh = q->sh;
+    a.qs = q->scales; a.qssb = q->ssb; a.qssh = q->ssh; a.q_layout = q->layout; a.q_block = q->block;
+    a.PB = p.B; a.P = p.P; a.Hk = p.Hk;
+    a.k = p.k; a.kb = p.kb; a.kt = p.kt; a.kh = p.kh;
+    a.ks = p.k_scale; a.ksb = p.ksb; a.kst = p.kst; a.ksh = p.ksh;
+    a.v = p.v; a.vb = p.vb; a.vt = p.vt; a.vh = p.vh;
+    a.vs = p.v_scale; a.vsb = p.vsb; a.vst = p.vst; a.vsh = p.vsh;
+    a.mu = k_mean; a.mb = mb; a.mh = mh;
+    a.score_scale = score_scale;
+    a.kv_tile = kv_tile;
+    a.out = out; a.ob = ob; a.ot = ot; a.oh = oh;
+    a.lse = lse; a.lb = lb; a.lh = lh;
+    return launch_prefix(a, stream);
+}
+
+// ---------------------------------------------------------------------------- D. paged GQA decode
+size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_len) {
+    if (num_seqs <= 0 || Hq <= 0 || D <= 0 || max_seq_len <= 0) return 0;
+    const int64_t segs = (max_seq_len + kDecodeSeg - 1) / kDecodeSeg;
+    return round_up(sizeof(float) * static_cast<size_t>(num_seqs) * Hq * segs * (D + 2));
+}
+
+int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
+                    const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
+                    const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
+                    int max_seq_len, int Hq, int D, float softmax_scale, float* out, int64_t on, int64_t oh,
+                    void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* what = "sq_paged_decode";
+    if (num_seqs < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
+        return fail(SQ_ERR_SHAPE, "%s: bad sizes (num_seqs %d, Hq %d, Hk %d)", what, num_seqs, Hq, Hk);
+    if (D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", what, D);
+    if (block_size != 16) return fail(SQ_ERR_UNSUPPORTED, "%s: block_size %d (only 16)", what, block_size);
+    if (Hq % Hk) return fail(SQ_ERR_SHAPE, "%s: Hq %d not a multiple of Hk %d", what, Hq, Hk);
+    const int G = Hq / Hk;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: Hq / Hk = %d (1, 2, 4 or 8)", what, G);
+    if (num_seqs == 0) return SQ_OK;
+    if (max_seq_len < 1) return fail(SQ_ERR_SHAPE, "%s: max_seq_len must be >= 1", what);
+    if (!q || !k_cache || !k_scale || !v_cache || !v_scale || !block_table || !seq_lens || !out)
+        return fail(SQ_ERR_NULL, "%s: a required pointer is NULL", what);
+    if (bt_stride < (max_seq_len + block_size - 1) / block_size)
+        return fail(SQ_ERR_STRIDE, "%s: block-table rows (%lld entries) shorter than max_seq_len needs", what,
+                    (long long)bt_stride);
+    if ((reinterpret_cast<uintptr_t>(q) & 15) || qn % 8 || qh % 8 || qn < 0 || qh < 0)
+        return fail(SQ_ERR_ALIGN, "%s: q rows must start on 16-byte boundaries", what);
+    if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15))
+        return fail(SQ_ERR_ALIGN, "%s: caches must be 16-byte aligned", what);
+    if ((reinterpret_cast<uintptr_t>(k_scale) & 1) || (reinterpret_cast<uintptr_t>(v_scale) & 1))
+        return fail(SQ_ERR_ALIGN, "%s: FP16 scales must be 2-byte aligned", what);
+    if (on < 0 || oh < 0) return fail(SQ_ERR_STRIDE, "%s: negative output stride", what);
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+        return fail(SQ_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", what);
+    {
+        const int st = check_ws(ws, ws_bytes, sq_paged_decode_workspace_bytes(num_seqs, Hq, D, max_seq_len), what);
+        if (st) return st;
+    }
+    DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q); a.qn = qn; a.qh = qh;
+    a.kc = k_cache; a.ks = k_scale; a.vc = v_cache; a.vs = v_scale;
+    a.num_blocks = num_blocks; a.bs = block_size; a.Hk = Hk; a.Hq = Hq; a.D = D;
+    a.bt = block_table; a.bt_stride = bt_stride; a.lens = seq_lens;
+    a.N = num_seqs; a.max_len = max_seq_len;
+    a.scale = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);  // log2 units
+    a.out = out; a.on = on; a.oh = oh;
+    a.part = static_cast<float*>(ws);
+    a.segs = (max_seq_len + kDecodeSeg - 1) / kDecodeSeg;
+    return launch_decode(a, stream);
+}
+
+}  // extern "C"

@@ -33,15 +33,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int64_t scale_idx(int64_t t, int layout, int block) {
-    switch (layout) {
-    case SQ_LAYOUT_THREAD_Q: return 8 * (t >> 5) + (t & 7);
-    case SQ_LAYOUT_THREAD_K: return 4 * (t >> 6) + ((t & 7) >> 1);
-    case SQ_LAYOUT_WARP_Q: return 4 * (t >> 7) + ((t & 127) >> 5);
-    default: return t / block;
-    }
-}
-
 // 4 floats -> 4 e4m3 bytes of 256 x (the scaled convert divides by its scale, 2^-8).
 __device__ __forceinline__ int pack_fp8x4_256(float a, float b, float c, float d) {
     v2s r = {0, 0};

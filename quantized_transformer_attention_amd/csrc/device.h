@@ -4,6 +4,8 @@
 
 #include <cstdint>
 
+#include "../../include/sq.h"
+
 namespace sq {
 
 constexpr int kWave = 64;
@@ -37,6 +39,16 @@ __device__ __forceinline__ float div_rn(float v, float s, float y) {
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Scale index of token t in a row-group layout [quant] module docstring.
+__device__ __forceinline__ int64_t scale_idx(int64_t t, int layout, int block) {
+    switch (layout) {
+    case SQ_LAYOUT_THREAD_Q: return 8 * (t >> 5) + (t & 7);
+    case SQ_LAYOUT_THREAD_K: return 4 * (t >> 6) + ((t & 7) >> 1);
+    case SQ_LAYOUT_WARP_Q: return 4 * (t >> 7) + ((t & 127) >> 5);
+    default: return t / block;
+    }
 }
 
 template <typename T>

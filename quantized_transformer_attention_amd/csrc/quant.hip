@@ -320,8 +320,9 @@ __global__ __launch_bounds__(256) void k_v_fp8(QuantVArgs a) {
             unpack_bf16x8(*reinterpret_cast<const uint4*>(a.v + b * a.sb + t * a.st + h * a.sh + lc * 8), x);
 #pragma unroll
             for (int k = 0; k < 8; k += 2) {
-                float q0 = fminf(fmaxf(div_rn(x[k], vs[k], y[k]), -448.0f), 448.0f);
-                float q1 = fminf(fmaxf(div_rn(x[k + 1], vs[k + 1], y[k + 1]), -448.0f), 448.0f);
+                // the quotient keeps the sign of x (a -0 input gives the -0 code, 0x80)
+                float q0 = fminf(fmaxf(copysignf(div_rn(x[k], vs[k], y[k]), x[k]), -448.0f), 448.0f);
+                float q1 = fminf(fmaxf(copysignf(div_rn(x[k + 1], vs[k + 1], y[k + 1]), x[k + 1]), -448.0f), 448.0f);
                 const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
                 code[k] = static_cast<uint8_t>(pk & 0xff);
                 code[k + 1] = static_cast<uint8_t>((pk >> 8) & 0xff);

@@ -125,6 +125,9 @@ struct PrefixArgs {
     int64_t lb, lh;
 };
 
+// Positions per split-KV segment of the paged decode (one workgroup each).
+constexpr int kDecodeSeg = 512;
+
 struct DecodeArgs {
     const uint16_t* q;
     int64_t qn, qh;
@@ -141,8 +144,8 @@ struct DecodeArgs {
     float scale;
     float* out;
     int64_t on, oh;
-    float* part;                // split-KV partials (N, Hq, segs, D + 2)
-    int segs, seg_tiles;        // segments per sequence and 64-key tiles per segment
+    float* part;                // split-KV partials (N, Hq, segs, D + 2): acc, max, exp-sum
+    int segs;                   // segments per sequence: ceil(max_len / kDecodeSeg)
 };
 
 // ---------------------------------------------------------------- launchers (*.hip)
