@@ -211,6 +211,14 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
     a.kv_tile = kv_tile;
     a.out = out; a.ob = ob; a.ot = ot; a.oh = oh;
     a.lse = lse; a.lb = lb; a.lh = lh;
+    // the key loop addresses one (b, kv head) slice of K and of V^T with 32-bit byte offsets
+    constexpr int64_t kLim = int64_t(1) << 31;
+    if ((k->S + 256) * k->st >= kLim)
+        return fail(SQ_ERR_UNSUPPORTED, "sq_attn: one kv head's keys span more than 2 GiB (S * st)");
+    if (v->dtype == SQ_FP8E4M3 && (k->D * v->sd + 256) >= kLim)
+        return fail(SQ_ERR_UNSUPPORTED, "sq_attn: one kv head's FP8 values span more than 2 GiB");
+    if (v->dtype == SQ_BF16 && 2 * k->D * (padded_keys(k->S) + 256) >= kLim)
+        return fail(SQ_ERR_UNSUPPORTED, "sq_attn: one kv head's values span more than 2 GiB");
     if (v->dtype == SQ_FP8E4M3) {
         if (kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "sq_attn: FP8 P.V needs kv_tile 128");
         if (v->st != 1) return fail(SQ_ERR_STRIDE, "sq_attn: FP8 values must be channel-major (st == 1)");

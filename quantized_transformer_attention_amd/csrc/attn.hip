@@ -49,23 +49,216 @@ struct Cfg {
     static constexpr int NC = D / 64;                // 64-channel chunks of Q.K^T
     static constexpr int NCT = D / 16;               // 16-channel tiles of P.V
     static constexpr int KQ = KT / 4;                // keys per lane group
-    static constexpr int KSTR = D + 16;              // LDS K row stride, bytes
-    static constexpr int VSTR = FP8 ? KT + 16 : 2 * KT + 16;  // LDS V^T row stride, bytes
+    static constexpr int VB = FP8 ? 1 : 2;           // bytes per V element
+    static constexpr int RBV = KT * VB;              // bytes of one V^T row (one channel)
+    static constexpr int KBYTES = KT * D, VBYTES = D * RBV;
+    static constexpr int KSM = (D / 16 < 8 ? D / 16 : 8) - 1;   // slot swizzle masks
+    static constexpr int VSM = 7;
 };
 
-template <int D, int KT, bool FP8>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-    using C = Cfg<D, KT, FP8>;
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[KT * C::KSTR];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[D * C::VSTR];
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, g = l >> 4;
-    const int64_t h = blockIdx.y, b = blockIdx.z;
-    const int64_t hk = h / (a.H / a.Hk);
-    const int64_t q0 = static_cast<int64_t>(blockIdx.x) * C::QPB + w * (C::NQ * 16);
+// LDS tiles are rows of 16-byte slots; slot s of row r is stored at slot s ^ (r & mask)
+// so that the 16 rows one MFMA operand read touches spread over the LDS banks.
+template <int MASK>
+__device__ __forceinline__ int swz(int row, int slot) { return slot ^ (row & MASK); }
 
-    // Q codes as the B operand of S^T = K Q^T (held for the whole key loop), q scales
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+// Copies key tile [kbase, kbase + KT) of K (rows permuted: key kappa -> row 16 t + 4 G + i
+// with kappa = G KQ + 4 t + i) and of V^T straight from global memory into LDS with
+// buffer_load_dwordx4 ... lds: lane i of a wave fills bytes [16 i, 16 i + 16) of a 1 KB
+// piece. The buffer resources end at the last valid byte of the (b, kv head) slices, so
+// rows past the end read as zeros (their scores are masked) and can never fault.
+template <int D, int KT, bool FP8>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int kst, int vrow,
+                                         int kbase, uint8_t* kl, uint8_t* vl, int w, int lane) {
+    using C = Cfg<D, KT, FP8>;
+    constexpr int KCH = C::KBYTES / 1024, VCH = C::VBYTES / 1024;
+    // the per-lane offsets are a few integer ops: recompute them here rather than keep
+    // them live (in registers the whole key loop) across the tile's math
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int u = 0; u < (KCH + 3) / 4; ++u) {
+        const int piece = 4 * u + w;
+        if (KCH % 4 == 0 || piece < KCH) {
+            const int o = 1024 * piece + 16 * lane;
+            const int row = o / D, ls = swz<C::KSM>(row, (o % D) / 16);
+            const int key = kbase + ((row & 15) >> 2) * C::KQ + 4 * (row >> 4) + (row & 3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lvoid_t*)(kl + 1024 * piece), 16, key * kst + ls * 16, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < (VCH + 3) / 4; ++u) {
+        const int piece = 4 * u + w;
+        if (VCH % 4 == 0 || piece < VCH) {
+            const int o = 1024 * piece + 16 * lane;
+            const int row = o / C::RBV, ls = swz<C::VSM>(row, (o % C::RBV) / 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lvoid_t*)(vl + 1024 * piece), 16,
+                                                     row * vrow + kbase * C::VB + ls * 16, 0, 0, 0);
+        }
+    }
+}
+
+// s_waitcnt vmcnt(0): every global load of this wave (the tile copies included) has landed.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D, int KT, bool FP8>
+struct WaveState {
+    using C = Cfg<D, KT, FP8>;
     v4i qop[C::NQ][C::NC];
     float qsc[C::NQ];
+    float m_run[C::NQ], l_run[C::NQ];
+    v4f o[C::NQ][C::NCT];
+};
+
+// One key tile: S^T = K Q^T on INT8 MFMA, online softmax in base 2, acc += P V.
+template <int D, int KT, bool FP8, bool TAIL>
+__device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
+                                          const uint8_t* v_lds, int64_t kbase, const float* ksp, int lq, int g) {
+    using C = Cfg<D, KT, FP8>;
+    // c = RN(qs ks) per k-scale group of this lane group's keys
+    const int64_t kg0 = kbase + C::KQ * g;
+    float cg[C::NQ][4];
+    {
+        float ks[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (!TAIL || kg0 < a.Sk) {
+            if (a.k_layout == SQ_LAYOUT_THREAD_K) {
+                const int64_t base = 4 * (kg0 >> 6);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ks[q] = ksp[base + q];
+            } else {
+                const float sv = ksp[kg0 / a.k_block];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ks[q] = sv;
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < C::NQ; ++n)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float c = st.qsc[n] * ks[q];
+                if (a.score_scale != 1.0f) c = c * a.score_scale;
+                cg[n][q] = c;
+            }
+    }
+
+    // S^T = K Q^T (int32)
+    v4i s[C::NT][C::NQ];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+#pragma unroll
+        for (int n = 0; n < C::NQ; ++n) s[t][n] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int ch = 0; ch < C::NC; ++ch) {
+            const int row = 16 * t + lq;
+            const v4i kop = *reinterpret_cast<const v4i*>(k_lds + row * D + swz<C::KSM>(row, 4 * ch + g) * 16);
+#pragma unroll
+            for (int n = 0; n < C::NQ; ++n) s[t][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, st.qop[n][ch], s[t][n], 0, 0, 0);
+        }
+    }
+
+    // online softmax, P operands
+    v8i pf8[C::NQ];
+    v8bf pbf[C::NQ][KT / 32];
+#pragma unroll
+    for (int n = 0; n < C::NQ; ++n) {
+        int amx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (TAIL && kg0 + 4 * t + i >= a.Sk) s[t][n][i] = INT32_MIN;
+                const int q = 2 * (t & 1) + (i >> 1);
+                amx[q] = max(amx[q], s[t][n][i]);
+            }
+        float mt = -__builtin_inff();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float mq = static_cast<float>(amx[q]) * cg[n][q];
+            if (!TAIL || amx[q] != INT32_MIN) mt = fmaxf(mt, mq);
+        }
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+        const float mo = st.m_run[n];
+        const float mn = fmaxf(mo, mt);
+        const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+        st.m_run[n] = mn;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = 2 * (t & 1) + (i >> 1);
+                const int av = s[t][n][i];
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(av), cg[n][q], -mn));
+                if (TAIL && av == INT32_MIN) pv = 0.0f;
+                p[i] = pv;
+                lsum += pv;
+            }
+            if constexpr (FP8) {
+                pf8[n][t] = pack_fp8x4_256(p[0], p[1], p[2], p[3]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pbf[n][t >> 1][4 * (t & 1) + i] = static_cast<__bf16>(p[i]);
+            }
+        }
+        st.l_run[n] = st.l_run[n] * alpha + lsum;
+        // rescale the accumulator rows (query 4 g + i of this n-tile) when a max moved
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct][i] *= ai;
+            }
+        }
+    }
+
+    // acc += Pt Vt
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) {
+        const int row = ct * 16 + lq;
+        if constexpr (FP8) {
+            const v4i lo = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VSM>(row, 2 * g) * 16);
+            const v4i hi = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VSM>(row, 2 * g + 1) * 16);
+            const v8i vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int n = 0; n < C::NQ; ++n)
+                st.o[n][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf8[n], vop, st.o[n][ct], 0, 0, 0, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int u = 0; u < KT / 32; ++u) {
+                const int ls = (C::KQ * g + 8 * u) / 8;       // 16-byte slot of keys KQ g + 8 u .. + 7
+                const v8bf vop = *reinterpret_cast<const v8bf*>(v_lds + row * C::RBV + swz<C::VSM>(row, ls) * 16);
+#pragma unroll
+                for (int n = 0; n < C::NQ; ++n)
+                    st.o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pbf[n][u], vop, st.o[n][ct], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Work items (b, h, query block) are handed out so that the workgroups that run on
+// one XCD at the same time (dispatch sends workgroup i to XCD i mod 8) share a head:
+// XCD x takes the contiguous item range [x per, (x + 1) per), in order.
+__device__ __forceinline__ int64_t xcd_item(int64_t L, int64_t per) { return (L & 7) * per + (L >> 3); }
+
+template <int D, int KT, bool FP8>
+__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
+    using C = Cfg<D, KT, FP8>;
+    __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::KBYTES + C::VBYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::KBYTES + C::VBYTES];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, g = l >> 4;
+    const int64_t nqb = (a.Sq + C::QPB - 1) / C::QPB;
+    const int64_t items = nqb * a.H * a.B;
+    const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
+    if (item >= items) return;  // uniform over the workgroup
+    const int64_t qb = item % nqb, h = (item / nqb) % a.H, b = item / (nqb * a.H);
+    const int64_t hk = h / (a.H / a.Hk);
+    const int64_t q0 = qb * C::QPB + w * (C::NQ * 16);
+
+    WaveState<D, KT, FP8> st;
 #pragma unroll
     for (int n = 0; n < C::NQ; ++n) {
         const int64_t qi = q0 + n * 16 + lq;
@@ -73,195 +266,55 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int ch = 0; ch < C::NC; ++ch) {
             v4i z = {0, 0, 0, 0};
-            qop[n][ch] = ok ? *reinterpret_cast<const v4i*>(a.q + b * a.qsb + qi * a.qst + h * a.qsh + ch * 64 + 16 * g) : z;
+            st.qop[n][ch] = ok ? *reinterpret_cast<const v4i*>(a.q + b * a.qsb + qi * a.qst + h * a.qsh + ch * 64 + 16 * g) : z;
         }
-        qsc[n] = ok ? a.qs[b * a.qssb + h * a.qssh + scale_idx(qi, a.q_layout, a.q_block)] : 0.0f;
+        st.qsc[n] = ok ? a.qs[b * a.qssb + h * a.qssh + scale_idx(qi, a.q_layout, a.q_block)] : 0.0f;
+        st.m_run[n] = -__builtin_inff();
+        st.l_run[n] = 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    float m_run[C::NQ], l_run[C::NQ];
-    v4f o[C::NQ][C::NCT];
+    const int8_t* kb = a.k + b * a.ksb + hk * a.ksh;
+    const uint8_t* vb = static_cast<const uint8_t*>(a.v) + (b * a.vsb + hk * a.vsh) * C::VB;
+    const float* ksp = a.ks + b * a.kssb + hk * a.kssh;
+    const bool tail = a.Sk % KT != 0;
+    const int ntiles = static_cast<int>((a.Sk + KT - 1) / KT);
+    const int last = ntiles - 1;
+    const int kst = static_cast<int>(a.kst), vrow = static_cast<int>(a.vsd) * C::VB;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kb), 0, static_cast<int>((a.Sk - 1) * a.kst + D), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), 0, D * vrow, 0x00020000);
+    // tile j streams into buffer j % 2 while tile j - 1 is processed from the other one
+    auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, l); };
+    auto step = [&](int j, const uint8_t* buf) {
+        if (tail && j == last) tile_step<D, KT, FP8, true>(a, st, buf, buf + C::KBYTES, static_cast<int64_t>(j) * KT, ksp, lq, g);
+        else tile_step<D, KT, FP8, false>(a, st, buf, buf + C::KBYTES, static_cast<int64_t>(j) * KT, ksp, lq, g);
+    };
+    copy(0, buf0);
+    wait_vm();
+    __syncthreads();
+    for (int j = 0; j < ntiles; j += 2) {
+        if (j + 1 < ntiles) copy(j + 1, buf1);
+        step(j, buf0);
+        wait_vm();
+        __syncthreads();
+        if (j + 1 >= ntiles) break;
+        if (j + 2 < ntiles) copy(j + 2, buf0);
+        step(j + 1, buf1);
+        wait_vm();
+        __syncthreads();
+    }
+
+    // epilogue: l over the 4 lane groups, lse, out = acc / l (x vs / 256)
 #pragma unroll
     for (int n = 0; n < C::NQ; ++n) {
-        m_run[n] = -__builtin_inff();
-        l_run[n] = 0.0f;
-#pragma unroll
-        for (int ct = 0; ct < C::NCT; ++ct) o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-
-    const int64_t ntiles = (a.Sk + KT - 1) / KT;
-    const int8_t* kbase_ptr = a.k + b * a.ksb + hk * a.ksh;
-    for (int64_t tile = 0; tile < ntiles; ++tile) {
-        const int64_t kbase = tile * KT;
-        __syncthreads();
-        // ---- stage K (rows permuted: key kappa -> row 16 t + 4 G + ii) and V^T
-        for (int j = tid; j < KT * D / 16; j += 256) {
-            const int kappa = j / (D / 16), part = j % (D / 16);
-            const int64_t key = kbase + kappa;
-            v4i val = {0, 0, 0, 0};
-            if (key < a.Sk) val = *reinterpret_cast<const v4i*>(kbase_ptr + key * a.kst + part * 16);
-            const int G4 = kappa / C::KQ, rem = kappa % C::KQ;
-            const int row = 16 * (rem >> 2) + 4 * G4 + (rem & 3);
-            *reinterpret_cast<v4i*>(k_lds + row * C::KSTR + part * 16) = val;
-        }
-        if constexpr (FP8) {
-            const uint8_t* vb = static_cast<const uint8_t*>(a.v) + b * a.vsb + hk * a.vsh;
-            for (int j = tid; j < D * KT / 16; j += 256) {
-                const int c = j / (KT / 16), part = j % (KT / 16);
-                const int64_t key = kbase + part * 16;
-                v4i val = {0, 0, 0, 0};
-                if (key < a.Sk) val = *reinterpret_cast<const v4i*>(vb + c * a.vsd + key);
-                *reinterpret_cast<v4i*>(v_lds + c * C::VSTR + part * 16) = val;
-            }
-        } else {
-            const uint16_t* vb = static_cast<const uint16_t*>(a.v) + b * a.vsb + hk * a.vsh;
-            for (int j = tid; j < D * KT / 8; j += 256) {
-                const int c = j / (KT / 8), part = j % (KT / 8);
-                const int64_t key = kbase + part * 8;
-                v4i val = {0, 0, 0, 0};
-                if (key < a.Sk) val = *reinterpret_cast<const v4i*>(vb + c * a.vsd + key);
-                *reinterpret_cast<v4i*>(v_lds + c * C::VSTR + part * 16) = val;
-            }
-        }
-        __syncthreads();
-
-        // ---- c = RN(qs ks) per k-scale group of this lane group's keys
-        const int64_t kg0 = kbase + C::KQ * g;
-        float cg[C::NQ][4];
-        {
-            float ks[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (kg0 < a.Sk) {
-                const float* kp = a.ks + b * a.kssb + hk * a.kssh;
-                if (a.k_layout == SQ_LAYOUT_THREAD_K) {
-                    const int64_t base = 4 * (kg0 >> 6);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) ks[q] = kp[base + q];
-                } else {
-                    const float s = kp[kg0 / a.k_block];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) ks[q] = s;
-                }
-            }
-#pragma unroll
-            for (int n = 0; n < C::NQ; ++n)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float c = qsc[n] * ks[q];
-                    if (a.score_scale != 1.0f) c = c * a.score_scale;
-                    cg[n][q] = c;
-                }
-        }
-
-        // ---- S^T = K Q^T (int32)
-        v4i s[C::NT][C::NQ];
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t) {
-#pragma unroll
-            for (int n = 0; n < C::NQ; ++n) s[t][n] = v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int ch = 0; ch < C::NC; ++ch) {
-                const v4i kop = *reinterpret_cast<const v4i*>(k_lds + (16 * t + lq) * C::KSTR + ch * 64 + 16 * g);
-#pragma unroll
-                for (int n = 0; n < C::NQ; ++n) s[t][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, qop[n][ch], s[t][n], 0, 0, 0);
-            }
-        }
-
-        const bool partial = kbase + KT > a.Sk;
-        // ---- online softmax, P operands
-        v8i pf8[C::NQ];
-        v8bf pbf[C::NQ][KT / 32];
-#pragma unroll
-        for (int n = 0; n < C::NQ; ++n) {
-            int amx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
-#pragma unroll
-            for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    int av = s[t][n][i];
-                    if (partial && kg0 + 4 * t + i >= a.Sk) {
-                        av = INT32_MIN;
-                        s[t][n][i] = INT32_MIN;
-                    }
-                    const int q = 2 * (t & 1) + (i >> 1);
-                    amx[q] = max(amx[q], av);
-                }
-            float mt = -__builtin_inff();
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (amx[q] != INT32_MIN) mt = fmaxf(mt, static_cast<float>(amx[q]) * cg[n][q]);
-            mt = fmaxf(mt, shfl_xor(mt, 16));
-            mt = fmaxf(mt, shfl_xor(mt, 32));
-            const float mo = m_run[n];
-            const float mn = fmaxf(mo, mt);
-            const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-            m_run[n] = mn;
-            float lsum = 0.0f;
-            float p[C::NT][4];
-#pragma unroll
-            for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int q = 2 * (t & 1) + (i >> 1);
-                    const int av = s[t][n][i];
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(av), cg[n][q], -mn));
-                    if (partial && av == INT32_MIN) pv = 0.0f;
-                    p[t][i] = pv;
-                    lsum += pv;
-                }
-            l_run[n] = l_run[n] * alpha + lsum;
-            if constexpr (FP8) {
-#pragma unroll
-                for (int t = 0; t < C::NT; ++t) pf8[n][t] = pack_fp8x4_256(p[t][0], p[t][1], p[t][2], p[t][3]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < KT / 32; ++u) {
-                    v8bf x;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        x[i] = static_cast<__bf16>(p[2 * u][i]);
-                        x[4 + i] = static_cast<__bf16>(p[2 * u + 1][i]);
-                    }
-                    pbf[n][u] = x;
-                }
-            }
-            // rescale the accumulator rows (query 4 g + i of this n-tile) when a max moved
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * g + i, kWave);
-#pragma unroll
-                    for (int ct = 0; ct < C::NCT; ++ct) o[n][ct][i] *= ai;
-                }
-            }
-        }
-
-        // ---- acc += Pt Vt
-#pragma unroll
-        for (int ct = 0; ct < C::NCT; ++ct) {
-            if constexpr (FP8) {
-                const v8i vop = *reinterpret_cast<const v8i*>(v_lds + (ct * 16 + lq) * C::VSTR + 32 * g);
-#pragma unroll
-                for (int n = 0; n < C::NQ; ++n)
-                    o[n][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf8[n], vop, o[n][ct], 0, 0, 0, 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int u = 0; u < KT / 32; ++u) {
-                    const v8bf vop = *reinterpret_cast<const v8bf*>(v_lds + (ct * 16 + lq) * C::VSTR + 2 * (C::KQ * g + 8 * u));
-#pragma unroll
-                    for (int n = 0; n < C::NQ; ++n)
-                        o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pbf[n][u], vop, o[n][ct], 0, 0, 0);
-                }
-            }
-        }
-    }
-
-    // ---- epilogue: l over the 4 lane groups, lse, out = acc / l (x vs / 256)
-#pragma unroll
-    for (int n = 0; n < C::NQ; ++n) {
-        float lt = l_run[n];
+        float lt = st.l_run[n];
         lt = lt + shfl_xor(lt, 16);
         lt = lt + shfl_xor(lt, 32);
         const int64_t qi = q0 + n * 16 + lq;
-        if (a.lse && g == 0 && qi < a.Sq) a.lse[b * a.lb + h * a.lh + qi] = m_run[n] + log2f(lt);
+        if (a.lse && g == 0 && qi < a.Sq) a.lse[b * a.lb + h * a.lh + qi] = st.m_run[n] + log2f(lt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float li = __shfl(lt, 4 * g + i, kWave);
@@ -272,7 +325,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
             for (int ct = 0; ct < C::NCT; ++ct) {
                 const int c = ct * 16 + lq;
-                float val = o[n][ct][i] * inv;
+                float val = st.o[n][ct][i] * inv;
                 if constexpr (FP8) val = val * (a.vscale[b * a.vssb + hk * a.vssh + c] * 0.00390625f);
                 op[c] = val;
             }
@@ -322,7 +375,8 @@ int launch_v_transpose(const VTransposeArgs& a, void* stream) {
 
 int launch_attn(const AttnArgs& a, void* stream) {
     if (a.B * a.Sq * a.H == 0) return SQ_OK;
-    dim3 grid(static_cast<unsigned>((a.Sq + 127) / 128), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
+    const int64_t items = (a.Sq + 127) / 128 * a.H * a.B;
+    dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
     hipStream_t s = S(stream);
     if (a.v_fp8) {
         if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 128, true>), grid, dim3(256), 0, s, a);
