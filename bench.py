@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video", choices=["video", "joint", "quantizer", "decode", "tiny"])
+    ap.add_argument("--workload", default="video", choices=["video", "joint", "quantizer", "decode", "copy"],
+                    help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
     return ap.parse_args()
@@ -286,6 +287,22 @@ def run_decode(args, torch, sq, gen, timer):
     return res, line
 
 
+def run_copy(args, torch, sq, gen, timer):
+    """A plain device-to-device copy of 1 GiB: the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE."""
+    dev = torch.device("cuda:0")
+    x = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    res = time_steps(args, torch, lambda: timer("copy", lambda: y.copy_(x)), timer)
+    nbytes = 2 * x.numel() * 2
+    ms = timer.avg_ms("copy")
+    line = {"metric": "device copy GB/s (read + write)", "value": nbytes / (res["ms"] * 1e-3) / 1e9, "unit": "GB/s",
+            "dtype": "bf16", "config": {"workload": "copy 1 GiB", "bytes_read": nbytes // 2, "bytes_written": nbytes // 2},
+            "roofline": {"bound": "hbm", "kernel": "copy", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                         "avg_launch_ms": ms}}
+    return res, line
+
+
 def time_steps(args, torch, step, timer):
     for _ in range(args.warmup):
         step()
@@ -343,7 +360,7 @@ def main():
         sys.exit("bench.py needs a GPU")
     sq.lib()
     timer = Timer(torch)
-    runners = {"video": run_video, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode}
+    runners = {"video": run_video, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode, "copy": run_copy}
     if args.workload not in runners:
         sys.exit("workload %s is not benchmarked yet" % args.workload)
     print("bench: workload %s, warmup %d, steps %d" % (args.workload, args.warmup, args.steps), file=sys.stderr,
