@@ -165,8 +165,9 @@ int sq_norm_stats(const sq_rows* x, float* mean_sq, int64_t msb, int64_t mst, vo
 /* ---- A2. k mean [quant] norm_rope_mean: mean over tokens of the normalized,
  * rotated rows per (b, head), FP32, written to mean[b*mb + h*mh + c]. Partial sums
  * per 64-row block in a fixed order (row 4i + r of a block joins partial r in
- * ascending i; the block's sum is (S0 + S1) + (S2 + S3); blocks added in ascending
- * order; divided by T), so the result is bit-reproducible. `norm` may be NULL
+ * ascending i; the block's sum is (S0 + S1) + (S2 + S3); block sums added in chunks of
+ * 16 consecutive blocks, ascending within a chunk, and the chunk sums added in
+ * ascending order; divided by T), so the result is bit-reproducible. `norm` may be NULL
  * (no norm); `rope` may be NULL (no rotation). */
 size_t sq_kmean_workspace_bytes(const sq_rows* k, const sq_norm* norm);
 int sq_kmean(const sq_rows* k, const sq_norm* norm, const sq_rope* rope, float* mean, int64_t mb, int64_t mh,

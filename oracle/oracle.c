@@ -281,8 +281,9 @@ void orc_prologue_rows(const orc_rows* r, float* out /* (B, T, H, D) */) {
  * Canonical order (reading; the pages fix only "FP32 partials per block, then a
  * sum over blocks, divided by the token count"): in a block, row t = 4i + r
  * (i = 0..15) joins partial S_r in ascending i, from zero; the block's partial is
- * (S_0 + S_1) + (S_2 + S_3); the blocks are added in ascending order from zero;
- * the total is divided by T. Rows at or beyond T add zero.
+ * (S_0 + S_1) + (S_2 + S_3); the blocks are added in chunks of 16 consecutive
+ * blocks (ascending within a chunk, from zero), the chunk sums in ascending order
+ * from zero; the total is divided by T. Rows at or beyond T add zero.
  * ---------------------------------------------------------------------------- */
 void orc_kmean(const orc_rows* rin, float* mean /* (B, H, D) */) {
     orc_rows r = *rin;
@@ -293,8 +294,8 @@ void orc_kmean(const orc_rows* rin, float* mean /* (B, H, D) */) {
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int64_t b = 0; b < r.B; ++b)
         for (int64_t h = 0; h < r.H; ++h) {
-            float total[512], S[4][512], z[512];
-            for (int64_t c = 0; c < D; ++c) total[c] = 0.0f;
+            float total[512], chunk[512], S[4][512], z[512];
+            for (int64_t c = 0; c < D; ++c) total[c] = chunk[c] = 0.0f;
             for (int64_t blk = 0; blk < nblk; ++blk) {
                 for (int k = 0; k < 4; ++k)
                     for (int64_t c = 0; c < D; ++c) S[k][c] = 0.0f;
@@ -304,7 +305,9 @@ void orc_kmean(const orc_rows* rin, float* mean /* (B, H, D) */) {
                         prologue(&r, b, t, h, (ms && t < r.T) ? ms[b * r.T + t] : 0.0f, z);
                         for (int64_t c = 0; c < D; ++c) S[k][c] = S[k][c] + z[c];
                     }
-                for (int64_t c = 0; c < D; ++c) total[c] = total[c] + ((S[0][c] + S[1][c]) + (S[2][c] + S[3][c]));
+                for (int64_t c = 0; c < D; ++c) chunk[c] = chunk[c] + ((S[0][c] + S[1][c]) + (S[2][c] + S[3][c]));
+                if (blk % 16 == 15 || blk == nblk - 1)
+                    for (int64_t c = 0; c < D; ++c) { total[c] = total[c] + chunk[c]; chunk[c] = 0.0f; }
             }
             for (int64_t c = 0; c < D; ++c) mean[(b * r.H + h) * D + c] = total[c] / (float)r.T;
         }

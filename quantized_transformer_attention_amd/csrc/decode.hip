@@ -44,16 +44,32 @@ __device__ __forceinline__ void unpack_i8x16(const uint4& u, float* f) {
 
 template <int G>
 __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
+    constexpr int ST = kTpw / 8;          // 8-position steps per wave
+    constexpr int PG = kTpw / 16;         // pages per wave
     __shared__ float sc[kSeg * G];
     __shared__ float red[4 * G * kD];
     __shared__ float wred[4 * G];
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lc = l & 7, tr = l >> 3;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lc = l & 7, tr = l >> 3;
     const int seg = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
     const int L = min(a.lens[n], a.max_len);
     const int s0 = seg * kSeg;
     if (s0 >= L) return;  // uniform over the workgroup
     const int s1 = min(L, s0 + kSeg);
+    const int wp0 = s0 + w * kTpw;        // first position of this wave (a multiple of 16)
     const int32_t* bt = a.bt + static_cast<int64_t>(n) * a.bt_stride;
+
+    // the physical block of each of the wave's pages (one table read per page; -1 if unused or invalid)
+    int myblk = -1;
+    if (l < PG && wp0 + 16 * l < s1) {
+        const int b = bt[(wp0 >> 4) + l];
+        myblk = (b >= 0 && b < a.num_blocks) ? b : -1;
+    }
+    int64_t rowbase[PG];
+#pragma unroll
+    for (int pg = 0; pg < PG; ++pg) {
+        const int b = __builtin_amdgcn_readlane(myblk, pg);
+        rowbase[pg] = b < 0 ? -1 : static_cast<int64_t>(b) * 16 * a.Hk + hk;   // row of slot 0, this kv head
+    }
 
     // the G query heads of this kv head, channels 16 lc .. 16 lc + 15, in log2 units
     float q[G][16];
@@ -67,31 +83,31 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
         for (int c = 0; c < 16; ++c) q[h][c] = f[c] * a.scale;
     }
 
-    // ---- pass 1: scores of the segment's positions
-    for (int st = 0; st < kTpw / 8; ++st) {
-        const int tl = w * kTpw + st * 8 + tr;
-        const int pos = s0 + tl;
+    // ---- pass 1: every key load of the wave in flight at once, then the scores
+    uint4 kraw[ST];
+    float ksc[ST];
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+        const int pos = wp0 + 8 * st + tr;
+        const int64_t rb = rowbase[st >> 1];
+        const bool ok = rb >= 0 && pos < s1;
+        const int64_t row = rb + static_cast<int64_t>(8 * (st & 1) + tr) * a.Hk;
+        kraw[st] = ok ? *reinterpret_cast<const uint4*>(a.kc + row * kD + 16 * lc) : make_uint4(0, 0, 0, 0);
+        ksc[st] = ok ? f16_to_f32(a.ks[row * (kD / 32) + (lc >> 1)]) : 0.0f;
+    }
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+        const int pos = wp0 + 8 * st + tr;
+        const bool ok = rowbase[st >> 1] >= 0 && pos < s1;
+        float kf[16];
+        unpack_i8x16(kraw[st], kf);
         float part[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) part[h] = 0.0f;
-        bool ok = pos < s1;
-        int64_t row = 0;
-        if (ok) {
-            const int phys = bt[pos >> 4];
-            ok = phys >= 0 && phys < a.num_blocks;
-            row = (static_cast<int64_t>(phys) * 16 + (pos & 15)) * a.Hk + hk;
-        }
-        if (ok) {
-            float kf[16];
-            unpack_i8x16(*reinterpret_cast<const uint4*>(a.kc + row * kD + 16 * lc), kf);
-            const float ks = f16_to_f32(a.ks[row * (kD / 32) + (lc >> 1)]);
+        for (int h = 0; h < G; ++h) {
+            float d = q[h][0] * kf[0];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float d = q[h][0] * kf[0];
-#pragma unroll
-                for (int c = 1; c < 16; ++c) d = __builtin_fmaf(q[h][c], kf[c], d);
-                part[h] = d * ks;
-            }
+            for (int c = 1; c < 16; ++c) d = __builtin_fmaf(q[h][c], kf[c], d);
+            part[h] = d * ksc[st];
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -101,8 +117,20 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
         }
         if (lc == 0) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) sc[tl * G + h] = ok ? part[h] : -__builtin_inff();
+            for (int h = 0; h < G; ++h) sc[(w * kTpw + 8 * st + tr) * G + h] = ok ? part[h] : -__builtin_inff();
         }
+    }
+    // the value loads go out before the segment max is formed
+    uint4 vraw[ST];
+    float vsc[ST];
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+        const int pos = wp0 + 8 * st + tr;
+        const int64_t rb = rowbase[st >> 1];
+        const bool ok = rb >= 0 && pos < s1;
+        const int64_t row = rb + static_cast<int64_t>(8 * (st & 1) + tr) * a.Hk;
+        vraw[st] = ok ? *reinterpret_cast<const uint4*>(a.vc + row * kD + 16 * lc) : make_uint4(0, 0, 0, 0);
+        vsc[st] = ok ? f16_to_f32(a.vs[row * (kD / 32) + (lc >> 1)]) : 0.0f;
     }
     __syncthreads();
 
@@ -121,7 +149,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     for (int h = 0; h < G; ++h)
         M[h] = fmaxf(fmaxf(wred[h], wred[G + h]), fmaxf(wred[2 * G + h], wred[3 * G + h]));
 
-    // ---- pass 2: p = 2^(s - M), acc += p * v
+    // ---- pass 2: p = 2^(s - M), acc += p * v (missing positions have s = -inf: p = 0, v = 0)
     float acc[G][16], ls[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -129,24 +157,22 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 #pragma unroll
         for (int c = 0; c < 16; ++c) acc[h][c] = 0.0f;
     }
-    for (int st = 0; st < kTpw / 8; ++st) {
-        const int tl = w * kTpw + st * 8 + tr;
-        const int pos = s0 + tl;
-        if (pos >= s1) break;  // positions only grow with st
-        const int phys = bt[pos >> 4];
-        if (phys < 0 || phys >= a.num_blocks) continue;
-        const int64_t row = (static_cast<int64_t>(phys) * 16 + (pos & 15)) * a.Hk + hk;
-        float vf[16];
-        unpack_i8x16(*reinterpret_cast<const uint4*>(a.vc + row * kD + 16 * lc), vf);
-        const float vsc = f16_to_f32(a.vs[row * (kD / 32) + (lc >> 1)]);
+    const bool any = M[0] > -__builtin_inff();   // every head's max is finite iff a position exists
+    if (any) {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) vf[c] = vf[c] * vsc;
+        for (int st = 0; st < ST; ++st) {
+            const int tl = w * kTpw + 8 * st + tr;
+            float vf[16];
+            unpack_i8x16(vraw[st], vf);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float p = __builtin_amdgcn_exp2f(sc[tl * G + h] - M[h]);
-            ls[h] += p;
+            for (int c = 0; c < 16; ++c) vf[c] = vf[c] * vsc[st];
 #pragma unroll
-            for (int c = 0; c < 16; ++c) acc[h][c] = __builtin_fmaf(p, vf[c], acc[h][c]);
+            for (int h = 0; h < G; ++h) {
+                const float p = __builtin_amdgcn_exp2f(sc[tl * G + h] - M[h]);
+                ls[h] += p;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc[h][c] = __builtin_fmaf(p, vf[c], acc[h][c]);
+            }
         }
     }
     // reduce over the 8 token lanes of each channel slice, then over the 4 waves

@@ -185,13 +185,31 @@ __global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
     }
 }
 
+// One workgroup per (b, h): block sums are added in chunks of 16 consecutive blocks
+// (ascending within a chunk), the chunk sums in ascending order, then divided by T.
+// The chunks of a group of 32 are summed in parallel, their sums kept in LDS.
 __global__ __launch_bounds__(256) void k_kmean_final(KmeanArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x, D = a.r.D;
-    if (i >= a.r.B * a.r.H * D) return;
-    const int64_t c = i % D, bh = i / D, b = bh / a.r.H, h = bh % a.r.H;
+    constexpr int CG = 32, CB = 16;
+    __shared__ float cs[CG * 128];
+    const int64_t D = a.r.D, bh = blockIdx.x, b = bh / a.r.H, h = bh % a.r.H;
+    const int tid = threadIdx.x, c = tid % D, r = tid / D, rpw = 256 / D;
+    const float* part = a.partial + bh * a.nblk * D;
+    const int64_t nchunk = (a.nblk + CB - 1) / CB;
     float tot = 0.0f;
-    for (int64_t blk = 0; blk < a.nblk; ++blk) tot = tot + a.partial[(bh * a.nblk + blk) * D + c];
-    a.mean[b * a.mb + h * a.mh + c] = tot / static_cast<float>(a.r.T);
+    for (int64_t g0 = 0; g0 < nchunk; g0 += CG) {
+        const int ng = static_cast<int>(nchunk - g0 < CG ? nchunk - g0 : CG);
+        for (int j = r; j < ng; j += rpw) {
+            const int64_t blk0 = (g0 + j) * CB, blk1 = blk0 + CB < a.nblk ? blk0 + CB : a.nblk;
+            float s = 0.0f;
+            for (int64_t blk = blk0; blk < blk1; ++blk) s = s + part[blk * D + c];
+            cs[j * D + c] = s;
+        }
+        __syncthreads();
+        if (tid < D)
+            for (int j = 0; j < ng; ++j) tot = tot + cs[j * D + c];
+        __syncthreads();
+    }
+    if (tid < D) a.mean[b * a.mb + h * a.mh + c] = tot / static_cast<float>(a.r.T);
 }
 
 // ---------------------------------------------------------------- A3: fused q/k quantization
@@ -404,8 +422,7 @@ int launch_kmean(const KmeanArgs& a, void* stream) {
         if (a.r.D == 128) launch_kmean_d<128>(a, grid, S(stream));
         else launch_kmean_d<64>(a, grid, S(stream));
     }
-    const int64_t n = a.r.B * a.r.H * a.r.D;
-    hipLaunchKernelGGL(k_kmean_final, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, S(stream), a);
+    hipLaunchKernelGGL(k_kmean_final, dim3(static_cast<unsigned>(a.r.B * a.r.H)), dim3(256), 0, S(stream), a);
     return check_launch("sq_kmean");
 }
 
