@@ -52,14 +52,21 @@ struct Cfg {
     static constexpr int VB = FP8 ? 1 : 2;           // bytes per V element
     static constexpr int RBV = KT * VB;              // bytes of one V^T row (one channel)
     static constexpr int KBYTES = KT * D, VBYTES = D * RBV;
-    static constexpr int KSM = (D / 16 < 8 ? D / 16 : 8) - 1;   // slot swizzle masks
-    static constexpr int VSM = 7;
+    static constexpr int KNS = D / 16, VNS = RBV / 16;   // 16-byte slots per K row and per V^T row
 };
 
-// LDS tiles are rows of 16-byte slots; slot s of row r is stored at slot s ^ (r & mask)
-// so that the 16 rows one MFMA operand read touches spread over the LDS banks.
-template <int MASK>
-__device__ __forceinline__ int swz(int row, int slot) { return slot ^ (row & MASK); }
+// LDS tiles are rows of 16-byte slots; slot s of row r is stored at slot s ^ f(r) so that
+// the rows one MFMA operand read touches (consecutive rows, one slot each) land in
+// distinct bank groups, whether the LDS serves 8 or 16 such lanes per cycle:
+//   8 slots per row (128 B):  f(r) = (r & 7) ^ ((r >> 3) & 1)
+//   4 slots per row (64 B):   f(r) = (r >> 1) & 3
+//   16 slots per row (256 B): f(r) = r & 15
+template <int NS>
+__device__ __forceinline__ int swz(int row, int slot) {
+    if constexpr (NS == 8) return slot ^ ((row & 7) ^ ((row >> 3) & 1));
+    else if constexpr (NS == 4) return slot ^ ((row >> 1) & 3);
+    else return slot ^ (row & 15);
+}
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
@@ -82,7 +89,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buf
         const int piece = 4 * u + w;
         if (KCH % 4 == 0 || piece < KCH) {
             const int o = 1024 * piece + 16 * lane;
-            const int row = o / D, ls = swz<C::KSM>(row, (o % D) / 16);
+            const int row = o / D, ls = swz<C::KNS>(row, (o % D) / 16);
             const int key = kbase + ((row & 15) >> 2) * C::KQ + 4 * (row >> 4) + (row & 3);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lvoid_t*)(kl + 1024 * piece), 16, key * kst + ls * 16, 0, 0, 0);
         }
@@ -92,7 +99,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buf
         const int piece = 4 * u + w;
         if (VCH % 4 == 0 || piece < VCH) {
             const int o = 1024 * piece + 16 * lane;
-            const int row = o / C::RBV, ls = swz<C::VSM>(row, (o % C::RBV) / 16);
+            const int row = o / C::RBV, ls = swz<C::VNS>(row, (o % C::RBV) / 16);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lvoid_t*)(vl + 1024 * piece), 16,
                                                      row * vrow + kbase * C::VB + ls * 16, 0, 0, 0);
         }
@@ -147,13 +154,12 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
 #pragma unroll
-        for (int n = 0; n < C::NQ; ++n) s[t][n] = v4i{0, 0, 0, 0};
-#pragma unroll
         for (int ch = 0; ch < C::NC; ++ch) {
             const int row = 16 * t + lq;
-            const v4i kop = *reinterpret_cast<const v4i*>(k_lds + row * D + swz<C::KSM>(row, 4 * ch + g) * 16);
+            const v4i kop = *reinterpret_cast<const v4i*>(k_lds + row * D + swz<C::KNS>(row, 4 * ch + g) * 16);
 #pragma unroll
-            for (int n = 0; n < C::NQ; ++n) s[t][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, st.qop[n][ch], s[t][n], 0, 0, 0);
+            for (int n = 0; n < C::NQ; ++n)
+                s[t][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, st.qop[n][ch], ch == 0 ? v4i{0, 0, 0, 0} : s[t][n], 0, 0, 0);
         }
     }
 
@@ -220,8 +226,8 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
     for (int ct = 0; ct < C::NCT; ++ct) {
         const int row = ct * 16 + lq;
         if constexpr (FP8) {
-            const v4i lo = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VSM>(row, 2 * g) * 16);
-            const v4i hi = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VSM>(row, 2 * g + 1) * 16);
+            const v4i lo = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VNS>(row, 2 * g) * 16);
+            const v4i hi = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VNS>(row, 2 * g + 1) * 16);
             const v8i vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
             for (int n = 0; n < C::NQ; ++n)
@@ -230,7 +236,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
 #pragma unroll
             for (int u = 0; u < KT / 32; ++u) {
                 const int ls = (C::KQ * g + 8 * u) / 8;       // 16-byte slot of keys KQ g + 8 u .. + 7
-                const v8bf vop = *reinterpret_cast<const v8bf*>(v_lds + row * C::RBV + swz<C::VSM>(row, ls) * 16);
+                const v8bf vop = *reinterpret_cast<const v8bf*>(v_lds + row * C::RBV + swz<C::VNS>(row, ls) * 16);
 #pragma unroll
                 for (int n = 0; n < C::NQ; ++n)
                     st.o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pbf[n][u], vop, st.o[n][ct], 0, 0, 0);

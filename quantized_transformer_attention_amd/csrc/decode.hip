@@ -50,7 +50,9 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     __shared__ float red[4 * G * kD];
     __shared__ float wred[4 * G];
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lc = l & 7, tr = l >> 3;
-    const int seg = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
+    // kv head fastest in the grid: the workgroups of one segment's 8 heads run together, so
+    // the rows of every cache slot (all heads side by side in NHD) are read in one window
+    const int hk = blockIdx.x, seg = blockIdx.y, n = blockIdx.z;
     const int L = min(a.lens[n], a.max_len);
     const int s0 = seg * kSeg;
     if (s0 >= L) return;  // uniform over the workgroup
@@ -95,6 +97,18 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
         kraw[st] = ok ? *reinterpret_cast<const uint4*>(a.kc + row * kD + 16 * lc) : make_uint4(0, 0, 0, 0);
         ksc[st] = ok ? f16_to_f32(a.ks[row * (kD / 32) + (lc >> 1)]) : 0.0f;
     }
+    // the value loads go out with the key loads: both streams in flight before any math
+    uint4 vraw[ST];
+    float vsc[ST];
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+        const int pos = wp0 + 8 * st + tr;
+        const int64_t rb = rowbase[st >> 1];
+        const bool ok = rb >= 0 && pos < s1;
+        const int64_t row = rb + static_cast<int64_t>(8 * (st & 1) + tr) * a.Hk;
+        vraw[st] = ok ? *reinterpret_cast<const uint4*>(a.vc + row * kD + 16 * lc) : make_uint4(0, 0, 0, 0);
+        vsc[st] = ok ? f16_to_f32(a.vs[row * (kD / 32) + (lc >> 1)]) : 0.0f;
+    }
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
         const int pos = wp0 + 8 * st + tr;
@@ -119,18 +133,6 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 #pragma unroll
             for (int h = 0; h < G; ++h) sc[(w * kTpw + 8 * st + tr) * G + h] = ok ? part[h] : -__builtin_inff();
         }
-    }
-    // the value loads go out before the segment max is formed
-    uint4 vraw[ST];
-    float vsc[ST];
-#pragma unroll
-    for (int st = 0; st < ST; ++st) {
-        const int pos = wp0 + 8 * st + tr;
-        const int64_t rb = rowbase[st >> 1];
-        const bool ok = rb >= 0 && pos < s1;
-        const int64_t row = rb + static_cast<int64_t>(8 * (st & 1) + tr) * a.Hk;
-        vraw[st] = ok ? *reinterpret_cast<const uint4*>(a.vc + row * kD + 16 * lc) : make_uint4(0, 0, 0, 0);
-        vsc[st] = ok ? f16_to_f32(a.vs[row * (kD / 32) + (lc >> 1)]) : 0.0f;
     }
     __syncthreads();
 
@@ -236,7 +238,7 @@ inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 int launch_decode(const DecodeArgs& a, void* stream) {
     if (a.N == 0) return SQ_OK;
     const int G = a.Hq / a.Hk;
-    dim3 g1(static_cast<unsigned>(a.segs), static_cast<unsigned>(a.Hk), static_cast<unsigned>(a.N));
+    dim3 g1(static_cast<unsigned>(a.Hk), static_cast<unsigned>(a.segs), static_cast<unsigned>(a.N));
     switch (G) {
     case 1: hipLaunchKernelGGL(k_decode_split<1>, g1, dim3(256), 0, S(stream), a); break;
     case 2: hipLaunchKernelGGL(k_decode_split<2>, g1, dim3(256), 0, S(stream), a); break;

@@ -126,7 +126,7 @@ struct PrefixArgs {
 };
 
 // Positions per split-KV segment of the paged decode (one workgroup each).
-constexpr int kDecodeSeg = 512;
+constexpr int kDecodeSeg = 256;
 
 struct DecodeArgs {
     const uint16_t* q;
