@@ -102,7 +102,8 @@ typedef struct {
  * (FP32). SPLIT_HALF pairs channel p with p + pairs; INTERLEAVED pairs 2p with
  * 2p + 1; channels >= 2*pairs pass through. rb = 0 serves every batch item.
  * A (..., pairs, 2) table has rp = 2, rc = 1; 2x2 matrices [[cos,-sin],[sin,cos]]
- * (..., pairs, 2, 2) have rp = 4, rc = 2. SPLIT_HALF needs pairs % 8 == 0. */
+ * (..., pairs, 2, 2) have rp = 4, rc = 2. SPLIT_HALF rotates all D/2 pairs (pairs == D/2);
+ * INTERLEAVED takes any pairs <= D/2. */
 typedef struct {
     sq_rope_mode mode;
     const float* table;
@@ -158,8 +159,9 @@ int64_t sq_scale_count(int64_t T, sq_layout layout, int block);
 /* ---- A1. Per-token mean of squares over all heads [kit] HeadGroup.mean_squares,
  * joint_qkv_attention's mean squares by head groups. mean_sq[b*msb + t*mst] =
  * (sum over heads in ascending order of the head's sum of squares) / (H*D), FP32;
- * each head's sum in the canonical order: D/8 partials of 8 contiguous channels
- * (x0*x0, then fma per channel), combined by an xor butterfly (offsets D/16 .. 1). */
+ * each head's sum in the canonical order: D/8 partials, partial l over channels
+ * 4l .. 4l+3 then D/2 + 4l .. D/2 + 4l + 3 (x*x for the first, then fma per channel),
+ * combined by an xor butterfly (offsets D/16 .. 1). */
 int sq_norm_stats(const sq_rows* x, float* mean_sq, int64_t msb, int64_t mst, void* stream);
 
 /* ---- A2. k mean [quant] norm_rope_mean: mean over tokens of the normalized,

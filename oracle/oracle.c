@@ -154,17 +154,20 @@ typedef struct {
 /*
  * Sum of squares of one row in the canonical order (reading: the pages fix the
  * order only for their own lane layout). The row splits into n = D/8 partial
- * sums of 8 contiguous channels: p = x0*x0, then p = fma(xk, xk, p) for k = 1..7.
- * An xor butterfly over the n partials (offsets n/2, ..., 1) then adds each
- * partial to its partner; every partial ends equal, and partial 0 is the sum.
+ * sums; partial l takes channels 4l .. 4l+3 and then D/2 + 4l .. D/2 + 4l + 3 (each
+ * channel with its split-half rotation partner): p = x*x for the first, then
+ * p = fma(x, x, p) for the other 7 in that order. An xor butterfly over the n
+ * partials (offsets n/2, ..., 1) then adds each partial to its partner; every
+ * partial ends equal, and partial 0 is the sum.
  */
 static float sumsq_canonical(const float* x, int64_t D) {
     int n = (int)(D / 8);
     float p[64], q[64];
     for (int l = 0; l < n; ++l) {
-        const float* c = x + 8 * l;
-        float s = c[0] * c[0];
-        for (int k = 1; k < 8; ++k) s = fmaf(c[k], c[k], s);
+        int ch[8];
+        for (int k = 0; k < 4; ++k) { ch[k] = 4 * l + k; ch[4 + k] = (int)(D / 2) + 4 * l + k; }
+        float s = x[ch[0]] * x[ch[0]];
+        for (int k = 1; k < 8; ++k) s = fmaf(x[ch[k]], x[ch[k]], s);
         p[l] = s;
     }
     for (int off = n / 2; off >= 1; off /= 2) {

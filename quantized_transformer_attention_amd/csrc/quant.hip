@@ -4,13 +4,18 @@
 // norm_rope_mean, norm_rope_quantize) and [kit] WanGP shared/attention_kit.py
 // (HeadGroup.mean_squares).
 //
-// Row layout in a wavefront: a row of D bf16 channels is D/8 lanes x 16 bytes, so
-// one 128-bit load per lane per row; D = 128 puts 4 rows in a wave, D = 64 puts 8.
-// Per-row reductions (sum of squares, |v| max) are xor butterflies inside the
-// row's lanes; the split-half rotation partner is the lane pairs/8 away.
+// Row layout in a wavefront: a row of D bf16 channels is D/8 lanes; lane l holds the
+// 4 channels [4l, 4l + 4) and their split-half rotation partners [D/2 + 4l, D/2 + 4l + 4)
+// (two 8-byte loads), so the full split-half rotation and the interleaved rotation are
+// lane-local (no cross-lane exchange) and each lane needs the cos/sin of only 4 pairs.
+// D = 128 puts 4 rows in a wave, D = 64 puts 8. Per-row reductions (sum of squares,
+// |v| max) are xor butterflies inside the row's lanes.
 // The quantizer keeps a whole 128-row tile of one head in registers (32 rows per
 // wave), so x is read from HBM once and the norm and rotation run once per element,
 // then reduces the layout's group maxima in LDS and writes codes from registers.
+// Work items (token tile, b, h) go out head-fastest and XCD-contiguous (workgroup i runs
+// on XCD i mod 8), so the heads of a token tile share that tile's RoPE table rows in
+// one XCD's L2 instead of fetching them from memory once per head.
 #include "device.h"
 #include "sq_internal.h"
 
@@ -18,8 +23,26 @@ namespace sq {
 
 namespace {
 
+// x[0..3] = channels 4 lc .. 4 lc + 3, x[4..7] = channels D/2 + 4 lc .. D/2 + 4 lc + 3.
+template <int D>
+__device__ __forceinline__ void load_row_bf16(const uint16_t* row, int lc, float* x) {
+    const uint2 u = *reinterpret_cast<const uint2*>(row + 4 * lc);
+    const uint2 v = *reinterpret_cast<const uint2*>(row + D / 2 + 4 * lc);
+    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+    x[4] = bf16_lo(v.x); x[5] = bf16_hi(v.x); x[6] = bf16_lo(v.y); x[7] = bf16_hi(v.y);
+}
+
+template <int D>
+__device__ __forceinline__ void load_row_f32(const float* row, int lc, float* x) {
+    const float4 u = *reinterpret_cast<const float4*>(row + 4 * lc);
+    const float4 v = *reinterpret_cast<const float4*>(row + D / 2 + 4 * lc);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+}
+
 // Canonical sum of squares of a row: per lane p = x0*x0 then fma over the other 7
-// channels; xor butterfly over the row's LPR lanes (offsets LPR/2 .. 1).
+// channels in the order held (4l .. 4l+3, D/2 + 4l .. D/2 + 4l + 3); xor butterfly
+// over the row's LPR lanes (offsets LPR/2 .. 1).
 template <int LPR>
 __device__ __forceinline__ float row_sumsq(const float* x) {
     float p = x[0] * x[0];
@@ -30,17 +53,37 @@ __device__ __forceinline__ float row_sumsq(const float* x) {
     return p;
 }
 
-// Row prologue [quant] _rows: z = rotate(bf16(norm(x) * w)) for the 8 channels
-// lc*8 .. lc*8+7 of row (b, t, h). Every lane of the wave must call it (shuffles);
+// cos and sin of pairs p0 .. p0 + 3 of a table row
+template <bool CONTIG>
+__device__ __forceinline__ void load_pairs4(const float* tb, const RowArgs& a, int64_t p0, float* cs, float* sn) {
+    if constexpr (CONTIG) {
+        const float4 u = *reinterpret_cast<const float4*>(tb + 2 * p0);
+        const float4 v = *reinterpret_cast<const float4*>(tb + 2 * p0 + 4);
+        cs[0] = u.x; sn[0] = u.y; cs[1] = u.z; sn[1] = u.w;
+        cs[2] = v.x; sn[2] = v.y; cs[3] = v.z; sn[3] = v.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            cs[k] = tb[a.rp * (p0 + k)];
+            sn[k] = tb[a.rp * (p0 + k) + a.rc];
+        }
+    }
+}
+
+// Row prologue [quant] _rows: z = rotate(bf16(norm(x) * w)) for the 8 channels a lane
+// holds of row (b, t, h). Every lane of the row must call it (the norm's butterfly);
 // rows with valid == false read nothing and their result is unspecified.
-template <int D, int NORM, int ROPE>
+// ROPE_SPLIT_HALF here rotates all D/2 pairs (the entry point checks pairs == D/2).
+template <int D, int NORM, int ROPE, bool CONTIG>
 __device__ __forceinline__ void row_prologue(const RowArgs& a, int64_t b, int64_t t, int64_t h, int lc, bool valid,
                                              float* z) {
     constexpr int LPR = D / 8;
     float x[8], y[8];
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (valid) raw = *reinterpret_cast<const uint4*>(a.x + b * a.sb + t * a.st + h * a.sh + lc * 8);
-    unpack_bf16x8(raw, x);
+    if (valid) load_row_bf16<D>(a.x + b * a.sb + t * a.st + h * a.sh, lc, x);
+    else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+    }
     if constexpr (NORM == SQ_NORM_NONE) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) y[k] = x[k];
@@ -53,9 +96,8 @@ __device__ __forceinline__ void row_prologue(const RowArgs& a, int64_t b, int64_
         }
         const float inv = 1.0f / sqrtf(ms + a.eps);
         const int64_t wrow = (a.wrows && valid) ? a.wrows[t] : 0;
-        const uint16_t* wp = a.w + wrow * a.wd + (NORM == SQ_NORM_ALL_HEADS ? h * D : 0) + lc * 8;
         float w[8];
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(wp), w);
+        load_row_bf16<D>(a.w + wrow * a.wd + (NORM == SQ_NORM_ALL_HEADS ? h * D : 0), lc, w);
 #pragma unroll
         for (int k = 0; k < 8; ++k) y[k] = bf16_round((x[k] * inv) * w[k]);
     }
@@ -63,43 +105,24 @@ __device__ __forceinline__ void row_prologue(const RowArgs& a, int64_t b, int64_
 #pragma unroll
         for (int k = 0; k < 8; ++k) z[k] = y[k];
     } else if constexpr (ROPE == SQ_ROPE_SPLIT_HALF) {
-        const int p8 = static_cast<int>(a.pairs / 8);          // lanes per half
-        const bool lead = lc < p8, trail = lc >= p8 && lc < 2 * p8;
-        const int lane = threadIdx.x & (kWave - 1);
-        const int src = lane + (lead ? p8 : (trail ? -p8 : 0));
-        float o[8];
+        // channel 4 lc + k (leading) with its partner D/2 + 4 lc + k (trailing), pair 4 lc + k
+        float cs[4], sn[4];
+        if (valid) load_pairs4<CONTIG>(a.table + a.rb * b + a.rs * t, a, 4 * lc, cs, sn);
+        else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = __shfl(y[k], src, kWave);
-        if ((lead || trail) && valid) {
-            const int64_t pair0 = lead ? lc * 8 : lc * 8 - a.pairs;
-            const float* tb = a.table + a.rb * b + a.rs * t;
-            float cs[8], sn[8];
-            if (a.rope_contig) {
-                const float4* p = reinterpret_cast<const float4*>(tb + 2 * pair0);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    float4 f = p[k];
-                    cs[2 * k] = f.x; sn[2 * k] = f.y; cs[2 * k + 1] = f.z; sn[2 * k + 1] = f.w;
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    cs[k] = tb[a.rp * (pair0 + k)];
-                    sn[k] = tb[a.rp * (pair0 + k) + a.rc];
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                z[k] = lead ? __builtin_fmaf(cs[k], y[k], (-sn[k]) * o[k]) : __builtin_fmaf(sn[k], o[k], cs[k] * y[k]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) z[k] = y[k];
+            for (int k = 0; k < 4; ++k) { cs[k] = 1.0f; sn[k] = 0.0f; }
         }
-    } else {  // interleaved: channel 2p with 2p + 1, both in this lane
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            z[k] = __builtin_fmaf(cs[k], y[k], (-sn[k]) * y[4 + k]);
+            z[4 + k] = __builtin_fmaf(sn[k], y[k], cs[k] * y[4 + k]);
+        }
+    } else {  // interleaved: channel 2p with 2p + 1; pairs 2 lc, 2 lc + 1 and D/4 + 2 lc, D/4 + 2 lc + 1
         const float* tb = a.table + a.rb * b + a.rs * t;
 #pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-            const int64_t pair = lc * 4 + k / 2;
+        for (int u = 0; u < 4; ++u) {
+            const int64_t pair = (u < 2 ? 0 : D / 4) + 2 * lc + (u & 1);
+            const int k = 2 * u;
             if (valid && pair < a.pairs) {
                 const float cs = tb[a.rp * pair], sn = tb[a.rp * pair + a.rc];
                 z[k] = __builtin_fmaf(cs, y[k], (-sn) * y[k + 1]);
@@ -130,6 +153,9 @@ __host__ __device__ __forceinline__ int groups_per_tile(int layout, int block) {
     }
 }
 
+// Work item of workgroup L when XCD x = L mod 8 takes the contiguous range [x per, (x + 1) per).
+__device__ __forceinline__ int64_t xcd_item(int64_t L, int64_t per) { return (L & 7) * per + (L >> 3); }
+
 // ---------------------------------------------------------------- A1: mean squares over all heads
 template <int D>
 __global__ __launch_bounds__(256) void k_norm_stats(NormStatsArgs a) {
@@ -141,10 +167,12 @@ __global__ __launch_bounds__(256) void k_norm_stats(NormStatsArgs a) {
     float tot = 0.0f;
     for (int64_t h0 = 0; h0 < a.H; h0 += HPI) {
         const int64_t h = h0 + lr;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (h < a.H) raw = *reinterpret_cast<const uint4*>(a.x + b * a.sb + t * a.st + h * a.sh + lc * 8);
         float x[8];
-        unpack_bf16x8(raw, x);
+        if (h < a.H) load_row_bf16<D>(a.x + b * a.sb + t * a.st + h * a.sh, lc, x);
+        else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+        }
         const float p = row_sumsq<LPR>(x);
 #pragma unroll
         for (int j = 0; j < HPI; ++j) {
@@ -156,13 +184,16 @@ __global__ __launch_bounds__(256) void k_norm_stats(NormStatsArgs a) {
 }
 
 // ---------------------------------------------------------------- A2: k mean
-// One wave per 64-row block: row 4i + r (i = 0..15) joins partial r; the block's
-// sum is (S0 + S1) + (S2 + S3), written to partial (b, h, blk, :).
-template <int D, int NORM, int ROPE>
+// One wave per 64-row block, 4 blocks per workgroup: row 4i + r (i = 0..15) joins
+// partial r; the block's sum is (S0 + S1) + (S2 + S3), written to partial (b, h, blk, :).
+template <int D, int NORM, int ROPE, bool CONTIG>
 __global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
     constexpr int LPR = D / 8;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lc = lane % LPR, r = lane / LPR;
-    const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + w, h = blockIdx.y, b = blockIdx.z;
+    const int64_t nbg = (a.nblk + 3) / 4, items = nbg * a.r.B * a.r.H;
+    const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
+    if (item >= items) return;  // uniform over the workgroup
+    const int64_t h = item % a.r.H, b = (item / a.r.H) % a.r.B, blk = (item / (a.r.H * a.r.B)) * 4 + w;
     if (blk >= a.nblk) return;  // wave-uniform
     const bool active = r < 4;
     float S[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -170,7 +201,7 @@ __global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
         const int64_t t = blk * 64 + 4 * i + r;
         const bool valid = active && t < a.r.T;
         float z[8];
-        row_prologue<D, NORM, ROPE>(a.r, b, t, h, lc, valid, z);
+        row_prologue<D, NORM, ROPE, CONTIG>(a.r, b, t, h, lc, valid, z);
 #pragma unroll
         for (int k = 0; k < 8; ++k) S[k] = S[k] + (valid ? z[k] : 0.0f);
     }
@@ -179,9 +210,9 @@ __global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) S[k] = S[k] + shfl_xor(S[k], 2 * LPR);
     if (r == 0) {
-        float4* dst = reinterpret_cast<float4*>(a.partial + ((b * a.r.H + h) * a.nblk + blk) * D + lc * 8);
-        dst[0] = make_float4(S[0], S[1], S[2], S[3]);
-        dst[1] = make_float4(S[4], S[5], S[6], S[7]);
+        float* dst = a.partial + ((b * a.r.H + h) * a.nblk + blk) * D;
+        *reinterpret_cast<float4*>(dst + 4 * lc) = make_float4(S[0], S[1], S[2], S[3]);
+        *reinterpret_cast<float4*>(dst + D / 2 + 4 * lc) = make_float4(S[4], S[5], S[6], S[7]);
     }
 }
 
@@ -213,35 +244,35 @@ __global__ __launch_bounds__(256) void k_kmean_final(KmeanArgs a) {
 }
 
 // ---------------------------------------------------------------- A3: fused q/k quantization
-template <int D, int NORM, int ROPE>
+template <int D, int NORM, int ROPE, bool CONTIG>
 __global__ __launch_bounds__(256) void k_quant_qk(QuantArgs a) {
     constexpr int LPR = D / 8, RPI = kWave / LPR, IT = 32 / RPI;
-    const int64_t tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int64_t ntile = (a.r.T + 127) / 128, items = ntile * a.r.B * a.r.H;
+    const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
+    if (item >= items) return;  // uniform over the workgroup
+    const int64_t h = item % a.r.H, b = (item / a.r.H) % a.r.B, tile = item / (a.r.H * a.r.B);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lc = lane % LPR, lr = lane / LPR;
     __shared__ uint32_t amax_s[32];
     __shared__ float scale_s[32];
     if (tid < 32) amax_s[tid] = 0u;
     __syncthreads();
     const int layout = a.layout, block = a.block;
+    const bool has_mean = a.mean != nullptr, has_scale = a.sm_scale != 1.0f;
     float mu[8];
-    if (a.mean) {
-        const float4* mp = reinterpret_cast<const float4*>(a.mean + b * a.mb + h * a.mh + lc * 8);
-        float4 m0 = mp[0], m1 = mp[1];
-        mu[0] = m0.x; mu[1] = m0.y; mu[2] = m0.z; mu[3] = m0.w; mu[4] = m1.x; mu[5] = m1.y; mu[6] = m1.z; mu[7] = m1.w;
-    }
+    if (has_mean) load_row_f32<D>(a.mean + b * a.mb + h * a.mh, lc, mu);
     float v[IT][8];
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int r = 32 * w + RPI * i + lr;
         const int64_t t = tile * 128 + r;
         const bool valid = t < a.r.T;
-        row_prologue<D, NORM, ROPE>(a.r, b, t, h, lc, valid, v[i]);
+        row_prologue<D, NORM, ROPE, CONTIG>(a.r, b, t, h, lc, valid, v[i]);
         float m = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             float z = v[i][k];
-            if (a.mean) z = z - mu[k];
-            z = z * a.sm_scale;
+            if (has_mean) z = z - mu[k];
+            if (has_scale) z = z * a.sm_scale;
             v[i][k] = valid ? z : 0.0f;
             m = fmaxf(m, fabsf(v[i][k]));
         }
@@ -262,20 +293,29 @@ __global__ __launch_bounds__(256) void k_quant_qk(QuantArgs a) {
     for (int i = 0; i < IT; ++i) {
         const int r = 32 * w + RPI * i + lr;
         const int64_t t = tile * 128 + r;
-        if (t >= a.r.T) continue;
         const float s = scale_s[local_group(r, layout, block)];
         const float y = 1.0f / s;
-        const bool fast = y < __builtin_inff();
+        float q[8];
+        if (__builtin_expect(__all(s > 0.0f && y < __builtin_inff()), 1)) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) q[k] = div_rn(v[i][k], s, y);
+        } else {
+            // a zero scale (all-zero group with scale_eps = 0) gives codes 0; a reciprocal that
+            // overflows takes the plain division
+#pragma unroll
+            for (int k = 0; k < 8; ++k) q[k] = s > 0.0f ? (y < __builtin_inff() ? div_rn(v[i][k], s, y) : v[i][k] / s) : 0.0f;
+        }
         uint32_t word[2] = {0u, 0u};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            float q = 0.0f;
-            if (s > 0.0f) q = fast ? div_rn(v[i][k], s, y) : v[i][k] / s;
-            const float tq = q + copysignf(0.5f, q);
-            const int c = static_cast<int>(tq);
+            const int c = static_cast<int>(q[k] + copysignf(0.5f, q[k]));
             word[k >> 2] |= (static_cast<uint32_t>(c) & 0xffu) << (8 * (k & 3));
         }
-        *reinterpret_cast<uint2*>(a.codes + b * a.ob + t * a.ot + h * a.oh + lc * 8) = make_uint2(word[0], word[1]);
+        if (t < a.r.T) {
+            int8_t* dst = a.codes + b * a.ob + t * a.ot + h * a.oh;
+            *reinterpret_cast<uint32_t*>(dst + 4 * lc) = word[0];
+            *reinterpret_cast<uint32_t*>(dst + D / 2 + 4 * lc) = word[1];
+        }
     }
 }
 
@@ -368,12 +408,18 @@ inline int check_launch(const char* what) {
     return SQ_OK;
 }
 
+template <int D, int NORM, int ROPE>
+void launch_quant_c(const QuantArgs& a, dim3 grid, hipStream_t s) {
+    if (a.r.rope_contig) hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, false>), grid, dim3(256), 0, s, a);
+}
+
 template <int D, int NORM>
 void launch_quant_rope(const QuantArgs& a, dim3 grid, hipStream_t s) {
     switch (a.r.rope) {
-    case SQ_ROPE_NONE: hipLaunchKernelGGL((k_quant_qk<D, NORM, SQ_ROPE_NONE>), grid, dim3(256), 0, s, a); break;
-    case SQ_ROPE_SPLIT_HALF: hipLaunchKernelGGL((k_quant_qk<D, NORM, SQ_ROPE_SPLIT_HALF>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_quant_qk<D, NORM, SQ_ROPE_INTERLEAVED>), grid, dim3(256), 0, s, a); break;
+    case SQ_ROPE_NONE: launch_quant_c<D, NORM, SQ_ROPE_NONE>(a, grid, s); break;
+    case SQ_ROPE_SPLIT_HALF: launch_quant_c<D, NORM, SQ_ROPE_SPLIT_HALF>(a, grid, s); break;
+    default: launch_quant_c<D, NORM, SQ_ROPE_INTERLEAVED>(a, grid, s); break;
     }
 }
 
@@ -386,12 +432,18 @@ void launch_quant_d(const QuantArgs& a, dim3 grid, hipStream_t s) {
     }
 }
 
+template <int D, int NORM, int ROPE>
+void launch_kmean_c(const KmeanArgs& a, dim3 grid, hipStream_t s) {
+    if (a.r.rope_contig) hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, false>), grid, dim3(256), 0, s, a);
+}
+
 template <int D, int NORM>
 void launch_kmean_rope(const KmeanArgs& a, dim3 grid, hipStream_t s) {
     switch (a.r.rope) {
-    case SQ_ROPE_NONE: hipLaunchKernelGGL((k_kmean_partial<D, NORM, SQ_ROPE_NONE>), grid, dim3(256), 0, s, a); break;
-    case SQ_ROPE_SPLIT_HALF: hipLaunchKernelGGL((k_kmean_partial<D, NORM, SQ_ROPE_SPLIT_HALF>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_kmean_partial<D, NORM, SQ_ROPE_INTERLEAVED>), grid, dim3(256), 0, s, a); break;
+    case SQ_ROPE_NONE: launch_kmean_c<D, NORM, SQ_ROPE_NONE>(a, grid, s); break;
+    case SQ_ROPE_SPLIT_HALF: launch_kmean_c<D, NORM, SQ_ROPE_SPLIT_HALF>(a, grid, s); break;
+    default: launch_kmean_c<D, NORM, SQ_ROPE_INTERLEAVED>(a, grid, s); break;
     }
 }
 
@@ -417,7 +469,8 @@ int launch_norm_stats(const NormStatsArgs& a, void* stream) {
 
 int launch_kmean(const KmeanArgs& a, void* stream) {
     if (a.r.B * a.r.H * a.r.D == 0) return SQ_OK;
-    dim3 grid(static_cast<unsigned>((a.nblk + 3) / 4), static_cast<unsigned>(a.r.H), static_cast<unsigned>(a.r.B));
+    const int64_t items = (a.nblk + 3) / 4 * a.r.B * a.r.H;
+    dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
     if (a.nblk > 0) {
         if (a.r.D == 128) launch_kmean_d<128>(a, grid, S(stream));
         else launch_kmean_d<64>(a, grid, S(stream));
@@ -428,7 +481,8 @@ int launch_kmean(const KmeanArgs& a, void* stream) {
 
 int launch_quant_qk(const QuantArgs& a, void* stream) {
     if (a.r.B * a.r.T * a.r.H == 0) return SQ_OK;
-    dim3 grid(static_cast<unsigned>((a.r.T + 127) / 128), static_cast<unsigned>(a.r.H), static_cast<unsigned>(a.r.B));
+    const int64_t items = (a.r.T + 127) / 128 * a.r.B * a.r.H;
+    dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
     if (a.r.D == 128) launch_quant_d<128>(a, grid, S(stream));
     else launch_quant_d<64>(a, grid, S(stream));
     return check_launch("sq_quant_qk");

@@ -74,8 +74,9 @@ int check_rope(const sq_rope* r, const sq_rows* x, const char* what) {
     if (!r->table) return fail(SQ_ERR_NULL, "%s: rope table is NULL", what);
     if (r->pairs < 1 || r->pairs > x->D / 2)
         return fail(SQ_ERR_SHAPE, "%s: rope pairs %lld outside [1, D/2]", what, (long long)r->pairs);
-    if (r->mode == SQ_ROPE_SPLIT_HALF && r->pairs % 8)
-        return fail(SQ_ERR_UNSUPPORTED, "%s: split-half rope needs pairs %% 8 == 0", what);
+    if (r->mode == SQ_ROPE_SPLIT_HALF && r->pairs != x->D / 2)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: split-half rope rotates all D/2 pairs (pairs %lld, D %lld)", what,
+                    (long long)r->pairs, (long long)x->D);
     if (r->rb < 0 || r->rs < 0 || r->rp < 0) return fail(SQ_ERR_STRIDE, "%s: negative rope stride", what);
     if ((reinterpret_cast<uintptr_t>(r->table) & 3) != 0) return fail(SQ_ERR_ALIGN, "%s: rope table misaligned", what);
     return SQ_OK;
