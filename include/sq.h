@@ -139,7 +139,9 @@ typedef struct {
 /* A cached q8 prefix [kit] KVPrefix (q8 form), GROUP, quantize_q8: keys and values
  * int8 (Bp, P, Hk, D) with FP16 scales (Bp, P, Hk, D/32), one scale per 32 channels;
  * Bp = 1 serves every batch item. Element (b, p, h, c) of k at k[b*kb + p*kt + h*kh + c],
- * its scale at k_scale[b*ksb + p*kst + h*ksh + c/32]; likewise v. */
+ * its scale at k_scale[b*ksb + p*kst + h*ksh + c/32]; likewise v. Token rows may not
+ * overlap (kt, vt >= D; kst, vst >= D/32), and one (b, kv head) slice of each tensor,
+ * P + 128 rows long, must span < 2 GiB (SQ_ERR_STRIDE / SQ_ERR_UNSUPPORTED otherwise). */
 typedef struct {
     int64_t B, P, Hk, D;
     const int8_t* k;

@@ -294,6 +294,17 @@ int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const fl
     if (kv_tile != 64 && kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: kv_tile must be 64 or 128", what);
     if (!(score_scale > 0.0f) || !std::isfinite(score_scale))
         return fail(SQ_ERR_SHAPE, "%s: score_scale must be finite and > 0", what);
+    {
+        // rows may not overlap, and one (b, kv head) slice, read in whole tiles past P,
+        // must stay within 32-bit byte offsets
+        const int64_t groups = p.D / 32;
+        if (p.P > 1 && (p.kt < p.D || p.vt < p.D || p.kst < groups || p.vst < groups))
+            return fail(SQ_ERR_STRIDE, "%s: prefix token strides must cover a whole row", what);
+        const int64_t rows = p.P + 128, lim = int64_t(1) << 31;
+        if (rows * p.kt + p.D >= lim || rows * p.vt + p.D >= lim || 2 * (rows * p.kst + groups) >= lim ||
+            2 * (rows * p.vst + groups) >= lim)
+            return fail(SQ_ERR_UNSUPPORTED, "%s: one prefix slice spans 2 GiB or more", what);
+    }
     PrefixArgs a{};
     a.q = q->codes; a.B = q->B; a.Sq = q->S; a.H = q->H; a.D = q->D;
     a.qsb = q->sb; a.qst = q->st; a.qsh = q->sh;

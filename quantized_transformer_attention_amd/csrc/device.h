@@ -56,4 +56,28 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
     return __shfl_xor(v, mask, kWave);
 }
 
+// LDS tiles are rows of 16-byte slots; slot s of row r is stored at slot s ^ f(r) so that
+// the rows one MFMA operand read touches (consecutive rows, one slot each) land in
+// distinct bank groups, whether the LDS serves 8 or 16 such lanes per cycle:
+//   8 slots per row (128 B):  f(r) = (r & 7) ^ ((r >> 3) & 1)
+//   4 slots per row (64 B):   f(r) = (r >> 1) & 3
+//   16 slots per row (256 B): f(r) = r & 15
+template <int NS>
+__device__ __forceinline__ int swz(int row, int slot) {
+    if constexpr (NS == 8) return slot ^ ((row & 7) ^ ((row >> 3) & 1));
+    else if constexpr (NS == 4) return slot ^ ((row >> 1) & 3);
+    else return slot ^ (row & 15);
+}
+
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+// s_waitcnt vmcnt(0): every global load of this wave (the tile copies included) has landed.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Work items (b, h, query block) are handed out so that the workgroups that run on
+// one XCD at the same time (dispatch sends workgroup i to XCD i mod 8) share a head:
+// XCD x takes the contiguous item range [x per, (x + 1) per), in order.
+__device__ __forceinline__ int64_t xcd_item(int64_t L, int64_t per) { return (L & 7) * per + (L >> 3); }
+
 }  // namespace sq

@@ -153,9 +153,6 @@ __host__ __device__ __forceinline__ int groups_per_tile(int layout, int block) {
     }
 }
 
-// Work item of workgroup L when XCD x = L mod 8 takes the contiguous range [x per, (x + 1) per).
-__device__ __forceinline__ int64_t xcd_item(int64_t L, int64_t per) { return (L & 7) * per + (L >> 3); }
-
 // ---------------------------------------------------------------- A1: mean squares over all heads
 template <int D>
 __global__ __launch_bounds__(256) void k_norm_stats(NormStatsArgs a) {

@@ -35,6 +35,9 @@ PREFIX_CASES = [
     (128, 2, 2, 3, 1, 70, 257, (3, 128), 64, False),
     (64, 1, 1, 4, 4, 130, 100, (0, 32), 128, True),
     (64, 1, 1, 2, 2, 1, 1, (0, 64), 64, True),
+    (128, 1, 1, 2, 2, 300, 128, (0, 64), 64, True),     # whole tiles only: no masked key
+    (64, 2, 1, 2, 1, 97, 192, (3, 128), 64, False),
+    (128, 1, 1, 2, 1, 140, 640, (1, 32), 128, True),
 ]
 
 
