@@ -207,6 +207,9 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
     a.qs = q->scales; a.qssb = q->ssb; a.qssh = q->ssh; a.q_layout = q->layout; a.q_block = q->block;
     a.k = k->codes; a.Sk = k->S; a.Hk = k->H; a.ksb = k->sb; a.kst = k->st; a.ksh = k->sh;
     a.ks = k->scales; a.kssb = k->ssb; a.kssh = k->ssh; a.k_layout = k->layout; a.k_block = k->block;
+    a.k_shift = 0;
+    while ((1 << a.k_shift) < k->block) ++a.k_shift;
+    a.k_nscale = static_cast<int>(sq_scale_count(k->S, k->layout, k->block));
     a.score_scale = score_scale;
     a.kv_tile = kv_tile;
     a.out = out; a.ob = ob; a.ot = ot; a.oh = oh;

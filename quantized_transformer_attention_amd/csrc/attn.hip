@@ -35,7 +35,7 @@ typedef short v2s __attribute__((ext_vector_type(2)));
 
 // 4 floats -> 4 e4m3 bytes of 256 x (the scaled convert divides by its scale, 2^-8).
 __device__ __forceinline__ int pack_fp8x4_256(float a, float b, float c, float d) {
-    v2s r = {0, 0};
+    v2s r;   // both halves are written below: no initial value is needed
     r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, 0.00390625f, false);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, 0.00390625f, true);
     return __builtin_bit_cast(int, r);
@@ -60,34 +60,56 @@ struct Cfg {
 // buffer_load_dwordx4 ... lds: lane i of a wave fills bytes [16 i, 16 i + 16) of a 1 KB
 // piece. The buffer resources end at the last valid byte of the (b, kv head) slices, so
 // rows past the end read as zeros (their scores are masked) and can never fault.
+//
+// Wave w fills pieces 4 u + w. Piece 4 u + w starts 4096 u / D rows (K) and 4096 u / RBV
+// rows (V^T) after piece w, a whole number of swizzle periods, so a lane's slot is the same
+// in every piece and its source offset moves by a wave-uniform amount: the per-lane part
+// is computed once (dma_lane_offsets) and a tile costs one add per piece.
+template <int D, int KT, bool FP8>
+struct DmaOffsets {
+    int k, v;   // byte offsets of this lane's 16 bytes of piece w, relative to tile 0
+};
+
+template <int D, int KT, bool FP8>
+__device__ __forceinline__ DmaOffsets<D, KT, FP8> dma_lane_offsets(int kst, int vrow, int w, int lane) {
+    using C = Cfg<D, KT, FP8>;
+    static_assert((4096 / D) % 16 == 0, "K pieces must advance by whole swizzle periods");
+    static_assert((4096 / C::RBV) % 16 == 0, "V pieces must advance by whole swizzle periods");
+    DmaOffsets<D, KT, FP8> r;
+    {
+        const int o = 1024 * w + 16 * lane;
+        const int row = o / D, ls = swz<C::KNS>(row, (o % D) / 16);
+        const int key = ((row & 15) >> 2) * C::KQ + 4 * (row >> 4) + (row & 3);
+        r.k = key * kst + ls * 16;
+    }
+    {
+        const int o = 1024 * w + 16 * lane;
+        const int row = o / C::RBV, ls = swz<C::VNS>(row, (o % C::RBV) / 16);
+        r.v = row * vrow + ls * 16;
+    }
+    return r;
+}
+
 template <int D, int KT, bool FP8>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int kst, int vrow,
-                                         int kbase, uint8_t* kl, uint8_t* vl, int w, int lane) {
+                                         int kbase, uint8_t* kl, uint8_t* vl, int w, DmaOffsets<D, KT, FP8> off) {
     using C = Cfg<D, KT, FP8>;
     constexpr int KCH = C::KBYTES / 1024, VCH = C::VBYTES / 1024;
-    // the per-lane offsets are a few integer ops: recompute them here rather than keep
-    // them live (in registers the whole key loop) across the tile's math
-    asm volatile("" : "+v"(lane));
+    static_assert(KCH % 4 == 0 && VCH % 4 == 0, "every wave fills the same number of pieces");
+    // wave-uniform offsets recomputed per tile (scalar adds) rather than hoisted out of the
+    // key loop, where they would crowd the scalar registers into spilling
+    asm volatile("" : "+s"(w), "+s"(kst), "+s"(vrow));
+    // piece 4 u + w of K: keys advance by (4096 u / D rows) / 16 rows per 4 keys
+    const int kb = kbase * kst;
 #pragma unroll
-    for (int u = 0; u < (KCH + 3) / 4; ++u) {
-        const int piece = 4 * u + w;
-        if (KCH % 4 == 0 || piece < KCH) {
-            const int o = 1024 * piece + 16 * lane;
-            const int row = o / D, ls = swz<C::KNS>(row, (o % D) / 16);
-            const int key = kbase + ((row & 15) >> 2) * C::KQ + 4 * (row >> 4) + (row & 3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lvoid_t*)(kl + 1024 * piece), 16, key * kst + ls * 16, 0, 0, 0);
-        }
-    }
+    for (int u = 0; u < KCH / 4; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lvoid_t*)(kl + 1024 * (4 * u + w)), 16,
+                                                 off.k + kb + (u * (4096 / D) / 4) * kst, 0, 0, 0);
+    const int vb = kbase * C::VB;
 #pragma unroll
-    for (int u = 0; u < (VCH + 3) / 4; ++u) {
-        const int piece = 4 * u + w;
-        if (VCH % 4 == 0 || piece < VCH) {
-            const int o = 1024 * piece + 16 * lane;
-            const int row = o / C::RBV, ls = swz<C::VNS>(row, (o % C::RBV) / 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lvoid_t*)(vl + 1024 * piece), 16,
-                                                     row * vrow + kbase * C::VB + ls * 16, 0, 0, 0);
-        }
-    }
+    for (int u = 0; u < VCH / 4; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lvoid_t*)(vl + 1024 * (4 * u + w)), 16,
+                                                 off.v + vb + (u * (4096 / C::RBV)) * vrow, 0, 0, 0);
 }
 
 
@@ -100,64 +122,69 @@ struct WaveState {
     v4f o[C::NQ][C::NCT];
 };
 
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+// Key scales of the KQ keys [kg0, kg0 + KQ) of one lane group, by k-scale group q: THREAD_K
+// keeps 4 scales per 64 keys, key t in group (t >> 1) & 3; PER_BLOCK one per 32, 64 or 128
+// keys (KQ <= 32 keys never straddle a block). Past the last scale the buffer load gives 0.
+__device__ __forceinline__ v4f_t load_kscales(__amdgpu_buffer_rsrc_t r, int kg0, int layout, int shift) {
+    if (layout == SQ_LAYOUT_THREAD_K) {
+        return __builtin_bit_cast(v4f_t, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (kg0 >> 6), 0, 0));
+    } else {
+        const float s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (kg0 >> shift), 0, 0));
+        return v4f_t{s, s, s, s};
+    }
+}
+
 // One key tile: S^T = K Q^T on INT8 MFMA, online softmax in base 2, acc += P V.
+// ks: this lane group's key scales for the tile (load_kscales).
 template <int D, int KT, bool FP8, bool TAIL>
 __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
-                                          const uint8_t* v_lds, int64_t kbase, const float* ksp, int lq, int g) {
+                                          const uint8_t* v_lds, int kbase, v4f_t ks, int lq, int g) {
     using C = Cfg<D, KT, FP8>;
-    // c = RN(qs ks) per k-scale group of this lane group's keys
-    const int64_t kg0 = kbase + C::KQ * g;
+    // c = RN(qs ks) per k-scale group of this lane group's keys (times score_scale: exact for 1)
+    const int kg0 = kbase + C::KQ * g;
     float cg[C::NQ][4];
-    {
-        float ks[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (!TAIL || kg0 < a.Sk) {
-            if (a.k_layout == SQ_LAYOUT_THREAD_K) {
-                const int64_t base = 4 * (kg0 >> 6);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) ks[q] = ksp[base + q];
-            } else {
-                const float sv = ksp[kg0 / a.k_block];
+    for (int n = 0; n < C::NQ; ++n)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) ks[q] = sv;
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < C::NQ; ++n)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float c = st.qsc[n] * ks[q];
-                if (a.score_scale != 1.0f) c = c * a.score_scale;
-                cg[n][q] = c;
-            }
-    }
+        for (int q = 0; q < 4; ++q) cg[n][q] = (st.qsc[n] * ks[q]) * a.score_scale;
 
-    // S^T = K Q^T (int32)
-    v4i s[C::NT][C::NQ];
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-#pragma unroll
-        for (int ch = 0; ch < C::NC; ++ch) {
-            const int row = 16 * t + lq;
-            const v4i kop = *reinterpret_cast<const v4i*>(k_lds + row * D + swz<C::KNS>(row, 4 * ch + g) * 16);
-#pragma unroll
-            for (int n = 0; n < C::NQ; ++n)
-                s[t][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, st.qop[n][ch], ch == 0 ? v4i{0, 0, 0, 0} : s[t][n], 0, 0, 0);
-        }
-    }
-
-    // online softmax, P operands
+    // per 16-query tile n: S^T = K Q^T (int32), then the online softmax and its P operand.
+    // Only one tile's scores are live; K is read from LDS again for the second tile.
     v8i pf8[C::NQ];
     v8bf pbf[C::NQ][KT / 32];
+    float alpha[C::NQ];
+    int lane = 16 * g + lq;
 #pragma unroll
     for (int n = 0; n < C::NQ; ++n) {
+        // fresh lane offsets per tile n: without them the first tile's K operand reads would
+        // be kept in registers for the second
+        asm volatile("" : "+v"(lane));
+        const int klq = lane & 15, kg = lane >> 4;
+        v4i s[C::NT];
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t) {
+#pragma unroll
+            for (int ch = 0; ch < C::NC; ++ch) {
+                const int row = 16 * t + klq;
+                const v4i kop = *reinterpret_cast<const v4i*>(k_lds + row * D + swz<C::KNS>(row, 4 * ch + kg) * 16);
+                s[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, st.qop[n][ch], ch == 0 ? v4i{0, 0, 0, 0} : s[t], 0, 0, 0);
+            }
+        }
+        // keys of this lane group in the tile (all KQ but in the last one); opaque so that the
+        // masks of the last tile are not computed once before the key loop and kept (64
+        // scalar registers of lane masks)
+        int nval = static_cast<int>(a.Sk) - kg0;
+        if (TAIL) asm volatile("" : "+v"(nval));
         int amx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
 #pragma unroll
         for (int t = 0; t < C::NT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (TAIL && kg0 + 4 * t + i >= a.Sk) s[t][n][i] = INT32_MIN;
+                if (TAIL && 4 * t + i >= nval) s[t][i] = INT32_MIN;
                 const int q = 2 * (t & 1) + (i >> 1);
-                amx[q] = max(amx[q], s[t][n][i]);
+                amx[q] = max(amx[q], s[t][i]);
             }
         float mt = -__builtin_inff();
 #pragma unroll
@@ -169,7 +196,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
         mt = fmaxf(mt, shfl_xor(mt, 32));
         const float mo = st.m_run[n];
         const float mn = fmaxf(mo, mt);
-        const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+        alpha[n] = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
         st.m_run[n] = mn;
         float lsum = 0.0f;
 #pragma unroll
@@ -178,7 +205,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int q = 2 * (t & 1) + (i >> 1);
-                const int av = s[t][n][i];
+                const int av = s[t][i];
                 float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(av), cg[n][q], -mn));
                 if (TAIL && av == INT32_MIN) pv = 0.0f;
                 p[i] = pv;
@@ -191,17 +218,20 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
                 for (int i = 0; i < 4; ++i) pbf[n][t >> 1][4 * (t & 1) + i] = static_cast<__bf16>(p[i]);
             }
         }
-        st.l_run[n] = st.l_run[n] * alpha + lsum;
-        // rescale the accumulator rows (query 4 g + i of this n-tile) when a max moved
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * g + i, kWave);
-#pragma unroll
-                for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct][i] *= ai;
-            }
-        }
+        st.l_run[n] = st.l_run[n] * alpha[n] + lsum;
     }
+
+    // Rescale the accumulator rows (query 4 g + i of tile n) by alpha. Unconditional: alpha is
+    // exactly 1 where no max moved, and a branch around the product makes the compiler keep a
+    // second copy of the accumulator (register moves every tile, spills).
+#pragma unroll
+    for (int n = 0; n < C::NQ; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha[n], 4 * g + i, kWave);
+#pragma unroll
+            for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct][i] *= ai;
+        }
 
     // acc += Pt Vt
 #pragma unroll
@@ -233,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     using C = Cfg<D, KT, FP8>;
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::KBYTES + C::VBYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::KBYTES + C::VBYTES];
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lq = l & 15, g = l >> 4;
     const int64_t nqb = (a.Sq + C::QPB - 1) / C::QPB;
     const int64_t items = nqb * a.H * a.B;
     const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
@@ -259,9 +289,18 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
+    // what the epilogue needs, folded to a few values before the key loop (fewer live scalars)
+    float* const obase = a.out + b * a.ob + h * a.oh;
+    const int64_t ot = a.ot;
+    float* const lbase = a.lse ? a.lse + b * a.lb + h * a.lh : nullptr;
+    const float* const vsbase = FP8 ? a.vscale + b * a.vssb + hk * a.vssh : nullptr;
+    const int q0i = static_cast<int>(q0), Sq = static_cast<int>(a.Sq);
+
     const int8_t* kb = a.k + b * a.ksb + hk * a.ksh;
     const uint8_t* vb = static_cast<const uint8_t*>(a.v) + (b * a.vsb + hk * a.vsh) * C::VB;
     const float* ksp = a.ks + b * a.kssb + hk * a.kssh;
+    const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ksp), 0, 4 * a.k_nscale, 0x00020000);
+    const int kl_layout = a.k_layout, kl_shift = a.k_shift;
     const bool tail = a.Sk % KT != 0;
     const int ntiles = static_cast<int>((a.Sk + KT - 1) / KT);
     const int last = ntiles - 1;
@@ -270,23 +309,36 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kb), 0, static_cast<int>((a.Sk - 1) * a.kst + D), 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), 0, D * vrow, 0x00020000);
+    const DmaOffsets<D, KT, FP8> doff = dma_lane_offsets<D, KT, FP8>(kst, vrow, w, l);
     // tile j streams into buffer j % 2 while tile j - 1 is processed from the other one
-    auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, l); };
-    auto step = [&](int j, const uint8_t* buf) {
-        if (tail && j == last) tile_step<D, KT, FP8, true>(a, st, buf, buf + C::KBYTES, static_cast<int64_t>(j) * KT, ksp, lq, g);
-        else tile_step<D, KT, FP8, false>(a, st, buf, buf + C::KBYTES, static_cast<int64_t>(j) * KT, ksp, lq, g);
+    auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, doff); };
+    // the key scales of tile j + 1 are fetched (before its K/V copy) while tile j is
+    // processed, so no wait on them ever waits for a copy in flight
+    auto kscales = [&](int j) { return load_kscales(ksr, j * KT + C::KQ * g, kl_layout, kl_shift); };
+    auto step = [&](int j, const uint8_t* buf, v4f_t ks) {
+        if (tail && j == last) tile_step<D, KT, FP8, true>(a, st, buf, buf + C::KBYTES, j * KT, ks, lq, g);
+        else tile_step<D, KT, FP8, false>(a, st, buf, buf + C::KBYTES, j * KT, ks, lq, g);
     };
+    v4f_t ks_next = kscales(0);
     copy(0, buf0);
     wait_vm();
     __syncthreads();
     for (int j = 0; j < ntiles; j += 2) {
-        if (j + 1 < ntiles) copy(j + 1, buf1);
-        step(j, buf0);
+        v4f_t ks_cur = ks_next;
+        if (j + 1 < ntiles) {
+            ks_next = kscales(j + 1);
+            copy(j + 1, buf1);
+        }
+        step(j, buf0, ks_cur);
         wait_vm();
         __syncthreads();
         if (j + 1 >= ntiles) break;
-        if (j + 2 < ntiles) copy(j + 2, buf0);
-        step(j + 1, buf1);
+        ks_cur = ks_next;
+        if (j + 2 < ntiles) {
+            ks_next = kscales(j + 2);
+            copy(j + 2, buf0);
+        }
+        step(j + 1, buf1, ks_cur);
         wait_vm();
         __syncthreads();
     }
@@ -297,20 +349,20 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         float lt = st.l_run[n];
         lt = lt + shfl_xor(lt, 16);
         lt = lt + shfl_xor(lt, 32);
-        const int64_t qi = q0 + n * 16 + lq;
-        if (a.lse && g == 0 && qi < a.Sq) a.lse[b * a.lb + h * a.lh + qi] = st.m_run[n] + log2f(lt);
+        const int qi = q0i + n * 16 + lq;
+        if (lbase && g == 0 && qi < Sq) lbase[qi] = st.m_run[n] + log2f(lt);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float li = __shfl(lt, 4 * g + i, kWave);
             const float inv = 1.0f / li;
-            const int64_t qr = q0 + n * 16 + 4 * g + i;
-            if (qr >= a.Sq) continue;
-            float* op = a.out + b * a.ob + qr * a.ot + h * a.oh;
+            const int qr = q0i + n * 16 + 4 * g + i;
+            if (qr >= Sq) continue;
+            float* op = obase + qr * ot;
 #pragma unroll
             for (int ct = 0; ct < C::NCT; ++ct) {
                 const int c = ct * 16 + lq;
                 float val = st.o[n][ct][i] * inv;
-                if constexpr (FP8) val = val * (a.vscale[b * a.vssb + hk * a.vssh + c] * 0.00390625f);
+                if constexpr (FP8) val = val * (vsbase[c] * 0.00390625f);
                 op[c] = val;
             }
         }

@@ -80,6 +80,7 @@ struct AttnArgs {
     const float* ks;
     int64_t kssb, kssh;
     int k_layout, k_block;
+    int k_shift, k_nscale;      // PER_BLOCK: log2(k_block); scales per (b, kv head)
     const void* v;              // channel-major bf16 or fp8 (sb, sh, sd; tokens contiguous)
     int v_fp8;
     int64_t vsb, vsh, vsd;
