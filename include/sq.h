@@ -241,7 +241,11 @@ int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const fl
  * scales [num_blocks, block_size, Hk, D/32]; keys and values are code * scale.
  * Softmax of (q . k) * softmax_scale; out FP32 (N, Hq, D) at out[n*on + h*oh + c].
  * max_seq_len is a host bound for the workspace and the grid (no device read).
- * block_size 16; D 128; Hq % Hk == 0 with Hq / Hk <= 16. */
+ * block_size 16; D 128; Hq / Hk in {1, 2, 4, 8}. q 16-byte aligned rows, caches
+ * 16-byte aligned, scale tensors 8-byte aligned (one row of 4 FP16 per slot and head).
+ * Both products run on f16 matrix units with FP32 accumulation: q is carried as f16
+ * after an exact power-of-two rescale per head, and the weight of a value row is
+ * f16(p * value scale) (relative rounding <= 2^-11 per weight). */
 size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_len);
 int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
                     const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,

@@ -358,8 +358,8 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
         return fail(SQ_ERR_ALIGN, "%s: q rows must start on 16-byte boundaries", what);
     if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15))
         return fail(SQ_ERR_ALIGN, "%s: caches must be 16-byte aligned", what);
-    if ((reinterpret_cast<uintptr_t>(k_scale) & 1) || (reinterpret_cast<uintptr_t>(v_scale) & 1))
-        return fail(SQ_ERR_ALIGN, "%s: FP16 scales must be 2-byte aligned", what);
+    if ((reinterpret_cast<uintptr_t>(k_scale) & 7) || (reinterpret_cast<uintptr_t>(v_scale) & 7))
+        return fail(SQ_ERR_ALIGN, "%s: FP16 scale rows must be 8-byte aligned", what);
     if (on < 0 || oh < 0) return fail(SQ_ERR_STRIDE, "%s: negative output stride", what);
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
         return fail(SQ_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", what);

@@ -11,18 +11,26 @@
 // The path is bound by HBM: per cached token and kv head 2 x 128 code bytes + 2 x 8
 // scale bytes. One workgroup (4 waves) owns one segment of kDecodeSeg positions of
 // one (sequence, kv head) and serves all Hq / Hk query heads from a single read of
-// the segment's K and V:
-//  * lane l holds channels 16 (l % 8) .. +15 of token l / 8 of an 8-token step, so a
-//    128-byte cache row is one 16-byte load per lane, 8 lanes per row;
-//  * pass 1 writes the segment's scores (log2 units: q carries softmax_scale *
-//    log2 e) to LDS; per-group dots are scaled by their FP16 key scale before the
-//    8-lane butterfly;
-//  * pass 2 reads V once, p = 2^(s - M) against the segment max M (no rescaling in
-//    the loop), and accumulates p * code * scale in FP32;
+// the segment's K and V; each wave takes 64 positions (4 pages). Both contractions run
+// on the f16 matrix cores (f32 accumulation), the query heads padded to 16 rows:
+//  * Q.K: K codes are loaded straight into the B operand layout (8 channels of one
+//    position per lane) and widened exactly to f16 (byte permute + packed f16 subtract);
+//    q is f16 after an exact power-of-two
+//    rescale per head (the head's largest |q| lands in [2^14, 2^15), so no bf16 value
+//    overflows); one MFMA per 32-channel q8 group, whose dot then meets its FP16 key scale
+//    in FP32. Scores (log2 units) go to LDS.
+//  * P.V: p = 2^(s - M) against the segment max M (no rescaling in the loop); the value
+//    scale is folded into the weight, P' = f16(p * vs) per 32-channel group, and V codes
+//    are staged in LDS and read back transposed (ds_read_b64_tr_b8:
+//    8 positions of one channel per lane), widened exactly to f16.
+//  * every load of a wave is issued up front and unconditionally (no per-lane guard, which
+//    would make each load wait for the one before).
 //  * the partial (acc, M, l) of each (query head, segment) goes to the workspace;
 //    k_decode_reduce merges the segments of a query by their maxima.
-// Positions whose block-table entry is outside [0, num_blocks) are skipped (never
-// read), so a bad table cannot fault the device.
+// Positions whose block-table entry is outside [0, num_blocks) are skipped: their rows are
+// read from block 0 instead (never from the bad entry), their scores are -inf and their
+// value scales zero, so a bad table cannot fault the device; with no blocks at all nothing
+// is read and the output is 0.
 #include "device.h"
 #include "sq_internal.h"
 
@@ -32,181 +40,252 @@ namespace {
 constexpr int kD = 128;
 constexpr int kSeg = kDecodeSeg;
 constexpr int kTpw = kSeg / 4;  // positions per wave
+static_assert(kTpw == 64, "a wave takes 4 pages");
 
-__device__ __forceinline__ void unpack_i8x16(const uint4& u, float* f) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f[4 * k + j] = static_cast<float>(static_cast<int8_t>((w[k] >> (8 * j)) & 0xff));
-    }
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// 8 int8 (byte k = element k) -> 8 f16, exact: byte b ^ 0x80 = b + 128 goes under the f16
+// exponent byte 0x64 (f16 0x64uu = 1024 + uu), then 1152 comes off in packed f16
+__device__ __forceinline__ v8h i8x8_to_f16(uint32_t w0, uint32_t w1) {
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+    const h2 bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    h2 r[4];
+    r[0] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) - bias;
+    r[1] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) - bias;
+    r[2] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) - bias;
+    r[3] = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) - bias;
+    return __builtin_bit_cast(v8h, r);
 }
 
 template <int G>
-__global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
-    constexpr int ST = kTpw / 8;          // 8-position steps per wave
-    constexpr int PG = kTpw / 16;         // pages per wave
-    __shared__ float sc[kSeg * G];
-    __shared__ float red[4 * G * kD];
-    __shared__ float wred[4 * G];
-    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lc = l & 7, tr = l >> 3;
-    // kv head fastest in the grid: the workgroups of one segment's 8 heads run together, so
-    // the rows of every cache slot (all heads side by side in NHD) are read in one window
-    const int hk = blockIdx.x, seg = blockIdx.y, n = blockIdx.z;
-    const int L = min(a.lens[n], a.max_len);
+__global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) float sc[G][kSeg];             // scores [head][position]
+    __shared__ __attribute__((aligned(1024))) uint8_t vst[4][kTpw * kD];   // each wave's V rows; then its partial acc
+    __shared__ __attribute__((aligned(16))) uint32_t vss[4][kTpw * 2];     // their scales (4 FP16 per row)
+    __shared__ float wred[4][G];
+    __shared__ float lred[4][G];
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, j = l >> 4, lc = l & 15;
+    // The Hk workgroups of one (sequence, segment) run back to back on one XCD (workgroup i
+    // goes to XCD i % 8), so each cache slot's rows and scale rows (all heads side by side in
+    // NHD) are fetched from HBM once into that XCD's L2; the (sequence, segment) pairs are
+    // dealt round-robin over the XCDs, which keeps their loads even.
+    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const int64_t chunk = 8 * static_cast<int64_t>(k / a.Hk) + xcd;
+    if (chunk >= static_cast<int64_t>(a.segs) * a.N) return;  // uniform over the workgroup
+    const int hk = k % a.Hk;
+    const int seg = static_cast<int>(chunk % a.segs);
+    const int n = static_cast<int>(chunk / a.segs);
+    const int L = a.num_blocks > 0 ? min(a.lens[n], a.max_len) : 0;   // empty cache: no position is readable
     const int s0 = seg * kSeg;
     if (s0 >= L) return;  // uniform over the workgroup
     const int s1 = min(L, s0 + kSeg);
     const int wp0 = s0 + w * kTpw;        // first position of this wave (a multiple of 16)
     const int32_t* bt = a.bt + static_cast<int64_t>(n) * a.bt_stride;
 
-    // the physical block of each of the wave's pages (one table read per page; -1 if unused or invalid)
+    // the physical block of each of the wave's 4 pages (one table read per page; -1 if unused or invalid)
     int myblk = -1;
-    if (l < PG && wp0 + 16 * l < s1) {
+    if (l < 4 && wp0 + 16 * l < s1) {
         const int b = bt[(wp0 >> 4) + l];
         myblk = (b >= 0 && b < a.num_blocks) ? b : -1;
     }
-    int64_t rowbase[PG];
+    int64_t rowbase[4];
 #pragma unroll
-    for (int pg = 0; pg < PG; ++pg) {
+    for (int pg = 0; pg < 4; ++pg) {
         const int b = __builtin_amdgcn_readlane(myblk, pg);
         rowbase[pg] = b < 0 ? -1 : static_cast<int64_t>(b) * 16 * a.Hk + hk;   // row of slot 0, this kv head
     }
 
-    // the G query heads of this kv head, channels 16 lc .. 16 lc + 15, in log2 units
-    float q[G][16];
+    // ---- all loads of the wave go out first, q and K (needed first) before V, so the scores
+    // can start while the values are still in flight. Register loads only: a use of a register
+    // load while an LDS copy (global_load_lds) is in flight waits for everything outstanding.
+    // Like every load here they are unconditional (a lane-dependent guard around each load
+    // makes it wait for the one before): a page outside the table reads block 0's rows instead,
+    // positions past the end read their page's unused slots; all of them get score -inf and
+    // value scale 0.
+    uint4 qraw[4];
+    {
+        const uint16_t* qp = a.q + static_cast<int64_t>(n) * a.qn + static_cast<int64_t>(hk * G + min(lc, G - 1)) * a.qh;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const uint16_t* qp = a.q + static_cast<int64_t>(n) * a.qn + static_cast<int64_t>(hk * G + h) * a.qh + 16 * lc;
-        float f[16];
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(qp), f);
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(qp + 8), f + 8);
+        for (int g = 0; g < 4; ++g) qraw[g] = *reinterpret_cast<const uint4*>(qp + 32 * g + 8 * j);
+    }
+    // K of page t: lane (j, lc) takes position 16 t + lc, channels 32 g + 8 j .. + 7 of each group g
+    uint2 kr[4][4];
+    uint2 ksr[4];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) q[h][c] = f[c] * a.scale;
+    for (int t = 0; t < 4; ++t) {
+        const int64_t row = (rowbase[t] >= 0 ? rowbase[t] : hk) + static_cast<int64_t>(lc) * a.Hk;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) kr[t][g] = *reinterpret_cast<const uint2*>(a.kc + row * kD + 32 * g + 8 * j);
+        ksr[t] = *reinterpret_cast<const uint2*>(a.ks + row * (kD / 32));
     }
 
-    // ---- pass 1: every key load of the wave in flight at once, then the scores
-    uint4 kraw[ST];
-    float ksc[ST];
+    // V rows: load r holds rows 8 r .. 8 r + 7 (lane l: row 8 r + l / 8, bytes 16 (l % 8)); V scales:
+    // lane l takes row l's 4 FP16. Both go to LDS once the scores are done.
+    uint4 vraw[8];
 #pragma unroll
-    for (int st = 0; st < ST; ++st) {
-        const int pos = wp0 + 8 * st + tr;
-        const int64_t rb = rowbase[st >> 1];
-        const bool ok = rb >= 0 && pos < s1;
-        const int64_t row = rb + static_cast<int64_t>(8 * (st & 1) + tr) * a.Hk;
-        kraw[st] = ok ? *reinterpret_cast<const uint4*>(a.kc + row * kD + 16 * lc) : make_uint4(0, 0, 0, 0);
-        ksc[st] = ok ? f16_to_f32(a.ks[row * (kD / 32) + (lc >> 1)]) : 0.0f;
+    for (int r = 0; r < 8; ++r) {
+        const int64_t rb = rowbase[r >> 1] >= 0 ? rowbase[r >> 1] : hk;
+        const int slot = 8 * (r & 1) + (l >> 3);
+        vraw[r] = *reinterpret_cast<const uint4*>(a.vc + (rb + static_cast<int64_t>(slot) * a.Hk) * kD + 16 * (l & 7));
     }
-    // the value loads go out with the key loads: both streams in flight before any math
-    uint4 vraw[ST];
-    float vsc[ST];
-#pragma unroll
-    for (int st = 0; st < ST; ++st) {
-        const int pos = wp0 + 8 * st + tr;
-        const int64_t rb = rowbase[st >> 1];
-        const bool ok = rb >= 0 && pos < s1;
-        const int64_t row = rb + static_cast<int64_t>(8 * (st & 1) + tr) * a.Hk;
-        vraw[st] = ok ? *reinterpret_cast<const uint4*>(a.vc + row * kD + 16 * lc) : make_uint4(0, 0, 0, 0);
-        vsc[st] = ok ? f16_to_f32(a.vs[row * (kD / 32) + (lc >> 1)]) : 0.0f;
+    uint2 vsr;
+    {
+        const int64_t rb0 = rowbase[l >> 4];
+        const int64_t rb = rb0 >= 0 ? rb0 : hk;
+        vsr = *reinterpret_cast<const uint2*>(a.vs + (rb + static_cast<int64_t>(l & 15) * a.Hk) * (kD / 32));
     }
+    // ---- q of head m = lc (zero rows for m >= G): channels 32 g + 8 j .. + 7 as f16, times
+    // 2^sh with sh per head putting its largest |q| in [2^14, 2^15)
+    v8h qa[4];
+    int sh = 0;
+    {
+        float f[4][8];
+        float mx = 0.0f;
 #pragma unroll
-    for (int st = 0; st < ST; ++st) {
-        const int pos = wp0 + 8 * st + tr;
-        const bool ok = rowbase[st >> 1] >= 0 && pos < s1;
-        float kf[16];
-        unpack_i8x16(kraw[st], kf);
-        float part[G];
+        for (int g = 0; g < 4; ++g) {
+            unpack_bf16x8(qraw[g], f[g]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float d = q[h][0] * kf[0];
-#pragma unroll
-            for (int c = 1; c < 16; ++c) d = __builtin_fmaf(q[h][c], kf[c], d);
-            part[h] = d * ksc[st];
+            for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(f[g][k]));
         }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        sh = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) + 1 : 0;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            part[h] += shfl_xor(part[h], 1);
-            part[h] += shfl_xor(part[h], 2);
-            part[h] += shfl_xor(part[h], 4);
-        }
-        if (lc == 0) {
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int h = 0; h < G; ++h) sc[(w * kTpw + 8 * st + tr) * G + h] = ok ? part[h] : -__builtin_inff();
+            for (int k = 0; k < 8; ++k)
+                qa[g][k] = lc < G ? static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[g][k], sh)) : static_cast<_Float16>(0.0f);
+    }
+
+    // ---- pass 1: scores of the wave's 64 positions
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        v4f dg[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            dg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[g], i8x8_to_f16(kr[t][g].x, kr[t][g].y),
+                                                          v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        // lane (j, lc) now holds heads 4 j + i of position 16 t + lc
+        const int pos = wp0 + 16 * t + lc;
+        const bool ok = rowbase[t] >= 0 && pos < s1;
+        const float k0 = f16_to_f32(ksr[t].x & 0xffff), k1 = f16_to_f32(ksr[t].x >> 16);
+        const float k2 = f16_to_f32(ksr[t].y & 0xffff), k3 = f16_to_f32(ksr[t].y >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * j + i;
+            float sv = dg[0][i] * k0;
+            sv = __builtin_fmaf(dg[1][i], k1, sv);
+            sv = __builtin_fmaf(dg[2][i], k2, sv);
+            sv = __builtin_fmaf(dg[3][i], k3, sv);
+            const int shh = __shfl(sh, min(h, 15), kWave);
+            sv = __builtin_amdgcn_ldexpf(sv, -shh) * a.scale;
+            if (h < G) sc[h][w * kTpw + 16 * t + lc] = ok ? sv : -__builtin_inff();
         }
+    }
+    // this wave's V rows and value scales to LDS (scales zero on rows past the end of the
+    // sequence or on an unread page)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(vst[w] + 1024 * r + 16 * l) = vraw[r];
+    {
+        const bool okv = rowbase[l >> 4] >= 0 && wp0 + l < s1;
+        *reinterpret_cast<uint2*>(&vss[w][2 * l]) = okv ? vsr : make_uint2(0u, 0u);
     }
     __syncthreads();
 
-    // ---- segment max per query head
+    // ---- segment max per query head (thread tid: position tid)
     float M[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float m = -__builtin_inff();
-        for (int t = tid; t < kSeg; t += 256) m = fmaxf(m, sc[t * G + h]);
+        float m = sc[h][tid];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
-        if (l == 0) wred[w * G + h] = m;
+        if (l == 0) wred[w][h] = m;
     }
     __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) M[h] = fmaxf(fmaxf(wred[0][h], wred[1][h]), fmaxf(wred[2][h], wred[3][h]));
+
+    // ---- pass 2: p = 2^(s - M), acc += f16(p vs) . v
+    float Mm = -__builtin_inff();
 #pragma unroll
     for (int h = 0; h < G; ++h)
-        M[h] = fmaxf(fmaxf(wred[h], wred[G + h]), fmaxf(wred[2 * G + h], wred[3 * G + h]));
+        if (lc == h) Mm = M[h];
+    const bool live = lc < G && Mm > -__builtin_inff();
+    v4f o[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) o[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float lsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r0 = 32 * u + 8 * j;             // first of this lane's 8 positions (wave-local)
+        float p[8];
+        if (live) {
+            const float4 a0 = *reinterpret_cast<const float4*>(&sc[min(lc, G - 1)][w * kTpw + r0]);
+            const float4 a1 = *reinterpret_cast<const float4*>(&sc[min(lc, G - 1)][w * kTpw + r0 + 4]);
+            const float sv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) p[k] = __builtin_amdgcn_exp2f(sv[k] - Mm);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) p[k] = 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) lsum += p[k];
+        // weights per group: P'_g[k] = f16(p[k] * vs[k][g])
+        v8h pw[4];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint2 s2 = *reinterpret_cast<const uint2*>(&vss[w][2 * (r0 + k)]);
+            const uint32_t sw[4] = {s2.x & 0xffff, s2.x >> 16, s2.y & 0xffff, s2.y >> 16};
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                pw[g][k] = static_cast<_Float16>(p[k] * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sw[g]))));
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            // lanes 2 k and 2 k + 1 of the group give row r0 + k's channels 16 ct .. + 7 and + 8 .. + 15;
+            // lane lc receives channel 16 ct + lc of the 8 rows
+            typedef __attribute__((address_space(3))) v2i* lv2p;
+            const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lv2p)(vst[w] + (r0 + (lc >> 1)) * kD + 16 * ct + 8 * (lc & 1)));
+            o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[ct >> 1], i8x8_to_f16(raw[0], raw[1]), o[ct], 0, 0, 0);
+        }
+    }
+    lsum += shfl_xor(lsum, 16);
+    lsum += shfl_xor(lsum, 32);
 
-    // ---- pass 2: p = 2^(s - M), acc += p * v (missing positions have s = -inf: p = 0, v = 0)
-    float acc[G][16], ls[G];
+    // ---- the 4 waves' partials (same max) summed; lane (j, lc) of o[ct] holds heads 4 j + i, channel 16 ct + lc
+    float* red = reinterpret_cast<float*>(vst[w]);   // this wave's own rows: read by nobody else
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        ls[h] = 0.0f;
+    for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[h][c] = 0.0f;
-    }
-    const bool any = M[0] > -__builtin_inff();   // every head's max is finite iff a position exists
-    if (any) {
-#pragma unroll
-        for (int st = 0; st < ST; ++st) {
-            const int tl = w * kTpw + 8 * st + tr;
-            float vf[16];
-            unpack_i8x16(vraw[st], vf);
-#pragma unroll
-            for (int c = 0; c < 16; ++c) vf[c] = vf[c] * vsc[st];
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = __builtin_amdgcn_exp2f(sc[tl * G + h] - M[h]);
-                ls[h] += p;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) acc[h][c] = __builtin_fmaf(p, vf[c], acc[h][c]);
-            }
-        }
-    }
-    // reduce over the 8 token lanes of each channel slice, then over the 4 waves
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int off = 8; off < 64; off <<= 1) {
-            ls[h] += shfl_xor(ls[h], off);
-#pragma unroll
-            for (int c = 0; c < 16; ++c) acc[h][c] += shfl_xor(acc[h][c], off);
-        }
-    }
-    __syncthreads();  // wred reuse
-    if (tr == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c) red[(w * G + h) * kD + 16 * lc + c] = acc[h][c];
-        }
-    }
-    if (l == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) wred[w * G + h] = ls[h];
-    }
+        for (int i = 0; i < 4; ++i)
+            if (4 * j + i < G) red[(4 * j + i) * kD + 16 * ct + lc] = o[ct][i];
+    if (j == 0 && lc < G) lred[w][lc] = lsum;
     __syncthreads();
     const int nseg = a.segs;
-    for (int i = tid; i < G * (kD + 2); i += 256) {
-        const int h = i / (kD + 2), c = i % (kD + 2);
+    for (int idx = tid; idx < G * (kD + 2); idx += 256) {
+        const int h = idx / (kD + 2), c = idx % (kD + 2);
         float v;
-        if (c < kD) v = (red[h * kD + c] + red[(G + h) * kD + c]) + (red[(2 * G + h) * kD + c] + red[(3 * G + h) * kD + c]);
-        else if (c == kD) v = M[h];
-        else v = (wred[h] + wred[G + h]) + (wred[2 * G + h] + wred[3 * G + h]);
+        if (c < kD) {
+            const float* r0 = reinterpret_cast<const float*>(vst[0]);
+            const float* r1 = reinterpret_cast<const float*>(vst[1]);
+            const float* r2 = reinterpret_cast<const float*>(vst[2]);
+            const float* r3 = reinterpret_cast<const float*>(vst[3]);
+            v = (r0[h * kD + c] + r1[h * kD + c]) + (r2[h * kD + c] + r3[h * kD + c]);
+        } else if (c == kD) {
+            float mh = -__builtin_inff();
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+                if (q == h) mh = M[q];
+            v = mh;
+        } else {
+            v = (lred[0][h] + lred[1][h]) + (lred[2][h] + lred[3][h]);
+        }
         a.part[((static_cast<int64_t>(n) * a.Hq + hk * G + h) * nseg + seg) * (kD + 2) + c] = v;
     }
 }
@@ -214,7 +293,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 // Merge the segments of one (sequence, query head): weights 2^(M_s - max M).
 __global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
     const int c = threadIdx.x, hq = blockIdx.x, n = blockIdx.y;
-    const int L = min(a.lens[n], a.max_len);
+    const int L = a.num_blocks > 0 ? min(a.lens[n], a.max_len) : 0;
     const int nseg = L > 0 ? (L + kSeg - 1) / kSeg : 0;
     const float* p = a.part + (static_cast<int64_t>(n) * a.Hq + hq) * a.segs * (kD + 2);
     float mg = -__builtin_inff();
@@ -238,7 +317,8 @@ inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 int launch_decode(const DecodeArgs& a, void* stream) {
     if (a.N == 0) return SQ_OK;
     const int G = a.Hq / a.Hk;
-    dim3 g1(static_cast<unsigned>(a.Hk), static_cast<unsigned>(a.segs), static_cast<unsigned>(a.N));
+    const int64_t chunks = static_cast<int64_t>(a.segs) * a.N;      // (sequence, segment) pairs
+    dim3 g1(static_cast<unsigned>((chunks + 7) / 8 * 8 * a.Hk));
     switch (G) {
     case 1: hipLaunchKernelGGL(k_decode_split<1>, g1, dim3(256), 0, S(stream), a); break;
     case 2: hipLaunchKernelGGL(k_decode_split<2>, g1, dim3(256), 0, S(stream), a); break;
