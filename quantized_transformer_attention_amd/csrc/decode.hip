@@ -65,9 +65,7 @@ template <int G>
 __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float sc[G][kSeg];             // scores [head][position]
     __shared__ __attribute__((aligned(1024))) uint8_t vst[4][kTpw * kD];   // each wave's V rows; then its partial acc
-    __shared__ __attribute__((aligned(16))) uint32_t vss[4][kTpw * 2];     // their scales (4 FP16 per row)
-    __shared__ float wred[4][G];
-    __shared__ float lred[4][G];
+    __shared__ __attribute__((aligned(16))) float4 vsf[4][kTpw];           // their scales as FP32 (4 per row)
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, j = l >> 4, lc = l & 15;
     // The Hk workgroups of one (sequence, segment) run back to back on one XCD (workgroup i
     // goes to XCD i % 8), so each cache slot's rows and scale rows (all heads side by side in
@@ -161,7 +159,11 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
                 qa[g][k] = lc < G ? static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[g][k], sh)) : static_cast<_Float16>(0.0f);
     }
 
-    // ---- pass 1: scores of the wave's 64 positions
+    // ---- pass 1: scores of the wave's 64 positions. Lane (j, lc) produces heads 4 j + i; their
+    // score scale softmax_scale * log2 e * 2^-sh (a power-of-two change of a float: exact)
+    float scl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scl[i] = __builtin_amdgcn_ldexpf(a.scale, -__shfl(sh, min(4 * j + i, 15), kWave));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         v4f dg[4];
@@ -181,8 +183,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
             sv = __builtin_fmaf(dg[1][i], k1, sv);
             sv = __builtin_fmaf(dg[2][i], k2, sv);
             sv = __builtin_fmaf(dg[3][i], k3, sv);
-            const int shh = __shfl(sh, min(h, 15), kWave);
-            sv = __builtin_amdgcn_ldexpf(sv, -shh) * a.scale;
+            sv = sv * scl[i];
             if (h < G) sc[h][w * kTpw + 16 * t + lc] = ok ? sv : -__builtin_inff();
         }
     }
@@ -192,22 +193,22 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(vst[w] + 1024 * r + 16 * l) = vraw[r];
     {
         const bool okv = rowbase[l >> 4] >= 0 && wp0 + l < s1;
-        *reinterpret_cast<uint2*>(&vss[w][2 * l]) = okv ? vsr : make_uint2(0u, 0u);
+        const h2 s01 = __builtin_bit_cast(h2, vsr.x), s23 = __builtin_bit_cast(h2, vsr.y);
+        vsf[w][l] = okv ? make_float4(static_cast<float>(s01[0]), static_cast<float>(s01[1]), static_cast<float>(s23[0]),
+                                      static_cast<float>(s23[1]))
+                        : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     __syncthreads();
 
-    // ---- segment max per query head (thread tid: position tid)
+    // ---- segment max per query head, by every wave over all 256 positions (no exchange)
     float M[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float m = sc[h][tid];
+        float m = fmaxf(fmaxf(sc[h][l], sc[h][64 + l]), fmaxf(sc[h][128 + l], sc[h][192 + l]));
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
-        if (l == 0) wred[w][h] = m;
+        M[h] = m;
     }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) M[h] = fmaxf(fmaxf(wred[0][h], wred[1][h]), fmaxf(wred[2][h], wred[3][h]));
 
     // ---- pass 2: p = 2^(s - M), acc += f16(p vs) . v
     float Mm = -__builtin_inff();
@@ -239,11 +240,11 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
         v8h pw[4];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const uint2 s2 = *reinterpret_cast<const uint2*>(&vss[w][2 * (r0 + k)]);
-            const uint32_t sw[4] = {s2.x & 0xffff, s2.x >> 16, s2.y & 0xffff, s2.y >> 16};
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                pw[g][k] = static_cast<_Float16>(p[k] * static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sw[g]))));
+            const float4 sf = vsf[w][r0 + k];
+            pw[0][k] = static_cast<_Float16>(p[k] * sf.x);
+            pw[1][k] = static_cast<_Float16>(p[k] * sf.y);
+            pw[2][k] = static_cast<_Float16>(p[k] * sf.z);
+            pw[3][k] = static_cast<_Float16>(p[k] * sf.w);
         }
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
@@ -265,7 +266,9 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (4 * j + i < G) red[(4 * j + i) * kD + 16 * ct + lc] = o[ct][i];
-    if (j == 0 && lc < G) lred[w][lc] = lsum;
+    // this wave's exp-sums in its own (now unused) scale rows
+    float* lred = reinterpret_cast<float*>(vsf[w]);
+    if (j == 0 && lc < G) lred[lc] = lsum;
     __syncthreads();
     const int nseg = a.segs;
     for (int idx = tid; idx < G * (kD + 2); idx += 256) {
@@ -284,7 +287,11 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
                 if (q == h) mh = M[q];
             v = mh;
         } else {
-            v = (lred[0][h] + lred[1][h]) + (lred[2][h] + lred[3][h]);
+            const float* l0 = reinterpret_cast<const float*>(vsf[0]);
+            const float* l1 = reinterpret_cast<const float*>(vsf[1]);
+            const float* l2 = reinterpret_cast<const float*>(vsf[2]);
+            const float* l3 = reinterpret_cast<const float*>(vsf[3]);
+            v = (l0[h] + l1[h]) + (l2[h] + l3[h]);
         }
         a.part[((static_cast<int64_t>(n) * a.Hq + hk * G + h) * nseg + seg) * (kD + 2) + c] = v;
     }
