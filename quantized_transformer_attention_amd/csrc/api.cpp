@@ -39,7 +39,13 @@ int check_prologue(const sq_rows* x, const sq_norm* n, const sq_rope* r, const c
     int st = check_rows(x, what);
     if (!st) st = check_norm(n, x, what);
     if (!st) st = check_rope(r, x, what);
-    return st;
+    if (st) return st;
+    // rows of a tile are addressed by 24-bit byte offsets from the tile's first token
+    constexpr int64_t kMaxTokenBytes = int64_t(1) << 24;
+    if (x->st * 2 >= kMaxTokenBytes || (r && r->mode != SQ_ROPE_NONE && r->rs * 4 >= kMaxTokenBytes) ||
+        (n && n->mode == SQ_NORM_ALL_HEADS && n->mean_sq && n->mst * 4 >= kMaxTokenBytes))
+        return fail(SQ_ERR_STRIDE, "%s: a token stride of x, the rope table or mean_sq spans 16 MiB or more", what);
+    return SQ_OK;
 }
 
 }  // namespace
@@ -108,6 +114,7 @@ int sq_quant_qk(const sq_rows* x, const sq_norm* norm, const sq_rope* rope, cons
     if (ob < 0 || ot < 0 || oh < 0 || ssb < 0 || ssh < 0) return fail(SQ_ERR_STRIDE, "sq_quant_qk: negative stride");
     if ((reinterpret_cast<uintptr_t>(codes) & 7) || ob % 8 || ot % 8 || oh % 8)
         return fail(SQ_ERR_ALIGN, "sq_quant_qk: code rows must start on 8-byte boundaries");
+    if (ot >= (int64_t(1) << 24)) return fail(SQ_ERR_STRIDE, "sq_quant_qk: the code token stride spans 16 MiB or more");
     if (mean && ((reinterpret_cast<uintptr_t>(mean) & 15) || mb % 4 || mh % 4))
         return fail(SQ_ERR_ALIGN, "sq_quant_qk: mean rows must be 16-byte aligned");
     if (!std::isfinite(sm_scale) || !std::isfinite(scale_eps) || scale_eps < 0.0f)

@@ -24,6 +24,15 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
 // Round to bfloat16, nearest even (v_cvt_pk_bf16_f32), back to float.
 __device__ __forceinline__ float bf16_round(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
 
+// Both of a and b rounded to bf16 (nearest even) by one paired conversion.
+__device__ __forceinline__ void bf16_round2(float& a, float& b) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){a, b}, b2_t));
+    a = __uint_as_float(u << 16);
+    b = __uint_as_float(u & 0xffff0000u);
+}
+
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
@@ -62,6 +71,55 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
 //   8 slots per row (128 B):  f(r) = (r & 7) ^ ((r >> 3) & 1)
 //   4 slots per row (64 B):   f(r) = (r >> 1) & 3
 //   16 slots per row (256 B): f(r) = r & 15
+// Lane (l + n) mod 16 of lane l's 16-lane row (DPP row rotate).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + N, 0xf, 0xf, true));
+}
+
+// Reductions over a row of LPR lanes (LPR in {8, 16}); every lane of the row gets the
+// result. The sum adds partners at lane offsets LPR/2, .., 2, 1 in that order: rotating a
+// 16-lane row by 8, 4, 2, 1 pairs each lane with the same values as xor offsets 8, 4, 2, 1
+// (after a step the row repeats with that period), so both give the same bits.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float p) {
+    if constexpr (LPR == 16) {
+        p = p + row_ror<8>(p);
+        p = p + row_ror<4>(p);
+        p = p + row_ror<2>(p);
+        p = p + row_ror<1>(p);
+    } else {
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) p = p + __shfl_xor(p, off, kWave);
+    }
+    return p;
+}
+
+// Maximum of non-negative, non-NaN values (compared as their bit patterns, which order
+// such floats; 0 is then the identity that lets the rotation fold into the max).
+template <int LPR>
+__device__ __forceinline__ float row_max(float m) {
+    if constexpr (LPR == 16) {
+        uint32_t u = __float_as_uint(m);
+        u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x128, 0xf, 0xf, true)));
+        u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x124, 0xf, 0xf, true)));
+        u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x122, 0xf, 0xf, true)));
+        u = max(u, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), 0x121, 0xf, 0xf, true)));
+        m = __uint_as_float(u);
+    } else {
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    }
+    return m;
+}
+
+// Lane J of this lane's LPR-lane row (a swizzle inside the 32-lane half; rows are aligned).
+template <int LPR, int J>
+__device__ __forceinline__ float row_lane(float v) {
+    constexpr int pattern = (0x1f & ~(LPR - 1)) | (J << 5);
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), pattern));
+}
+
 template <int NS>
 __device__ __forceinline__ int swz(int row, int slot) {
     if constexpr (NS == 8) return slot ^ ((row & 7) ^ ((row >> 3) & 1));

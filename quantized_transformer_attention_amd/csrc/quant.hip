@@ -48,101 +48,199 @@ __device__ __forceinline__ float row_sumsq(const float* x) {
     float p = x[0] * x[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) p = __builtin_fmaf(x[k], x[k], p);
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) p = p + shfl_xor(p, off);
-    return p;
+    return row_sum<LPR>(p);
 }
 
-// cos and sin of pairs p0 .. p0 + 3 of a table row
-template <bool CONTIG>
-__device__ __forceinline__ void load_pairs4(const float* tb, const RowArgs& a, int64_t p0, float* cs, float* sn) {
-    if constexpr (CONTIG) {
-        const float4 u = *reinterpret_cast<const float4*>(tb + 2 * p0);
-        const float4 v = *reinterpret_cast<const float4*>(tb + 2 * p0 + 4);
-        cs[0] = u.x; sn[0] = u.y; cs[1] = u.z; sn[1] = u.w;
-        cs[2] = v.x; sn[2] = v.y; cs[3] = v.z; sn[3] = v.w;
-    } else {
+// Row prologue [quant] _rows: z = rotate(bf16(norm(x) * w)) for the 8 channels a lane
+// holds of row (b, t, h), in two halves so that a wave can put the loads of all its rows
+// in flight before it computes any of them: row_fetch issues the loads (unconditionally,
+// so a caller passes a row index clamped into [0, T) and masks the result of a row past
+// the end), rows4 computes four steps of rows. Every lane of a row takes part in rows4
+// (the norm's butterfly and the shared root). ROPE_SPLIT_HALF here rotates all D/2 pairs (the entry point checks
+// pairs == D/2). PERTOK: a weight row per token (RowArgs::wrows), else one shared row.
+template <int NORM, int ROPE, bool PERTOK>
+struct RowRaw {
+    uint2 xu, xv;     // bf16 channels 4 lc .. 4 lc + 3 and D/2 + 4 lc .. D/2 + 4 lc + 3
+    float ms;         // all-heads mean square of the token
+    uint2 wu, wv;     // per-token weight row, same channels as x
+    float tc[8];      // rotation table: cos 0..3 in tc[0..3], sin 0..3 in tc[4..7]
+};
+
+// Where the rows of a token range start (the range's first token t0 at (b, h)): a row
+// t0 + rr of a tensor sits rr times its token stride in bytes past the base; the entry
+// points keep those strides under 16 MiB, so a 24-bit multiply gives the offset.
+struct RowBase {
+    const char* x;
+    const char* ms;
+    const char* tb;
+    const int32_t* wr;
+    uint32_t xst, mst, tst;
+
+    __device__ __forceinline__ RowBase(const RowArgs& a, int64_t b, int64_t t0, int64_t h) {
+        x = reinterpret_cast<const char*>(a.x + b * a.sb + t0 * a.st + h * a.sh);
+        ms = a.ms ? reinterpret_cast<const char*>(a.ms + b * a.msb + t0 * a.mst) : nullptr;
+        tb = a.table ? reinterpret_cast<const char*>(a.table + a.rb * b + a.rs * t0) : nullptr;
+        wr = a.wrows ? a.wrows + t0 : nullptr;
+        xst = static_cast<uint32_t>(a.st * 2);
+        mst = static_cast<uint32_t>(a.mst * 4);
+        tst = static_cast<uint32_t>(a.rs * 4);
+    }
+};
+
+// Loads of row t0 + rr (rr < T - t0).
+template <int D, int NORM, int ROPE, bool CONTIG, bool PERTOK>
+__device__ __forceinline__ void row_fetch(const RowArgs& a, const RowBase& rb, uint32_t rr, int64_t h, int lc,
+                                          int64_t wrow, RowRaw<NORM, ROPE, PERTOK>& r) {
+    const char* xr = rb.x + __umul24(rr, rb.xst);
+    r.xu = *reinterpret_cast<const uint2*>(xr + 8 * lc);
+    r.xv = *reinterpret_cast<const uint2*>(xr + D + 8 * lc);
+    if constexpr (NORM == SQ_NORM_ALL_HEADS) r.ms = *reinterpret_cast<const float*>(rb.ms + __umul24(rr, rb.mst));
+    if constexpr (NORM != SQ_NORM_NONE && PERTOK) {
+        const uint16_t* wr = a.w + wrow * a.wd + (NORM == SQ_NORM_ALL_HEADS ? h * D : 0);
+        r.wu = *reinterpret_cast<const uint2*>(wr + 4 * lc);
+        r.wv = *reinterpret_cast<const uint2*>(wr + D / 2 + 4 * lc);
+    }
+    if constexpr (ROPE != SQ_ROPE_NONE) {
+        const float* tb = reinterpret_cast<const float*>(rb.tb + __umul24(rr, rb.tst));
+        if constexpr (ROPE == SQ_ROPE_SPLIT_HALF && CONTIG) {
+            // pairs 4 lc .. 4 lc + 3, stored (cos, sin) interleaved
+            const float4 u = *reinterpret_cast<const float4*>(tb + 8 * lc);
+            const float4 v = *reinterpret_cast<const float4*>(tb + 8 * lc + 4);
+            r.tc[0] = u.x; r.tc[4] = u.y; r.tc[1] = u.z; r.tc[5] = u.w;
+            r.tc[2] = v.x; r.tc[6] = v.y; r.tc[3] = v.z; r.tc[7] = v.w;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            cs[k] = tb[a.rp * (p0 + k)];
-            sn[k] = tb[a.rp * (p0 + k) + a.rc];
+            for (int u = 0; u < 4; ++u) {
+                // split half: pairs 4 lc + u; interleaved: pairs 2 lc, 2 lc + 1, D/4 + 2 lc, D/4 + 2 lc + 1
+                // (a pair past the rotated count reads pair 0 and is not applied)
+                int64_t pair = ROPE == SQ_ROPE_SPLIT_HALF ? 4 * lc + u : (u < 2 ? 0 : D / 4) + 2 * lc + (u & 1);
+                if (pair >= a.pairs) pair = 0;
+                r.tc[u] = tb[a.rp * pair];
+                r.tc[4 + u] = tb[a.rp * pair + a.rc];
+            }
         }
     }
 }
 
-// Row prologue [quant] _rows: z = rotate(bf16(norm(x) * w)) for the 8 channels a lane
-// holds of row (b, t, h). Every lane of the row must call it (the norm's butterfly);
-// rows with valid == false read nothing and their result is unspecified.
-// ROPE_SPLIT_HALF here rotates all D/2 pairs (the entry point checks pairs == D/2).
-template <int D, int NORM, int ROPE, bool CONTIG>
-__device__ __forceinline__ void row_prologue(const RowArgs& a, int64_t b, int64_t t, int64_t h, int lc, bool valid,
-                                             float* z) {
-    constexpr int LPR = D / 8;
-    float x[8], y[8];
-    if (valid) load_row_bf16<D>(a.x + b * a.sb + t * a.st + h * a.sh, lc, x);
-    else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = 0.0f;
-    }
+// First half of a row's arithmetic: its 8 channels in x and, with a norm, the value
+// ms + eps whose reciprocal square root scales the row.
+template <int D, int NORM, int ROPE, bool PERTOK>
+__device__ __forceinline__ float row_stats(const RowArgs& a, const RowRaw<NORM, ROPE, PERTOK>& r, float* x) {
+    x[0] = bf16_lo(r.xu.x); x[1] = bf16_hi(r.xu.x); x[2] = bf16_lo(r.xu.y); x[3] = bf16_hi(r.xu.y);
+    x[4] = bf16_lo(r.xv.x); x[5] = bf16_hi(r.xv.x); x[6] = bf16_lo(r.xv.y); x[7] = bf16_hi(r.xv.y);
+    if constexpr (NORM == SQ_NORM_HEAD) return row_sumsq<D / 8>(x) / static_cast<float>(D) + a.eps;
+    else if constexpr (NORM == SQ_NORM_ALL_HEADS) return r.ms + a.eps;
+    else return 1.0f;
+}
+
+// 1 / sqrt(v[j]) (both steps correctly rounded) for the four rows v[0..3] of a lane's
+// four consecutive steps: lane lc of a row evaluates step lc mod 4, then each step takes
+// its value from that lane of the row, so a wave evaluates the root once per four steps.
+template <int LPR>
+__device__ __forceinline__ void inv_rms4(const float* v, int lc, float* inv) {
+    const float t0 = (lc & 1) ? v[1] : v[0], t1 = (lc & 1) ? v[3] : v[2];
+    const float r = 1.0f / sqrtf((lc & 2) ? t1 : t0);
+    inv[0] = row_lane<LPR, 0>(r);
+    inv[1] = row_lane<LPR, 1>(r);
+    inv[2] = row_lane<LPR, 2>(r);
+    inv[3] = row_lane<LPR, 3>(r);
+}
+
+// Second half: z = rotate(bf16(x * inv * w)).
+template <int D, int NORM, int ROPE, bool PERTOK>
+__device__ __forceinline__ void row_apply(const RowArgs& a, const RowRaw<NORM, ROPE, PERTOK>& r, const float* x,
+                                          float inv, const float* wsh, int lc, float* z) {
+    float y[8];
     if constexpr (NORM == SQ_NORM_NONE) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) y[k] = x[k];
     } else {
-        float ms;
-        if constexpr (NORM == SQ_NORM_HEAD) {
-            ms = row_sumsq<LPR>(x) / static_cast<float>(D);
-        } else {
-            ms = valid ? a.ms[b * a.msb + t * a.mst] : 1.0f;
-        }
-        const float inv = 1.0f / sqrtf(ms + a.eps);
-        const int64_t wrow = (a.wrows && valid) ? a.wrows[t] : 0;
         float w[8];
-        load_row_bf16<D>(a.w + wrow * a.wd + (NORM == SQ_NORM_ALL_HEADS ? h * D : 0), lc, w);
+        if constexpr (PERTOK) {
+            w[0] = bf16_lo(r.wu.x); w[1] = bf16_hi(r.wu.x); w[2] = bf16_lo(r.wu.y); w[3] = bf16_hi(r.wu.y);
+            w[4] = bf16_lo(r.wv.x); w[5] = bf16_hi(r.wv.x); w[6] = bf16_lo(r.wv.y); w[7] = bf16_hi(r.wv.y);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) y[k] = bf16_round((x[k] * inv) * w[k]);
+            for (int k = 0; k < 8; ++k) w[k] = wsh[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = (x[k] * inv) * w[k];
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) bf16_round2(y[k], y[k + 1]);
     }
     if constexpr (ROPE == SQ_ROPE_NONE) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) z[k] = y[k];
     } else if constexpr (ROPE == SQ_ROPE_SPLIT_HALF) {
         // channel 4 lc + k (leading) with its partner D/2 + 4 lc + k (trailing), pair 4 lc + k
-        float cs[4], sn[4];
-        if (valid) load_pairs4<CONTIG>(a.table + a.rb * b + a.rs * t, a, 4 * lc, cs, sn);
-        else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) { cs[k] = 1.0f; sn[k] = 0.0f; }
-        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            z[k] = __builtin_fmaf(cs[k], y[k], (-sn[k]) * y[4 + k]);
-            z[4 + k] = __builtin_fmaf(sn[k], y[k], cs[k] * y[4 + k]);
+            const float cs = r.tc[k], sn = r.tc[4 + k];
+            z[k] = __builtin_fmaf(cs, y[k], (-sn) * y[4 + k]);
+            z[4 + k] = __builtin_fmaf(sn, y[k], cs * y[4 + k]);
         }
-    } else {  // interleaved: channel 2p with 2p + 1; pairs 2 lc, 2 lc + 1 and D/4 + 2 lc, D/4 + 2 lc + 1
-        const float* tb = a.table + a.rb * b + a.rs * t;
+    } else {  // interleaved: channel 2p with 2p + 1
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t pair = (u < 2 ? 0 : D / 4) + 2 * lc + (u & 1);
             const int k = 2 * u;
-            if (valid && pair < a.pairs) {
-                const float cs = tb[a.rp * pair], sn = tb[a.rp * pair + a.rc];
-                z[k] = __builtin_fmaf(cs, y[k], (-sn) * y[k + 1]);
-                z[k + 1] = __builtin_fmaf(sn, y[k], cs * y[k + 1]);
-            } else {
-                z[k] = y[k];
-                z[k + 1] = y[k + 1];
-            }
+            const float cs = r.tc[u], sn = r.tc[4 + u];
+            const float z0 = __builtin_fmaf(cs, y[k], (-sn) * y[k + 1]);
+            const float z1 = __builtin_fmaf(sn, y[k], cs * y[k + 1]);
+            const bool rot = pair < a.pairs;
+            z[k] = rot ? z0 : y[k];
+            z[k + 1] = rot ? z1 : y[k + 1];
         }
     }
 }
 
-__device__ __forceinline__ int local_group(int r, int layout, int block) {
-    switch (layout) {
-    case SQ_LAYOUT_THREAD_Q: return 8 * (r >> 5) + (r & 7);
-    case SQ_LAYOUT_THREAD_K: return 4 * (r >> 6) + ((r & 7) >> 1);
-    case SQ_LAYOUT_WARP_Q: return r >> 5;
-    default: return r / block;
+// Steps s0 .. s0 + 3 of a lane's fetched rows through both halves into z.
+template <int D, int NORM, int ROPE, bool PERTOK>
+__device__ __forceinline__ void rows4(const RowArgs& a, const RowRaw<NORM, ROPE, PERTOK>* raw, const float* wsh,
+                                      int lc, float (*z)[8]) {
+    float x[4][8], v[4], inv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = row_stats<D, NORM, ROPE, PERTOK>(a, raw[j], x[j]);
+    if constexpr (NORM != SQ_NORM_NONE) inv_rms4<D / 8>(v, lc, inv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) row_apply<D, NORM, ROPE, PERTOK>(a, raw[j], x[j], inv[j], wsh, lc, z[j]);
+}
+
+// The shared weight row of a head (PERTOK == false); unused without a norm.
+template <int D, int NORM>
+__device__ __forceinline__ void load_shared_weights(const RowArgs& a, int64_t h, int lc, float* w) {
+    if constexpr (NORM != SQ_NORM_NONE)
+        load_row_bf16<D>(a.w + (NORM == SQ_NORM_ALL_HEADS ? h * D : 0), lc, w);
+}
+
+// Weight rows of N tokens t0 + rr[i] (all 0 without per-token rows), loaded together.
+template <int N>
+__device__ __forceinline__ void load_wrows(const RowArgs& a, const RowBase& rb, const uint32_t* rr, int64_t* wrow) {
+    if (a.wrows) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) wrow[i] = rb.wr[rr[i]];
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) wrow[i] = 0;
     }
 }
+
+// Group of row r (0..127) of a tile: ((r >> sh) << mul) + ((r & mask) >> low), with the
+// four layouts' shifts and masks:
+//   THREAD_Q 8 (r / 32) + r mod 8;  THREAD_K 4 (r / 64) + (r mod 8) / 2;
+//   WARP_Q r / 32;                  PER_BLOCK r / block (block 32, 64 or 128).
+struct GroupMap {
+    int sh, mul, mask, low;
+    __device__ __forceinline__ GroupMap(int layout, int block) {
+        switch (layout) {
+        case SQ_LAYOUT_THREAD_Q: sh = 5; mul = 3; mask = 7; low = 0; break;
+        case SQ_LAYOUT_THREAD_K: sh = 6; mul = 2; mask = 7; low = 1; break;
+        case SQ_LAYOUT_WARP_Q: sh = 5; mul = 0; mask = 0; low = 0; break;
+        default: sh = block == 32 ? 5 : (block == 64 ? 6 : 7); mul = 0; mask = 0; low = 0; break;
+        }
+    }
+    __device__ __forceinline__ int operator()(int r) const { return ((r >> sh) << mul) + ((r & mask) >> low); }
+};
 
 __host__ __device__ __forceinline__ int groups_per_tile(int layout, int block) {
     switch (layout) {
@@ -154,53 +252,79 @@ __host__ __device__ __forceinline__ int groups_per_tile(int layout, int block) {
 }
 
 // ---------------------------------------------------------------- A1: mean squares over all heads
+// One wave per token; the heads go HPI at a time (a row per HPI-lane group), NB such
+// steps with their loads in flight together. Heads past H read head H - 1 and add nothing.
 template <int D>
 __global__ __launch_bounds__(256) void k_norm_stats(NormStatsArgs a) {
-    constexpr int LPR = D / 8, HPI = kWave / LPR;
+    constexpr int LPR = D / 8, HPI = kWave / LPR, NB = 4;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lc = lane % LPR, lr = lane / LPR;
     const int64_t tok = static_cast<int64_t>(blockIdx.x) * 4 + w;
     if (tok >= a.B * a.T) return;  // wave-uniform
     const int64_t b = tok / a.T, t = tok % a.T;
+    const uint16_t* xt = a.x + b * a.sb + t * a.st;
     float tot = 0.0f;
-    for (int64_t h0 = 0; h0 < a.H; h0 += HPI) {
-        const int64_t h = h0 + lr;
-        float x[8];
-        if (h < a.H) load_row_bf16<D>(a.x + b * a.sb + t * a.st + h * a.sh, lc, x);
-        else {
+    for (int64_t h0 = 0; h0 < a.H; h0 += HPI * NB) {
+        uint2 u[NB], v[NB];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+        for (int j = 0; j < NB; ++j) {
+            const int64_t h = h0 + HPI * j + lr < a.H ? h0 + HPI * j + lr : a.H - 1;
+            u[j] = *reinterpret_cast<const uint2*>(xt + h * a.sh + 4 * lc);
+            v[j] = *reinterpret_cast<const uint2*>(xt + h * a.sh + D / 2 + 4 * lc);
         }
-        const float p = row_sumsq<LPR>(x);
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its arithmetic
 #pragma unroll
-        for (int j = 0; j < HPI; ++j) {
-            const float s = __shfl(p, j * LPR, kWave);
-            if (h0 + j < a.H) tot = tot + s;
+        for (int j = 0; j < NB; ++j) {
+            const float x[8] = {bf16_lo(u[j].x), bf16_hi(u[j].x), bf16_lo(u[j].y), bf16_hi(u[j].y),
+                                bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y), bf16_hi(v[j].y)};
+            const float p = row_sumsq<LPR>(x);
+#pragma unroll
+            for (int i = 0; i < HPI; ++i) {
+                const float s = __shfl(p, i * LPR, kWave);
+                if (h0 + HPI * j + i < a.H) tot = tot + s;
+            }
         }
     }
     if (lane == 0) a.ms[b * a.msb + t * a.mst] = tot / static_cast<float>(a.H * D);
 }
 
 // ---------------------------------------------------------------- A2: k mean
-// One wave per 64-row block, 4 blocks per workgroup: row 4i + r (i = 0..15) joins
-// partial r; the block's sum is (S0 + S1) + (S2 + S3), written to partial (b, h, blk, :).
-template <int D, int NORM, int ROPE, bool CONTIG>
-__global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
+// A lane's 16 rows in four steps of 4 rows; the loads of a step go out before the
+// arithmetic of the step ahead of it, so two steps of loads are in flight at the start
+// and one while a step computes.
+template <int D, int NORM, int ROPE, bool CONTIG, bool PERTOK>
+__device__ __forceinline__ void kmean_block(const KmeanArgs& a, int64_t b, int64_t h, int64_t blk, int lc, int r) {
     constexpr int LPR = D / 8;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lc = lane % LPR, r = lane / LPR;
-    const int64_t nbg = (a.nblk + 3) / 4, items = nbg * a.r.B * a.r.H;
-    const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
-    if (item >= items) return;  // uniform over the workgroup
-    const int64_t h = item % a.r.H, b = (item / a.r.H) % a.r.B, blk = (item / (a.r.H * a.r.B)) * 4 + w;
-    if (blk >= a.nblk) return;  // wave-uniform
     const bool active = r < 4;
+    float wsh[8];
+    if constexpr (!PERTOK) load_shared_weights<D, NORM>(a.r, h, lc, wsh);
     float S[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i = 0; i < 16; ++i) {
-        const int64_t t = blk * 64 + 4 * i + r;
-        const bool valid = active && t < a.r.T;
-        float z[8];
-        row_prologue<D, NORM, ROPE, CONTIG>(a.r, b, t, h, lc, valid, z);
+    const RowBase base(a.r, b, blk * 64, h);
+    const uint32_t rlast = static_cast<uint32_t>(a.r.T - blk * 64 < 64 ? a.r.T - blk * 64 - 1 : 63);
+    uint32_t rr[16];
+    int64_t wrow[16] = {};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) S[k] = S[k] + (valid ? z[k] : 0.0f);
+    for (int i = 0; i < 16; ++i) rr[i] = min(static_cast<uint32_t>(4 * i + r), rlast);
+    if constexpr (PERTOK) load_wrows<16>(a.r, base, rr, wrow);
+    RowRaw<NORM, ROPE, PERTOK> raw[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) row_fetch<D, NORM, ROPE, CONTIG, PERTOK>(a.r, base, rr[i], h, lc, wrow[i], raw[i]);
+#pragma unroll
+    for (int j0 = 0; j0 < 16; j0 += 4) {
+        __builtin_amdgcn_sched_barrier(0);  // the step's loads stay ahead of the arithmetic below
+        float z[4][8];
+        rows4<D, NORM, ROPE, PERTOK>(a.r, raw + j0, wsh, lc, z);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool valid = active && blk * 64 + 4 * (j0 + j) + r < a.r.T;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) S[k] = S[k] + (valid ? z[j][k] : 0.0f);
+        }
+        if (j0 + 8 < 16) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = j0 + 8; i < j0 + 12; ++i)
+                row_fetch<D, NORM, ROPE, CONTIG, PERTOK>(a.r, base, rr[i], h, lc, wrow[i], raw[i]);
+        }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) S[k] = S[k] + shfl_xor(S[k], LPR);
@@ -213,35 +337,110 @@ __global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
     }
 }
 
-// One workgroup per (b, h): block sums are added in chunks of 16 consecutive blocks
-// (ascending within a chunk), the chunk sums in ascending order, then divided by T.
-// The chunks of a group of 32 are summed in parallel, their sums kept in LDS.
-__global__ __launch_bounds__(256) void k_kmean_final(KmeanArgs a) {
-    constexpr int CG = 32, CB = 16;
-    __shared__ float cs[CG * 128];
-    const int64_t D = a.r.D, bh = blockIdx.x, b = bh / a.r.H, h = bh % a.r.H;
-    const int tid = threadIdx.x, c = tid % D, r = tid / D, rpw = 256 / D;
-    const float* part = a.partial + bh * a.nblk * D;
+// One wave per 64-row block, 4 blocks per workgroup: row 4i + r (i = 0..15) joins
+// partial r; the block's sum is (S0 + S1) + (S2 + S3), written to partial (b, h, blk, :).
+template <int D, int NORM, int ROPE, bool CONTIG, bool PERTOK>
+__global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
+    constexpr int LPR = D / 8;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lc = lane % LPR, r = lane / LPR;
+    const int64_t nbg = (a.nblk + 3) / 4, items = nbg * a.r.B * a.r.H;
+    const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
+    if (item >= items) return;  // uniform over the workgroup
+    const int64_t h = item % a.r.H, b = (item / a.r.H) % a.r.B, blk = (item / (a.r.H * a.r.B)) * 4 + w;
+    if (blk >= a.nblk) return;  // wave-uniform
+    kmean_block<D, NORM, ROPE, CONTIG, PERTOK>(a, b, h, blk, lc, r);
+}
+
+// Block sums are added in chunks of 16 consecutive blocks (ascending within a chunk),
+// the chunk sums in ascending order, then divided by T. k_kmean_chunks: one thread per
+// (b, h, chunk, channel), the chunk's loads in flight together; the sum replaces the
+// chunk's first block sum (only this thread reads that chunk's blocks of this channel).
+__global__ __launch_bounds__(256) void k_kmean_chunks(KmeanArgs a) {
+    constexpr int CB = 16;
+    const int D = static_cast<int>(a.r.D), per = 256 / D;
     const int64_t nchunk = (a.nblk + CB - 1) / CB;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * per + threadIdx.x / D, bh = blockIdx.y;
+    const int c = threadIdx.x % D;
+    if (chunk >= nchunk) return;
+    float* part = a.partial + (bh * a.nblk + chunk * CB) * D + c;
+    const int nb = static_cast<int>(a.nblk - chunk * CB < CB ? a.nblk - chunk * CB : CB);
+    float v[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) v[j] = part[static_cast<int64_t>(j < nb ? j : 0) * D];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+        if (j < nb) s = s + v[j];
+    part[0] = s;
+}
+
+// One thread per (b, h, channel): the chunk sums in ascending order, 16 loads at a time.
+__global__ __launch_bounds__(256) void k_kmean_final(KmeanArgs a) {
+    constexpr int CB = 16, NL = 16;
+    const int64_t D = a.r.D, i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= a.r.B * a.r.H * D) return;
+    const int64_t bh = i / D, c = i % D, b = bh / a.r.H, h = bh % a.r.H;
+    const int64_t nchunk = (a.nblk + CB - 1) / CB;
+    const float* part = a.partial + bh * a.nblk * D + c;
     float tot = 0.0f;
-    for (int64_t g0 = 0; g0 < nchunk; g0 += CG) {
-        const int ng = static_cast<int>(nchunk - g0 < CG ? nchunk - g0 : CG);
-        for (int j = r; j < ng; j += rpw) {
-            const int64_t blk0 = (g0 + j) * CB, blk1 = blk0 + CB < a.nblk ? blk0 + CB : a.nblk;
-            float s = 0.0f;
-            for (int64_t blk = blk0; blk < blk1; ++blk) s = s + part[blk * D + c];
-            cs[j * D + c] = s;
-        }
-        __syncthreads();
-        if (tid < D)
-            for (int j = 0; j < ng; ++j) tot = tot + cs[j * D + c];
-        __syncthreads();
+    for (int64_t g = 0; g < nchunk; g += NL) {
+        float v[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) v[j] = part[(g + j < nchunk ? g + j : g) * CB * D];
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            if (g + j < nchunk) tot = tot + v[j];
     }
-    if (tid < D) a.mean[b * a.mb + h * a.mh + c] = tot / static_cast<float>(a.r.T);
+    a.mean[b * a.mb + h * a.mh + c] = tot / static_cast<float>(a.r.T);
 }
 
 // ---------------------------------------------------------------- A3: fused q/k quantization
-template <int D, int NORM, int ROPE, bool CONTIG>
+// The 32 rows of a wave (8 per lane at D = 128, 4 at D = 64): every load goes out first,
+// then each row is finished, centred and scaled (rows past T become 0) into v, and the
+// row |v| maxima join their groups' maxima in LDS.
+template <int D, int NORM, int ROPE, bool CONTIG, bool PERTOK>
+__device__ __forceinline__ void quant_rows(const QuantArgs& a, int64_t b, int64_t h, int64_t tile, int w, int lc,
+                                           int lr, uint32_t* amax_s, float (*v)[8]) {
+    constexpr int LPR = D / 8, RPI = kWave / LPR, IT = 32 / RPI;
+    float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0}, wsh[8];
+    if (a.mean) load_row_f32<D>(a.mean + b * a.mb + h * a.mh, lc, mu);
+    if constexpr (!PERTOK) load_shared_weights<D, NORM>(a.r, h, lc, wsh);
+    const GroupMap gmap(a.layout, a.block);
+    const RowBase base(a.r, b, tile * 128, h);
+    const uint32_t rlast = static_cast<uint32_t>(a.r.T - tile * 128 < 128 ? a.r.T - tile * 128 - 1 : 127);
+    uint32_t rr[IT];
+    int64_t wrow[IT] = {};
+#pragma unroll
+    for (int i = 0; i < IT; ++i) rr[i] = min(static_cast<uint32_t>(32 * w + RPI * i + lr), rlast);
+    if constexpr (PERTOK) load_wrows<IT>(a.r, base, rr, wrow);
+    RowRaw<NORM, ROPE, PERTOK> raw[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) row_fetch<D, NORM, ROPE, CONTIG, PERTOK>(a.r, base, rr[i], h, lc, wrow[i], raw[i]);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic
+    // rows past T are computed from a clamped row and never enter a group maximum or a store
+    float m[IT];
+#pragma unroll
+    for (int i0 = 0; i0 < IT; i0 += 4) {
+        rows4<D, NORM, ROPE, PERTOK>(a.r, raw + i0, wsh, lc, v + i0);
+#pragma unroll
+        for (int i = i0; i < i0 + 4; ++i) {
+            m[i] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                v[i][k] = (v[i][k] - mu[k]) * a.sm_scale;  // exact when there is no mean (0) or scale (1)
+                m[i] = fmaxf(m[i], fabsf(v[i][k]));
+            }
+            m[i] = row_max<LPR>(m[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int r = 32 * w + RPI * i + lr;
+        if (tile * 128 + r < a.r.T && lc == 0) atomicMax(&amax_s[gmap(r)], __float_as_uint(m[i]));
+    }
+}
+
+template <int D, int NORM, int ROPE, bool CONTIG, bool PERTOK>
 __global__ __launch_bounds__(256) void k_quant_qk(QuantArgs a) {
     constexpr int LPR = D / 8, RPI = kWave / LPR, IT = 32 / RPI;
     const int64_t ntile = (a.r.T + 127) / 128, items = ntile * a.r.B * a.r.H;
@@ -250,50 +449,38 @@ __global__ __launch_bounds__(256) void k_quant_qk(QuantArgs a) {
     const int64_t h = item % a.r.H, b = (item / a.r.H) % a.r.B, tile = item / (a.r.H * a.r.B);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lc = lane % LPR, lr = lane / LPR;
     __shared__ uint32_t amax_s[32];
-    __shared__ float scale_s[32];
+    __shared__ float2 scale_s[32];  // (scale, 1 / scale) of the tile's groups
+    __shared__ int slow_s;          // a group whose scale is 0 or whose reciprocal overflows
     if (tid < 32) amax_s[tid] = 0u;
+    if (tid == 0) slow_s = 0;
     __syncthreads();
-    const int layout = a.layout, block = a.block;
-    const bool has_mean = a.mean != nullptr, has_scale = a.sm_scale != 1.0f;
-    float mu[8];
-    if (has_mean) load_row_f32<D>(a.mean + b * a.mb + h * a.mh, lc, mu);
     float v[IT][8];
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-        const int r = 32 * w + RPI * i + lr;
-        const int64_t t = tile * 128 + r;
-        const bool valid = t < a.r.T;
-        row_prologue<D, NORM, ROPE, CONTIG>(a.r, b, t, h, lc, valid, v[i]);
-        float m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            float z = v[i][k];
-            if (has_mean) z = z - mu[k];
-            if (has_scale) z = z * a.sm_scale;
-            v[i][k] = valid ? z : 0.0f;
-            m = fmaxf(m, fabsf(v[i][k]));
-        }
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
-        if (valid && lc == 0) atomicMax(&amax_s[local_group(r, layout, block)], __float_as_uint(m));
-    }
+    const int layout = a.layout, block = a.block;
+    quant_rows<D, NORM, ROPE, CONTIG, PERTOK>(a, b, h, tile, w, lc, lr, amax_s, v);
     __syncthreads();
     const int ng = groups_per_tile(layout, block);
+    const GroupMap gmap(layout, block);
     if (tid < ng) {
         const float sc = __uint_as_float(amax_s[tid]) / 127.0f + a.scale_eps;
-        scale_s[tid] = sc;
+        const float y = 1.0f / sc;
+        scale_s[tid] = make_float2(sc, y);
+        if (!(sc > 0.0f && y < __builtin_inff())) slow_s = 1;
         const int64_t gi = tile * ng + tid;
         if (gi < a.nscale) a.scales[b * a.ssb + h * a.ssh + gi] = sc;
     }
     __syncthreads();
+    const bool fast = slow_s == 0;
+    float2 sy[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) sy[i] = scale_s[gmap(32 * w + RPI * i + lr)];
+    int8_t* dst0 = a.codes + b * a.ob + tile * 128 * a.ot + h * a.oh + 4 * lc;
+    const uint32_t ot = static_cast<uint32_t>(a.ot);
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int r = 32 * w + RPI * i + lr;
-        const int64_t t = tile * 128 + r;
-        const float s = scale_s[local_group(r, layout, block)];
-        const float y = 1.0f / s;
+        const float s = sy[i].x, y = sy[i].y;
         float q[8];
-        if (__builtin_expect(__all(s > 0.0f && y < __builtin_inff()), 1)) {
+        if (__builtin_expect(fast, 1)) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) q[k] = div_rn(v[i][k], s, y);
         } else {
@@ -308,10 +495,10 @@ __global__ __launch_bounds__(256) void k_quant_qk(QuantArgs a) {
             const int c = static_cast<int>(q[k] + copysignf(0.5f, q[k]));
             word[k >> 2] |= (static_cast<uint32_t>(c) & 0xffu) << (8 * (k & 3));
         }
-        if (t < a.r.T) {
-            int8_t* dst = a.codes + b * a.ob + t * a.ot + h * a.oh;
-            *reinterpret_cast<uint32_t*>(dst + 4 * lc) = word[0];
-            *reinterpret_cast<uint32_t*>(dst + D / 2 + 4 * lc) = word[1];
+        if (tile * 128 + r < a.r.T) {
+            int8_t* dst = dst0 + __umul24(static_cast<uint32_t>(r), ot);
+            *reinterpret_cast<uint32_t*>(dst) = word[0];
+            *reinterpret_cast<uint32_t*>(dst + D / 2) = word[1];
         }
     }
 }
@@ -405,10 +592,17 @@ inline int check_launch(const char* what) {
     return SQ_OK;
 }
 
+template <int D, int NORM, int ROPE, bool PERTOK>
+void launch_quant_w(const QuantArgs& a, dim3 grid, hipStream_t s) {
+    if (a.r.rope_contig) hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, true, PERTOK>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, false, PERTOK>), grid, dim3(256), 0, s, a);
+}
+
+// per-token weight rows only matter with a norm
 template <int D, int NORM, int ROPE>
 void launch_quant_c(const QuantArgs& a, dim3 grid, hipStream_t s) {
-    if (a.r.rope_contig) hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, false>), grid, dim3(256), 0, s, a);
+    if (NORM != SQ_NORM_NONE && a.r.wrows) launch_quant_w<D, NORM, ROPE, NORM != SQ_NORM_NONE>(a, grid, s);
+    else launch_quant_w<D, NORM, ROPE, false>(a, grid, s);
 }
 
 template <int D, int NORM>
@@ -429,10 +623,16 @@ void launch_quant_d(const QuantArgs& a, dim3 grid, hipStream_t s) {
     }
 }
 
+template <int D, int NORM, int ROPE, bool PERTOK>
+void launch_kmean_w(const KmeanArgs& a, dim3 grid, hipStream_t s) {
+    if (a.r.rope_contig) hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, true, PERTOK>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, false, PERTOK>), grid, dim3(256), 0, s, a);
+}
+
 template <int D, int NORM, int ROPE>
 void launch_kmean_c(const KmeanArgs& a, dim3 grid, hipStream_t s) {
-    if (a.r.rope_contig) hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, false>), grid, dim3(256), 0, s, a);
+    if (NORM != SQ_NORM_NONE && a.r.wrows) launch_kmean_w<D, NORM, ROPE, NORM != SQ_NORM_NONE>(a, grid, s);
+    else launch_kmean_w<D, NORM, ROPE, false>(a, grid, s);
 }
 
 template <int D, int NORM>
@@ -472,7 +672,12 @@ int launch_kmean(const KmeanArgs& a, void* stream) {
         if (a.r.D == 128) launch_kmean_d<128>(a, grid, S(stream));
         else launch_kmean_d<64>(a, grid, S(stream));
     }
-    hipLaunchKernelGGL(k_kmean_final, dim3(static_cast<unsigned>(a.r.B * a.r.H)), dim3(256), 0, S(stream), a);
+    const int64_t nchunk = (a.nblk + 15) / 16, per = 256 / a.r.D;
+    if (a.nblk > 0)
+        hipLaunchKernelGGL(k_kmean_chunks, dim3(static_cast<unsigned>((nchunk + per - 1) / per), static_cast<unsigned>(a.r.B * a.r.H)),
+                           dim3(256), 0, S(stream), a);
+    hipLaunchKernelGGL(k_kmean_final, dim3(static_cast<unsigned>((a.r.B * a.r.H * a.r.D + 255) / 256)), dim3(256), 0,
+                       S(stream), a);
     return check_launch("sq_kmean");
 }
 
