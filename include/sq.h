@@ -172,7 +172,10 @@ int sq_norm_stats(const sq_rows* x, float* mean_sq, int64_t msb, int64_t mst, vo
  * ascending i; the block's sum is (S0 + S1) + (S2 + S3); block sums added in chunks of
  * 16 consecutive blocks, ascending within a chunk, and the chunk sums added in
  * ascending order; divided by T), so the result is bit-reproducible. `norm` may be NULL
- * (no norm); `rope` may be NULL (no rotation). */
+ * (no norm); `rope` may be NULL (no rotation). The token strides of x (x->st * 2 bytes),
+ * of the rope table (rs * 4) and of mean_sq (mst * 4) must each be under 16 MiB
+ * (SQ_ERR_STRIDE otherwise); the same holds for sq_quant_qk, whose code token stride
+ * ot must also be under 16 MiB. */
 size_t sq_kmean_workspace_bytes(const sq_rows* k, const sq_norm* norm);
 int sq_kmean(const sq_rows* k, const sq_norm* norm, const sq_rope* rope, float* mean, int64_t mb, int64_t mh,
              void* ws, size_t ws_bytes, void* stream);
