@@ -297,21 +297,51 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     }
 }
 
-// Merge the segments of one (sequence, query head): weights 2^(M_s - max M).
+// Merge the segments of one (sequence, query head): weights 2^(M_s - max M). Thread c
+// owns channel c; the segments' maxima and weights are computed 128 at a time, one
+// segment per thread, and shared through LDS; each channel's weighted sum then reads
+// its partials 8 loads at a time.
 __global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
+    constexpr int SB = kD, NL = 8;
+    __shared__ float wl[2][SB];  // per segment of the pass: weight, exp-sum
+    __shared__ float red[kD / 64];
     const int c = threadIdx.x, hq = blockIdx.x, n = blockIdx.y;
     const int L = a.num_blocks > 0 ? min(a.lens[n], a.max_len) : 0;
     const int nseg = L > 0 ? (L + kSeg - 1) / kSeg : 0;
     const float* p = a.part + (static_cast<int64_t>(n) * a.Hq + hq) * a.segs * (kD + 2);
     float mg = -__builtin_inff();
-    for (int s = 0; s < nseg; ++s) mg = fmaxf(mg, p[s * (kD + 2) + kD]);
+    for (int s = c; s < nseg; s += SB) mg = fmaxf(mg, p[s * (kD + 2) + kD]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, shfl_xor(mg, off));
+    if ((c & 63) == 0) red[c >> 6] = mg;
+    __syncthreads();
+    mg = fmaxf(red[0], red[1]);
     float tot = 0.0f, o = 0.0f;
-    if (mg > -__builtin_inff()) {
-        for (int s = 0; s < nseg; ++s) {
-            const float ms = p[s * (kD + 2) + kD];
-            const float wgt = ms > -__builtin_inff() ? __builtin_amdgcn_exp2f(ms - mg) : 0.0f;
-            tot = __builtin_fmaf(wgt, p[s * (kD + 2) + kD + 1], tot);
-            o = __builtin_fmaf(wgt, p[s * (kD + 2) + c], o);
+    if (mg > -__builtin_inff()) {  // uniform over the workgroup
+        for (int s0 = 0; s0 < nseg; s0 += SB) {
+            const int s = s0 + c;
+            float wgt = 0.0f, ls = 0.0f;
+            if (s < nseg) {
+                const float ms = p[s * (kD + 2) + kD];
+                wgt = ms > -__builtin_inff() ? __builtin_amdgcn_exp2f(ms - mg) : 0.0f;
+                ls = p[s * (kD + 2) + kD + 1];
+            }
+            __syncthreads();  // the previous pass has finished reading wl
+            wl[0][c] = wgt;
+            wl[1][c] = ls;
+            __syncthreads();
+            const int ns = min(SB, nseg - s0);
+            for (int j0 = 0; j0 < ns; j0 += NL) {
+                float v[NL];
+#pragma unroll
+                for (int j = 0; j < NL; ++j) v[j] = p[(s0 + min(j0 + j, ns - 1)) * (kD + 2) + c];
+#pragma unroll
+                for (int j = 0; j < NL; ++j)
+                    if (j0 + j < ns) {
+                        tot = __builtin_fmaf(wl[0][j0 + j], wl[1][j0 + j], tot);
+                        o = __builtin_fmaf(wl[0][j0 + j], v[j], o);
+                    }
+            }
         }
     }
     a.out[static_cast<int64_t>(n) * a.on + static_cast<int64_t>(hq) * a.oh + c] = tot > 0.0f ? o / tot : 0.0f;
