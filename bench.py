@@ -242,7 +242,10 @@ def run_quantizer(args, torch, sq, gen, timer):
         "config": {"workload": "quantizer B=2 T=75600 H=40 d=128: k mean + q PER_BLOCK(128), THREAD_Q, WARP_Q + "
                                "k PER_BLOCK(64), THREAD_K", "B": c.B, "T": c.T, "H": c.H, "head_dim": c.D},
         "roofline": {"bound": "hbm", "kernel": "k_quant_qk", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": q_ms,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_for("k_quant_qk_quantizer", ["quant.hip", "device.h", "sq_internal.h"],
+                                            float(bytes_[qn])),
+                     "avg_launch_ms": q_ms,
                      "bytes_per_launch": bytes_[qn]},
         "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
         "stages_gbs": {n: b / (timer.avg_ms(n) * 1e-3) / 1e9 for n, b in bytes_.items()},
@@ -281,7 +284,9 @@ def run_decode(args, torch, sq, gen, timer):
                                "q8 cache", "num_seqs": c.N, "Hq": c.Hq, "Hk": c.Hk, "head_dim": c.D,
                    "sum_len": int(lens.sum())},
         "roofline": {"bound": "hbm", "kernel": "k_decode_split+k_decode_reduce", "achieved": achieved,
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_for("k_decode_split_decode", ["decode.hip", "device.h", "sq_internal.h"],
+                                            float(nbytes)),
                      "avg_launch_ms": d_ms, "bytes_per_launch": nbytes},
     }
     return res, line
