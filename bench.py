@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video", choices=["video", "joint", "quantizer", "decode", "copy"],
+    ap.add_argument("--workload", default="video",
+                    choices=["video", "joint", "quantizer", "decode", "cachewrite", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
@@ -292,6 +293,46 @@ def run_decode(args, torch, sq, gen, timer):
     return res, line
 
 
+def run_cachewrite(args, torch, sq, gen, timer):
+    """q8 paged-cache writer: a 131072-token prefill chunk of new K/V rows (Hk 8, d 128, bf16; 537 MB read, more
+    than the 256 MiB MALL, so the rows come from HBM) quantized and scattered to a random permutation of the slots of
+    an 8192-block cache (block 16)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    n, Hk, D, NB, bs = 131072, 8, 128, 8192, 16
+    g = gen.rng(2500, 0)
+    k = torch.from_numpy(gen.to_bf16_bits(g.standard_normal((n, Hk, D), dtype=np.float32)).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    v = torch.from_numpy(gen.to_bf16_bits(g.standard_normal((n, Hk, D), dtype=np.float32)).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    slots = torch.from_numpy(g.permutation(NB * bs)[:n].astype(np.int64)).to(dev)
+    kc = torch.zeros((NB, bs, Hk, D), dtype=torch.int8, device=dev)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((NB, bs, Hk, D // 32), dtype=torch.float16, device=dev)
+    vs = torch.zeros_like(ks)
+
+    def step():
+        timer("cachewrite", lambda: sq.sq_q8_cache_write(k, v, slots, kc, ks, vc, vs))
+
+    nbytes = 2 * n * Hk * D * 2 + n * 8 + 2 * n * Hk * D + 2 * n * Hk * (D // 32) * 2
+    res = time_steps(args, torch, step, timer)
+    ms = timer.avg_ms("cachewrite")
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "q8 paged-cache writer GB/s (algorithmic bytes) and % of HBM peak",
+        "value": nbytes / (res["ms"] * 1e-3) / 1e9, "unit": "GB/s", "dtype": "bf16->i8",
+        "config": {"workload": "q8 cache write: 131072 new tokens, Hk 8, d 128, bf16 rows, random slots of an "
+                               "8192 x 16 block cache", "n_tokens": n, "Hk": Hk, "head_dim": D},
+        "roofline": {"bound": "hbm", "kernel": "k_q8_cache_write", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_for("k_q8_cache_write_cachewrite", ["cache.hip", "device.h", "sq_internal.h"],
+                                            float(nbytes)),
+                     "avg_launch_ms": ms,
+                     "bytes_per_launch": nbytes},
+    }
+    return res, line
+
+
 def run_copy(args, torch, sq, gen, timer):
     """A plain device-to-device copy of 1 GiB: the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE."""
     dev = torch.device("cuda:0")
@@ -365,7 +406,8 @@ def main():
         sys.exit("bench.py needs a GPU")
     sq.lib()
     timer = Timer(torch)
-    runners = {"video": run_video, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode, "copy": run_copy}
+    runners = {"video": run_video, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode,
+               "cachewrite": run_cachewrite, "copy": run_copy}
     if args.workload not in runners:
         sys.exit("workload %s is not benchmarked yet" % args.workload)
     print("bench: workload %s, warmup %d, steps %d" % (args.workload, args.warmup, args.steps), file=sys.stderr,

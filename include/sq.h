@@ -256,6 +256,24 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
                     int max_seq_len, int Hq, int D, float softmax_scale, float* out, int64_t on, int64_t oh,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* ---- D2. q8 paged-cache writer [kit] quantize_q8 (per token, head and group of 32
+ * channels: scale = max(amax / 127, 1e-8) in FP32, code = x / scale (correctly
+ * rounded FP32 division) rounded half to even and clamped to [-127, 127], the scale
+ * stored as FP16 (round to nearest even)) and [impl] _store_kvcache_nhd (token t goes
+ * to slot s = slot_mapping[t]: cache block s / block_size, row s % block_size; s < 0
+ * skips the token). New rows k, v (n_tokens, Hk, D) of bf16 or FP32 (dtype): element
+ * (t, h, c) at k[t*kn + h*kh + c], v likewise with vn, vh; inputs finite. Caches and
+ * scales in the layout sq_paged_decode reads: [num_blocks, block_size, Hk, D] int8 and
+ * [num_blocks, block_size, Hk, D/32] FP16, contiguous. A slot at or past
+ * num_blocks * block_size is skipped as well, so a bad mapping cannot write outside
+ * the caches; two tokens mapped to one slot race (either row may land). D 64 or 128;
+ * k and v rows 16-byte aligned (strides in elements); caches 16-byte aligned, scales
+ * 2-byte aligned. No workspace; only enqueues on `stream`. */
+int sq_q8_cache_write(const void* k, const void* v, sq_dtype dtype, int64_t n_tokens, int Hk, int D, int64_t kn,
+                      int64_t kh, int64_t vn, int64_t vh, const int64_t* slot_mapping, int8_t* k_cache,
+                      uint16_t* k_scale, int8_t* v_cache, uint16_t* v_scale, int64_t num_blocks, int block_size,
+                      void* stream);
+
 const char* sq_status_string(int status);
 const char* sq_last_error(void);
 int sq_abi_version(void);

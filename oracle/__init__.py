@@ -297,6 +297,23 @@ def q8_quantize(x: np.ndarray):
     return codes, scales
 
 
+def q8_cache_write(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale):
+    """[kit] quantize_q8 of each new row, then [impl] _store_kvcache_nhd: token t's rows (Hk, D) go to cache block
+    slot // block_size, row slot % block_size of k_cache / v_cache [NB, bs, Hk, D] (codes) and k_scale / v_scale
+    [NB, bs, Hk, D/32] (FP16 bits); a negative slot skips the token (as does one past NB * bs). k, v (n, Hk, D) FP32
+    (bf16 inputs widened exactly). Updates the four cache arrays in place, tokens in order."""
+    NB, bs = k_cache.shape[0], k_cache.shape[1]
+    kc, ksc = q8_quantize(k)
+    vc, vsc = q8_quantize(v)
+    for t, s in enumerate(np.asarray(slot_mapping, np.int64)):
+        if s < 0 or s >= NB * bs:
+            continue
+        k_cache[s // bs, s % bs] = kc[t]
+        k_scale[s // bs, s % bs] = ksc[t]
+        v_cache[s // bs, s % bs] = vc[t]
+        v_scale[s // bs, s % bs] = vsc[t]
+
+
 def paged_decode(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, scale):
     """Binary64 paged decode over a q8 cache: out (N, Hq, D)."""
     q = _c(q, np.uint16)

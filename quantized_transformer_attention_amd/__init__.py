@@ -72,7 +72,7 @@ _lib = None
 EXPORTS = ["sq_scale_count", "sq_norm_stats", "sq_kmean_workspace_bytes", "sq_kmean", "sq_quant_qk_workspace_bytes",
            "sq_quant_qk", "sq_quant_v_fp8_workspace_bytes", "sq_quant_v_fp8", "sq_attn_workspace_bytes", "sq_attn",
            "sq_attn_prefix_lse_merge_workspace_bytes", "sq_attn_prefix_lse_merge", "sq_paged_decode_workspace_bytes",
-           "sq_paged_decode", "sq_status_string", "sq_last_error", "sq_abi_version"]
+           "sq_paged_decode", "sq_q8_cache_write", "sq_status_string", "sq_last_error", "sq_abi_version"]
 
 
 def lib():
@@ -106,6 +106,8 @@ def lib():
         L.sq_paged_decode_workspace_bytes.restype = _sz
         L.sq_paged_decode.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
                                       _int, _int, _int, _f32, _vp, _i64, _i64, _vp, _sz, _vp]
+        L.sq_q8_cache_write.argtypes = [_vp, _vp, _int, _i64, _int, _int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                        _vp, _i64, _int, _vp]
         L.sq_status_string.argtypes, L.sq_status_string.restype = [_int], ctypes.c_char_p
         L.sq_last_error.argtypes, L.sq_last_error.restype = [], ctypes.c_char_p
         L.sq_abi_version.restype = _int
@@ -356,3 +358,25 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
                              max_seq_len, Hq, D, softmax_scale, _ptr(out), out.stride(0), out.stride(1), _ptr(ws), nb,
                              _stream(dev)))
     return out
+
+
+def sq_q8_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                      k_scale: torch.Tensor, v_cache: torch.Tensor, v_scale: torch.Tensor) -> None:
+    """Quantize new rows k, v (n_tokens, Hk, D), bf16 or FP32, to q8 and write them into the paged caches
+    (int8 [NB, bs, Hk, D], FP16 scales [NB, bs, Hk, D/32]) at the slots slot_mapping (int64 (n_tokens,));
+    negative slots are skipped."""
+    n, Hk, D = k.shape
+    NB, bs = k_cache.shape[0], k_cache.shape[1]
+    if k.dtype != v.dtype or k.shape != v.shape:
+        raise ValueError("k and v must have one shape and dtype")
+    dt = {torch.bfloat16: SQ_BF16, torch.float32: SQ_F32}.get(k.dtype)
+    if dt is None:
+        raise ValueError("k and v must be bf16 or float32")
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    if k.stride(2) != 1 or v.stride(2) != 1:
+        raise ValueError("k and v need contiguous channels")
+    L = lib()
+    _check(L.sq_q8_cache_write(_ptr(k), _ptr(v), dt, n, Hk, D, k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                               _ptr(slot_mapping), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), NB, bs,
+                               _stream(k.device)))

@@ -332,6 +332,37 @@ int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const fl
     return launch_prefix(a, stream);
 }
 
+// ---------------------------------------------------------------------------- D2. q8 paged-cache writer
+int sq_q8_cache_write(const void* k, const void* v, sq_dtype dtype, int64_t n_tokens, int Hk, int D, int64_t kn,
+                      int64_t kh, int64_t vn, int64_t vh, const int64_t* slot_mapping, int8_t* k_cache,
+                      uint16_t* k_scale, int8_t* v_cache, uint16_t* v_scale, int64_t num_blocks, int block_size,
+                      void* stream) {
+    clear_error();
+    const char* what = "sq_q8_cache_write";
+    if (dtype != SQ_BF16 && dtype != SQ_F32) return fail(SQ_ERR_UNSUPPORTED, "%s: rows must be bf16 or FP32", what);
+    if (D != 64 && D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d is not 64 or 128", what, D);
+    if (n_tokens < 0 || Hk < 1 || num_blocks < 0 || block_size < 1)
+        return fail(SQ_ERR_SHAPE, "%s: n_tokens >= 0, Hk >= 1, num_blocks >= 0 and block_size >= 1 are required", what);
+    if (n_tokens == 0) return SQ_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !k_scale || !v_cache || !v_scale)
+        return fail(SQ_ERR_NULL, "%s: a row, slot-mapping, cache or scale pointer is NULL", what);
+    if (kn < 0 || kh < 0 || vn < 0 || vh < 0) return fail(SQ_ERR_STRIDE, "%s: negative stride", what);
+    const int64_t per16 = dtype == SQ_BF16 ? 8 : 4;   // elements per 16 bytes
+    if ((reinterpret_cast<uintptr_t>(k) & 15) || (reinterpret_cast<uintptr_t>(v) & 15) || kn % per16 || kh % per16 ||
+        vn % per16 || vh % per16)
+        return fail(SQ_ERR_ALIGN, "%s: k and v rows must start on 16-byte boundaries", what);
+    if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15) ||
+        (reinterpret_cast<uintptr_t>(k_scale) & 1) || (reinterpret_cast<uintptr_t>(v_scale) & 1))
+        return fail(SQ_ERR_ALIGN, "%s: caches must be 16-byte and scales 2-byte aligned", what);
+    CacheWriteArgs a{};
+    a.k = k; a.v = v; a.n = n_tokens; a.Hk = Hk; a.D = D;
+    a.kn = kn; a.kh = kh; a.vn = vn; a.vh = vh;
+    a.slots = slot_mapping;
+    a.kc = k_cache; a.ks = k_scale; a.vc = v_cache; a.vs = v_scale;
+    a.nslots = num_blocks * block_size;
+    return launch_cache_write(a, dtype == SQ_F32, stream);
+}
+
 // ---------------------------------------------------------------------------- D. paged GQA decode
 size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_len) {
     if (num_seqs <= 0 || Hq <= 0 || D <= 0 || max_seq_len <= 0) return 0;

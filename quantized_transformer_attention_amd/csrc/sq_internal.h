@@ -129,6 +129,20 @@ struct PrefixArgs {
 // Positions per split-KV segment of the paged decode (one workgroup each).
 constexpr int kDecodeSeg = 256;
 
+struct CacheWriteArgs {
+    const void* k;
+    const void* v;
+    int64_t n;                  // tokens
+    int Hk, D;
+    int64_t kn, kh, vn, vh;     // element strides
+    const int64_t* slots;
+    int8_t* kc;
+    uint16_t* ks;
+    int8_t* vc;
+    uint16_t* vs;
+    int64_t nslots;             // num_blocks * block_size
+};
+
 struct DecodeArgs {
     const uint16_t* q;
     int64_t qn, qh;
@@ -157,6 +171,7 @@ int launch_quant_v_fp8(const QuantVArgs& a, void* stream);
 int launch_v_transpose(const VTransposeArgs& a, void* stream);
 int launch_attn(const AttnArgs& a, void* stream);
 int launch_prefix(const PrefixArgs& a, void* stream);
+int launch_cache_write(const CacheWriteArgs& a, bool f32, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
 
 // ---------------------------------------------------------------- validation (validate.cpp)

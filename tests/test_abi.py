@@ -107,3 +107,26 @@ def test_attn_validation_errors():
     v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 8, 0x5000, 0, 0)
     assert call(_qk(), _qk(), vv=v8, tile=128) == -3       # channel stride below the key count
     assert call(_qk(S=0), _qk()) == 0                      # no queries: no-op
+
+
+def _call_cache_write(dtype=0, n=4, Hk=2, D=128, k=0x1000, v=0x2000, kn=256, kh=128, slots=0x3000, kc=0x4000,
+                      ks=0x5000, vc=0x6000, vs=0x7000, NB=4, bs=16):
+    L = sq.lib()
+    return L.sq_q8_cache_write(k, v, dtype, n, Hk, D, kn, kh, kn, kh, slots, kc, ks, vc, vs, NB, bs, None)
+
+
+def test_cache_write_validation_errors():
+    assert _call_cache_write(dtype=sq.SQ_F16) == -5          # only bf16 and FP32 rows
+    assert _call_cache_write(D=96) == -5
+    assert _call_cache_write(Hk=0) == -2
+    assert _call_cache_write(bs=0) == -2
+    assert _call_cache_write(n=0, k=None) == 0               # nothing to write: no pointer is read
+    assert _call_cache_write(k=None) == -1
+    assert _call_cache_write(slots=None) == -1
+    assert _call_cache_write(kn=-256) == -3
+    assert _call_cache_write(k=0x1008) == -4                 # rows 16-byte aligned
+    assert _call_cache_write(kh=132) == -4                   # bf16 strides in multiples of 8 elements
+    assert _call_cache_write(dtype=sq.SQ_F32, kh=130) == -4  # FP32 strides in multiples of 4 elements
+    assert _call_cache_write(kc=0x4008) == -4                # caches 16-byte aligned
+    assert _call_cache_write(ks=0x5001) == -4                # scales 2-byte aligned
+    assert b"16-byte" in sq.lib().sq_last_error()

@@ -450,6 +450,34 @@ def test_q8_quantizer():
     assert c[0, :9].tolist() == [127, 0, 2, 2, 0, -2, -2, 10, 12]
 
 
+def test_q8_cache_writer_placement():
+    """[impl] _store_kvcache_nhd placement written out by hand for a tiny cache (block 4, 3 blocks): slot 5 is
+    block 1 row 1, slot 0 block 0 row 0, slot 11 block 2 row 3; slot -1 and slot 12 (past the cache) write nothing;
+    every other row keeps its fill. The rows placed are the q8 rows of the tokens ([kit] quantize_q8)."""
+    g = np.random.default_rng(43)
+    n, Hk, D, NB, bs = 5, 2, 64, 3, 4
+    k = g.standard_normal((n, Hk, D)).astype(np.float32)
+    v = g.standard_normal((n, Hk, D)).astype(np.float32)
+    slots = np.array([5, -1, 0, 11, 12], np.int64)
+    kc = np.full((NB, bs, Hk, D), 99, np.int8)
+    vc = np.full((NB, bs, Hk, D), -99, np.int8)
+    ks = np.full((NB, bs, Hk, D // 32), 0x1234, np.uint16)
+    vs = np.full((NB, bs, Hk, D // 32), 0x4321, np.uint16)
+    O.q8_cache_write(k, v, slots, kc, ks, vc, vs)
+    qk, qks = O.q8_quantize(k)
+    qv, qvs = O.q8_quantize(v)
+    placed = {(1, 1): 0, (0, 0): 2, (2, 3): 3}
+    for b in range(NB):
+        for r in range(bs):
+            if (b, r) in placed:
+                t = placed[(b, r)]
+                assert (kc[b, r] == qk[t]).all() and (vc[b, r] == qv[t]).all()
+                assert (ks[b, r] == qks[t]).all() and (vs[b, r] == qvs[t]).all()
+            else:
+                assert (kc[b, r] == 99).all() and (vc[b, r] == -99).all()
+                assert (ks[b, r] == 0x1234).all() and (vs[b, r] == 0x4321).all()
+
+
 # ----------------------------------------------------------------------------- paged decode
 def _paged_case(g, N=3, Hq=8, Hk=2, D=64, bs=16, lens=(1, 17, 40)):
     pages = [(L + bs - 1) // bs for L in lens]
