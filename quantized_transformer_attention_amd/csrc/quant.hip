@@ -509,17 +509,28 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* p, int64_t n, uint32
     if (i < n) p[i] = value;
 }
 
+// Per-channel |v| maxima of a 256-token chunk of one (b, h): every row load of a wave first
+// (rows past T read row T - 1, which leaves a maximum unchanged), the wave's row groups
+// reduced by shuffles, the 4 waves in LDS, then one atomic per channel and workgroup.
 template <int D>
 __global__ __launch_bounds__(256) void k_v_amax(QuantVArgs a) {
-    constexpr int LPR = D / 8, RPI = kWave / LPR;
+    constexpr int LPR = D / 8, RPI = kWave / LPR, IT = 64 / RPI;
+    __shared__ float red[4][D];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lc = lane % LPR, lr = lane / LPR;
     const int64_t chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const uint16_t* base = a.v + b * a.sb + h * a.sh + lc * 8;
+    uint4 raw[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        int64_t t = chunk * 256 + w * 64 + RPI * i + lr;
+        if (t >= a.T) t = a.T - 1;
+        raw[i] = *reinterpret_cast<const uint4*>(base + t * a.st);
+    }
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i = 0; i < 64 / RPI; ++i) {
-        const int64_t t = chunk * 256 + w * 64 + RPI * i + lr;
-        if (t >= a.T) break;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
         float x[8];
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.v + b * a.sb + t * a.st + h * a.sh + lc * 8), x);
+        unpack_bf16x8(raw[i], x);
 #pragma unroll
         for (int k = 0; k < 8; ++k) m[k] = fmaxf(m[k], fabsf(x[k]));
     }
@@ -528,9 +539,13 @@ __global__ __launch_bounds__(256) void k_v_amax(QuantVArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) m[k] = fmaxf(m[k], shfl_xor(m[k], off));
     if (lr == 0) {
-        uint32_t* dst = a.amax + (b * a.H + h) * D + lc * 8;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) atomicMax(dst + k, __float_as_uint(m[k]));
+        for (int k = 0; k < 8; ++k) red[w][lc * 8 + k] = m[k];
+    }
+    __syncthreads();
+    if (tid < D) {
+        const float mx = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+        atomicMax(a.amax + (b * a.H + h) * D + tid, __float_as_uint(mx));
     }
 }
 
@@ -552,23 +567,29 @@ __global__ __launch_bounds__(256) void k_v_fp8(QuantVArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) a.vs[b * a.vsb + h * a.vsh + lc * 8 + k] = vs[k];
     }
+    // every row load first (rows past T read row T - 1; their codes are then zeroed)
+    uint4 raw[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        int64_t t = tile * 128 + 32 * w + RPI * i + lr;
+        if (t >= a.T) t = a.T - 1;
+        raw[i] = *reinterpret_cast<const uint4*>(a.v + b * a.sb + t * a.st + h * a.sh + lc * 8);
+    }
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int r = 32 * w + RPI * i + lr;
-        const int64_t t = tile * 128 + r;
-        uint8_t code[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (t < a.T) {
-            float x[8];
-            unpack_bf16x8(*reinterpret_cast<const uint4*>(a.v + b * a.sb + t * a.st + h * a.sh + lc * 8), x);
+        const bool valid = tile * 128 + r < a.T;
+        uint8_t code[8];
+        float x[8];
+        unpack_bf16x8(raw[i], x);
 #pragma unroll
-            for (int k = 0; k < 8; k += 2) {
-                // the quotient keeps the sign of x (a -0 input gives the -0 code, 0x80)
-                float q0 = fminf(fmaxf(copysignf(div_rn(x[k], vs[k], y[k]), x[k]), -448.0f), 448.0f);
-                float q1 = fminf(fmaxf(copysignf(div_rn(x[k + 1], vs[k + 1], y[k + 1]), x[k + 1]), -448.0f), 448.0f);
-                const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-                code[k] = static_cast<uint8_t>(pk & 0xff);
-                code[k + 1] = static_cast<uint8_t>((pk >> 8) & 0xff);
-            }
+        for (int k = 0; k < 8; k += 2) {
+            // the quotient keeps the sign of x (a -0 input gives the -0 code, 0x80)
+            float q0 = fminf(fmaxf(copysignf(div_rn(x[k], vs[k], y[k]), x[k]), -448.0f), 448.0f);
+            float q1 = fminf(fmaxf(copysignf(div_rn(x[k + 1], vs[k + 1], y[k + 1]), x[k + 1]), -448.0f), 448.0f);
+            const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            code[k] = valid ? static_cast<uint8_t>(pk & 0xff) : 0;
+            code[k + 1] = valid ? static_cast<uint8_t>((pk >> 8) & 0xff) : 0;
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) tileT[(lc * 8 + k) * LDS_STRIDE + r] = code[k];
