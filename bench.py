@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video",
-                    choices=["video", "joint", "quantizer", "decode", "cachewrite", "copy"],
+                    choices=["video", "joint", "quantizer", "decode", "cachewrite", "merge", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
@@ -333,6 +333,36 @@ def run_cachewrite(args, torch, sq, gen, timer):
     return res, line
 
 
+def run_merge(args, torch, sq, gen, timer):
+    """Log-sum-exp merge of two attention outputs of the video shape (B=1, Sq=32760, H=40, d=128, FP32: 671 MB
+    each, beyond the 256 MiB MALL), as a native cached prefix's second pass is merged."""
+    dev = torch.device("cuda:0")
+    B, S, H, D = 1, 32760, 40, 128
+    gt = torch.Generator(device=dev)
+    gt.manual_seed(2700)
+    out = torch.randn((B, S, H, D), generator=gt, device=dev)
+    other = torch.randn((B, S, H, D), generator=gt, device=dev)
+    lse = torch.randn((B, H, S), generator=gt, device=dev) * 8
+    olse = torch.randn((B, H, S), generator=gt, device=dev) * 8
+
+    def step():
+        timer("merge", lambda: sq.sq_lse_merge(out, lse, other, olse))
+
+    nbytes = 3 * B * S * H * D * 4 + 3 * B * H * S * 4
+    res = time_steps(args, torch, step, timer)
+    ms = timer.avg_ms("merge")
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "log-sum-exp merge GB/s (algorithmic bytes) and % of HBM peak",
+        "value": nbytes / (res["ms"] * 1e-3) / 1e9, "unit": "GB/s", "dtype": "f32",
+        "config": {"workload": "merge of two attention outputs B=1 Sq=32760 H=40 d=128 FP32", "B": B, "Sq": S, "H": H,
+                   "head_dim": D},
+        "roofline": {"bound": "hbm", "kernel": "k_lse_merge", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": ms, "bytes_per_launch": nbytes},
+    }
+    return res, line
+
+
 def run_copy(args, torch, sq, gen, timer):
     """A plain device-to-device copy of 1 GiB: the known-size kernel that calibrates FETCH_SIZE / WRITE_SIZE."""
     dev = torch.device("cuda:0")
@@ -407,7 +437,7 @@ def main():
     sq.lib()
     timer = Timer(torch)
     runners = {"video": run_video, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode,
-               "cachewrite": run_cachewrite, "copy": run_copy}
+               "cachewrite": run_cachewrite, "merge": run_merge, "copy": run_copy}
     if args.workload not in runners:
         sys.exit("workload %s is not benchmarked yet" % args.workload)
     print("bench: workload %s, warmup %d, steps %d" % (args.workload, args.warmup, args.steps), file=sys.stderr,

@@ -235,6 +235,21 @@ int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const fl
                              float score_scale, int kv_tile, float* out, int64_t ob, int64_t ot, int64_t oh,
                              float* lse, int64_t lb, int64_t lh, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- C2. Log-sum-exp merge of two attentions of the same queries over disjoint key
+ * sets [kit] _merge_lse_ (the merge of a native cached prefix's pass, _attend_with_prefix):
+ * per (b, i, h): top = max(a, b) of the two base-2 log-sum-exps; wa = 2^(a - top),
+ * wb = 2^(b - top); out = out * (wa / (wa + wb)) + other * (wb / (wa + wb)); lse = top +
+ * log2(wa + wb) (written so merges chain; the pages' merge leaves it as it was). Both
+ * -inf: out 0, lse -inf. out, other FP32 (B, S, H, D) at out[b*ob + i*ot + h*oh + c]
+ * (other likewise with pb, pt, ph); lse, other_lse FP32 (B, H, S) at lse[b*lb + h*lh + i]
+ * (other_lse with qb, qh): the layouts sq_attn writes. A native prefix: k mean of the
+ * prefix keys (sq_kmean), prefix keys quantized with it (sq_quant_qk), prefix values to
+ * FP8 (sq_quant_v_fp8), the projected keys quantized with the same mean, one sq_attn pass
+ * per key set, then this merge. D 64 or 128; out/other rows 16-byte aligned. */
+int sq_lse_merge(float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh, const float* other,
+                 int64_t pb, int64_t pt, int64_t ph, const float* other_lse, int64_t qb, int64_t qh, int64_t B, int64_t S,
+                 int64_t H, int64_t D, void* stream);
+
 /* ---- D. Paged GQA decode over a q8 cache [impl] _cache_seq, _sdpa_one,
  * _decode_torch; [tq] block-table addressing and split-KV segments. Sequence n of
  * length L = seq_lens[n] (1 <= L <= max_seq_len) has one query (bf16 (N, Hq, D) at

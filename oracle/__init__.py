@@ -297,6 +297,25 @@ def q8_quantize(x: np.ndarray):
     return codes, scales
 
 
+def lse_merge(out, lse, other, other_lse):
+    """[kit] _merge_lse_ in binary64: out (B, S, H, D) and lse (B, H, S) over one key set, other / other_lse over
+    a disjoint one; top = max of the base-2 log-sum-exps, weights 2^(lse - top) over their sum. Returns the merged
+    out and the merged lse = top + log2(sum of weights); both -inf gives out 0 and lse -inf."""
+    a = np.asarray(lse, np.float64)
+    b = np.asarray(other_lse, np.float64)
+    top = np.maximum(a, b)
+    live = top > -np.inf
+    ts = np.where(live, top, 0.0)
+    wa = np.where(live, np.exp2(a - ts), 0.0)
+    wb = np.where(live, np.exp2(b - ts), 0.0)
+    tot = wa + wb
+    fa = np.where(live, wa / np.where(live, tot, 1.0), 0.0).transpose(0, 2, 1)[..., None]
+    fb = np.where(live, wb / np.where(live, tot, 1.0), 0.0).transpose(0, 2, 1)[..., None]
+    o = np.asarray(out, np.float64) * fa + np.asarray(other, np.float64) * fb
+    l = np.where(live, ts + np.log2(np.where(live, tot, 1.0)), -np.inf)
+    return o, l
+
+
 def q8_cache_write(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale):
     """[kit] quantize_q8 of each new row, then [impl] _store_kvcache_nhd: token t's rows (Hk, D) go to cache block
     slot // block_size, row slot % block_size of k_cache / v_cache [NB, bs, Hk, D] (codes) and k_scale / v_scale

@@ -72,7 +72,7 @@ _lib = None
 EXPORTS = ["sq_scale_count", "sq_norm_stats", "sq_kmean_workspace_bytes", "sq_kmean", "sq_quant_qk_workspace_bytes",
            "sq_quant_qk", "sq_quant_v_fp8_workspace_bytes", "sq_quant_v_fp8", "sq_attn_workspace_bytes", "sq_attn",
            "sq_attn_prefix_lse_merge_workspace_bytes", "sq_attn_prefix_lse_merge", "sq_paged_decode_workspace_bytes",
-           "sq_paged_decode", "sq_q8_cache_write", "sq_status_string", "sq_last_error", "sq_abi_version"]
+           "sq_paged_decode", "sq_q8_cache_write", "sq_lse_merge", "sq_status_string", "sq_last_error", "sq_abi_version"]
 
 
 def lib():
@@ -106,6 +106,8 @@ def lib():
         L.sq_paged_decode_workspace_bytes.restype = _sz
         L.sq_paged_decode.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
                                       _int, _int, _int, _f32, _vp, _i64, _i64, _vp, _sz, _vp]
+        L.sq_lse_merge.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                   _i64, _i64, _i64, _vp]
         L.sq_q8_cache_write.argtypes = [_vp, _vp, _int, _i64, _int, _int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                                         _vp, _i64, _int, _vp]
         L.sq_status_string.argtypes, L.sq_status_string.restype = [_int], ctypes.c_char_p
@@ -380,3 +382,18 @@ def sq_q8_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tens
     _check(L.sq_q8_cache_write(_ptr(k), _ptr(v), dt, n, Hk, D, k.stride(0), k.stride(1), v.stride(0), v.stride(1),
                                _ptr(slot_mapping), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), NB, bs,
                                _stream(k.device)))
+
+
+def sq_lse_merge(out: torch.Tensor, lse: torch.Tensor, other: torch.Tensor, other_lse: torch.Tensor) -> None:
+    """In place: (out, lse) becomes the attention of the same queries over both key sets, from (out, lse) over one
+    and (other, other_lse) over the other. out, other FP32 (B, S, H, D); lse, other_lse FP32 (B, H, S), base 2."""
+    B, S, H, D = out.shape
+    for t in (out, lse, other, other_lse):
+        if t.dtype != torch.float32:
+            raise ValueError("sq_lse_merge takes FP32 tensors")
+    if out.stride(3) != 1 or other.stride(3) != 1 or lse.stride(2) != 1 or other_lse.stride(2) != 1:
+        raise ValueError("channels and tokens of the log-sum-exps must be contiguous")
+    L = lib()
+    _check(L.sq_lse_merge(_ptr(out), out.stride(0), out.stride(1), out.stride(2), _ptr(lse), lse.stride(0),
+                          lse.stride(1), _ptr(other), other.stride(0), other.stride(1), other.stride(2), _ptr(other_lse),
+                          other_lse.stride(0), other_lse.stride(1), B, S, H, D, _stream(out.device)))

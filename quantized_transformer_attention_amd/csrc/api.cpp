@@ -332,6 +332,25 @@ int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const fl
     return launch_prefix(a, stream);
 }
 
+// ---------------------------------------------------------------------------- C2. log-sum-exp merge
+int sq_lse_merge(float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh, const float* other,
+                 int64_t pb, int64_t pt, int64_t ph, const float* other_lse, int64_t qb, int64_t qh, int64_t B, int64_t S,
+                 int64_t H, int64_t D, void* stream) {
+    clear_error();
+    const char* what = "sq_lse_merge";
+    if (D != 64 && D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %lld is not 64 or 128", what, (long long)D);
+    if (B < 0 || S < 0 || H < 0) return fail(SQ_ERR_SHAPE, "%s: negative size", what);
+    if (B * S * H == 0) return SQ_OK;
+    if (!out || !lse || !other || !other_lse) return fail(SQ_ERR_NULL, "%s: an output or log-sum-exp pointer is NULL", what);
+    if (ob < 0 || ot < 0 || oh < 0 || lb < 0 || lh < 0 || pb < 0 || pt < 0 || ph < 0 || qb < 0 || qh < 0)
+        return fail(SQ_ERR_STRIDE, "%s: negative stride", what);
+    if ((reinterpret_cast<uintptr_t>(out) & 15) || (reinterpret_cast<uintptr_t>(other) & 15) || ob % 4 || ot % 4 ||
+        oh % 4 || pb % 4 || pt % 4 || ph % 4)
+        return fail(SQ_ERR_ALIGN, "%s: out and other rows must start on 16-byte boundaries", what);
+    MergeArgs a{out, ob, ot, oh, lse, lb, lh, other, pb, pt, ph, other_lse, qb, qh, B, S, H, D};
+    return launch_lse_merge(a, stream);
+}
+
 // ---------------------------------------------------------------------------- D2. q8 paged-cache writer
 int sq_q8_cache_write(const void* k, const void* v, sq_dtype dtype, int64_t n_tokens, int Hk, int D, int64_t kn,
                       int64_t kh, int64_t vn, int64_t vh, const int64_t* slot_mapping, int8_t* k_cache,

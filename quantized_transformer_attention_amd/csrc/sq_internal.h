@@ -129,6 +129,18 @@ struct PrefixArgs {
 // Positions per split-KV segment of the paged decode (one workgroup each).
 constexpr int kDecodeSeg = 256;
 
+struct MergeArgs {
+    float* out;
+    int64_t ob, ot, oh;
+    float* lse;
+    int64_t lb, lh;
+    const float* other;
+    int64_t pb, pt, ph;
+    const float* other_lse;
+    int64_t qb, qh;
+    int64_t B, S, H, D;
+};
+
 struct CacheWriteArgs {
     const void* k;
     const void* v;
@@ -171,6 +183,7 @@ int launch_quant_v_fp8(const QuantVArgs& a, void* stream);
 int launch_v_transpose(const VTransposeArgs& a, void* stream);
 int launch_attn(const AttnArgs& a, void* stream);
 int launch_prefix(const PrefixArgs& a, void* stream);
+int launch_lse_merge(const MergeArgs& a, void* stream);
 int launch_cache_write(const CacheWriteArgs& a, bool f32, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
 

@@ -130,3 +130,19 @@ def test_cache_write_validation_errors():
     assert _call_cache_write(kc=0x4008) == -4                # caches 16-byte aligned
     assert _call_cache_write(ks=0x5001) == -4                # scales 2-byte aligned
     assert b"16-byte" in sq.lib().sq_last_error()
+
+
+def _call_merge(out=0x1000, lse=0x2000, other=0x3000, olse=0x4000, D=128, ob=128 * 4 * 10, ot=128 * 4, oh=128,
+                lh=10, B=1, S=10, H=4):
+    L = sq.lib()
+    return L.sq_lse_merge(out, ob, ot, oh, lse, 4 * 10, lh, other, ob, ot, oh, olse, 4 * 10, lh, B, S, H, D, None)
+
+
+def test_lse_merge_validation_errors():
+    assert _call_merge(D=96) == -5
+    assert _call_merge(S=-1) == -2
+    assert _call_merge(S=0, out=None) == 0                  # nothing to merge
+    assert _call_merge(lse=None) == -1
+    assert _call_merge(lh=-1) == -3
+    assert _call_merge(out=0x1004) == -4                    # rows 16-byte aligned
+    assert _call_merge(oh=130) == -4

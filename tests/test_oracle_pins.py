@@ -450,6 +450,38 @@ def test_q8_quantizer():
     assert c[0, :9].tolist() == [127, 0, 2, 2, 0, -2, -2, 10, 12]
 
 
+def _textbook_attention(q, k, v):
+    """Binary64 softmax(q k^T) v per (b, h) with its base-2 log-sum-exp; q (B, S, H, D), k, v (B, T, H, D)."""
+    s = np.einsum("bshd,bthd->bhst", q, k) * np.log2(np.e)          # base-2 scores
+    m = s.max(-1, keepdims=True)
+    p = np.exp2(s - m)
+    l = p.sum(-1, keepdims=True)
+    out = np.einsum("bhst,bthd->bshd", p / l, v)
+    return out, (m + np.log2(l))[..., 0]
+
+
+def test_lse_merge_equals_attention_over_joined_keys():
+    """[kit] _merge_lse_: attention over key set A merged with attention over a disjoint set B equals attention
+    over A and B joined (binary64, to rounding); an empty side (lse -inf) leaves the other; both empty give 0."""
+    g = np.random.default_rng(44)
+    B, S, H, D = 2, 5, 3, 16
+    q = g.standard_normal((B, S, H, D)) * 0.4
+    ka, va = g.standard_normal((B, 7, H, D)), g.standard_normal((B, 7, H, D))
+    kb, vb = g.standard_normal((B, 11, H, D)) + 0.5, g.standard_normal((B, 11, H, D))
+    oa, la = _textbook_attention(q, ka, va)
+    ob, lb = _textbook_attention(q, kb, vb)
+    oj, lj = _textbook_attention(q, np.concatenate([ka, kb], 1), np.concatenate([va, vb], 1))
+    om, lm = O.lse_merge(oa, la, ob, lb)
+    np.testing.assert_allclose(om, oj, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lm, lj, rtol=0, atol=1e-12)
+    empty = np.full_like(lb, -np.inf)
+    om, lm = O.lse_merge(oa, la, ob * 0 + 123.0, empty)
+    np.testing.assert_array_equal(om, oa)
+    np.testing.assert_array_equal(lm, la)
+    om, lm = O.lse_merge(oa, empty, ob, empty)
+    assert (om == 0).all() and (lm == -np.inf).all()
+
+
 def test_q8_cache_writer_placement():
     """[impl] _store_kvcache_nhd placement written out by hand for a tiny cache (block 4, 3 blocks): slot 5 is
     block 1 row 1, slot 0 block 0 row 0, slot 11 block 2 row 3; slot -1 and slot 12 (past the cache) write nothing;
