@@ -81,11 +81,12 @@ def _declare(L):
     L.orc_scale_index.argtypes, L.orc_scale_index.restype = [_i64, _int, _int], _i64
     L.orc_quant_qk.argtypes = [P(_Rows), _int, _int, _f32, _vp, _vp]
     L.orc_quant_v_fp8.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _vp]
-    L.orc_attn.argtypes = [P(_QK), P(_QK), _vp, _int, _vp, _f32, _int, _f64, _vp, _i64, _vp, _vp, _vp]
+    L.orc_attn.argtypes = [P(_QK), P(_QK), _vp, _int, _vp, _f32, _int, _f64, _int, _vp, _vp, _i64, _vp, _vp, _vp]
     L.orc_prefix_merge.argtypes = [P(_QK), P(_Prefix), _vp, _f32, _int, _f64, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                    _vp, _vp]
     L.orc_q8_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp]
-    L.orc_paged_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _f64, _vp]
+    L.orc_paged_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _f64, _vp,
+                                   _vp]
     L.orc_attn_exact.argtypes = [P(_Rows), P(_Rows), _vp, P(_Prefix), _vp, _i64, _vp]
 
 
@@ -233,8 +234,9 @@ def _qk_struct(t: QK):
 
 
 def attn(q: QK, k: QK, v: np.ndarray, fp8: bool, vs=None, score_scale=1.0, kv_tile=64, rows=None,
-         flip_rel=2.0 ** -22, want_allow=True):
-    """Quantized-mode attention core: out (B, rows, H, D), lse (B, H, rows), allow."""
+         flip_rel=2.0 ** -22, want_allow=True, causal=False, sinks=None):
+    """Quantized-mode attention core: out (B, rows, H, D), lse (B, H, rows), allow. causal: query i attends keys
+    0 .. i + Sk - Sq; sinks: FP32 (H,) per-head sink logits ([tq] USE_SINKS) or None."""
     qs, kq = _qk_struct(q)
     ks, kk = _qk_struct(k)
     v = _c(v, np.uint8 if fp8 else np.uint16)
@@ -245,8 +247,9 @@ def attn(q: QK, k: QK, v: np.ndarray, fp8: bool, vs=None, score_scale=1.0, kv_ti
     out = np.empty((B, n, H, D), np.float64)
     lse = np.empty((B, H, n), np.float64)
     allow = np.empty((B, n, H, D), np.float64) if want_allow else None
+    sk_ = _c(sinks, np.float32) if sinks is not None else None
     lib().orc_attn(ctypes.byref(qs), ctypes.byref(ks), _p(v), int(fp8), _p(vs_), score_scale, kv_tile, flip_rel,
-                   _p(rows), n, _p(out), _p(lse), _p(allow))
+                   int(causal), _p(sk_), _p(rows), n, _p(out), _p(lse), _p(allow))
     return out, lse, allow
 
 
@@ -333,16 +336,17 @@ def q8_cache_write(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale):
         v_scale[s // bs, s % bs] = vsc[t]
 
 
-def paged_decode(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, scale):
-    """Binary64 paged decode over a q8 cache: out (N, Hq, D)."""
+def paged_decode(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, scale, sinks=None):
+    """Binary64 paged decode over a q8 cache: out (N, Hq, D). sinks: FP32 (Hq,) per-head sink logits or None."""
     q = _c(q, np.uint16)
     kc, ks, vc, vsc = _c(k_cache, np.int8), _c(k_scale, np.uint16), _c(v_cache, np.int8), _c(v_scale, np.uint16)
     bt, sl = _c(block_table, np.int32), _c(seq_lens, np.int32)
     N, Hq, D = q.shape
     bs, Hk = kc.shape[1], kc.shape[2]
     out = np.empty((N, Hq, D), np.float64)
+    sk_ = _c(sinks, np.float32) if sinks is not None else None
     lib().orc_paged_decode(_p(q), _p(kc), _p(ks), _p(vc), _p(vsc), bs, Hk, _p(bt), bt.shape[1], _p(sl), N, Hq, D,
-                           float(scale), _p(out))
+                           float(scale), _p(sk_), _p(out))
     return out
 
 

@@ -471,10 +471,12 @@ static double pt_flip(float p, int fp8, double flip_rel) {
 void orc_attn(const orc_qk* q, const orc_qk* k,
               const void* v, int fp8, const float* vs,
               float score_scale, int kv_tile, double flip_rel,
+              int causal, const float* sinks /* (H,) natural-log logits or NULL */,
               const int64_t* rows, int64_t nrows,
               double* out /* (B, nrows, H, D) */, double* lse /* (B, H, nrows) */,
               double* allow /* (B, nrows, H, D) or NULL */) {
     const int64_t B = q->B, H = q->H, D = q->D, Sk = k->S, Hk = k->H, G = H / Hk;
+    const int64_t off = Sk - q->S;   /* causal: query i sees keys 0 .. i + Sk - Sq */
     const int64_t nq = orc_scale_count(q->S, q->layout, q->block);
     const int64_t nk = orc_scale_count(Sk, k->layout, k->block);
 #pragma omp parallel for collapse(3) schedule(dynamic)
@@ -489,10 +491,13 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                 float* c = (float*)malloc(sizeof(float) * (size_t)kv_tile);
                 double* ptv = (double*)malloc(sizeof(double) * (size_t)kv_tile);
                 for (int64_t d = 0; d < D; ++d) acc[d] = al[d] = 0.0;
-                float m = -INFINITY;
-                double l = 0.0;
-                for (int64_t j0 = 0; j0 < Sk; j0 += kv_tile) {
-                    int64_t n = Sk - j0 < kv_tile ? Sk - j0 : kv_tile;
+                /* [tq] sinks: the softmax starts from M = the head's sink logit (base 2 here:
+                 * RN(s_h * log2 e) in FP32), L = 1, so the sink joins the denominator only */
+                float m = sinks ? sinks[h] * 1.44269504f : -INFINITY;
+                double l = sinks ? 1.0 : 0.0;
+                const int64_t kend = causal ? (i + off + 1 < Sk ? i + off + 1 : Sk) : Sk;
+                for (int64_t j0 = 0; j0 < kend; j0 += kv_tile) {
+                    int64_t n = kend - j0 < kv_tile ? kend - j0 : kv_tile;
                     float mt = -INFINITY;
                     for (int64_t jj = 0; jj < n; ++jj) {
                         int64_t j = j0 + jj;
@@ -683,7 +688,8 @@ void orc_q8_quantize(const float* x, int64_t rows, int64_t D, int8_t* codes, uin
 void orc_paged_decode(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
                       const int8_t* vc, const uint16_t* vsc, int64_t bs, int64_t Hk,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
-                      int64_t N, int64_t Hq, int64_t D, double scale, double* out) {
+                      int64_t N, int64_t Hq, int64_t D, double scale,
+                      const float* sinks /* (Hq,) natural-log logits or NULL */, double* out) {
     const int64_t G = Hq / Hk, NG = D / 32;
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int64_t n = 0; n < N; ++n)
@@ -701,6 +707,9 @@ void orc_paged_decode(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
                 s[pos] = dot * scale;
                 m = fmax(m, s[pos]);
             }
+            /* [tq] sinks: exp(s_h) joins the denominator only */
+            if (sinks) m = fmax(m, (double)sinks[h]);
+            if (sinks) l = exp((double)sinks[h] - m);
             for (int64_t pos = 0; pos < L; ++pos) {
                 int64_t phys = block_table[n * bt_stride + pos / bs], slot = pos % bs;
                 int64_t base = (phys * bs + slot) * Hk + hk;

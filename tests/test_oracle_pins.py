@@ -627,3 +627,81 @@ def test_quantized_pipeline_tracks_exact_attention_tiny():
     ref = O.attn_exact(inp.q, pq, inp.k, pk, inp.v)
     cos = (out * ref).sum() / np.sqrt((out ** 2).sum() * (ref ** 2).sum())
     assert cos > 0.999, cos
+
+
+# ----------------------------------------------------------------------------- causal mask and sinks
+def _core_inputs(g, B=1, Sq=70, Sk=200, H=2, D=64, fp8=True):
+    qc = g.integers(-127, 128, size=(B, Sq, H, D)).astype(np.int8)
+    kc = g.integers(-127, 128, size=(B, Sk, H, D)).astype(np.int8)
+    qs = g.uniform(1e-3, 4e-3, size=(B, H, O.scale_count(Sq, 0, 64))).astype(np.float32)
+    ks = g.uniform(1e-3, 4e-3, size=(B, H, O.scale_count(Sk, 2, 64))).astype(np.float32)
+    if fp8:
+        v = (g.integers(0, 0x7f, size=(B, Sk, H, D)) | (g.integers(0, 2, size=(B, Sk, H, D)) << 7)).astype(np.uint8)
+        vs = np.full((B, H, D), 0.01, np.float32)
+    else:
+        v, vs = gen.normal_bf16((B, Sk, H, D), g), None
+    return qc, qs, kc, ks, v, vs
+
+
+def test_causal_row_equals_attention_over_its_visible_keys():
+    """[tq] causal rows (query i at position context + i sees keys 0 .. context + i, context = Sk - Sq): each causal
+    row equals the non-causal core run over those keys alone (same tiles from key 0), bit for bit."""
+    g = np.random.default_rng(61)
+    for fp8 in (True, False):
+        qc, qs, kc, ks, v, vs = _core_inputs(g, fp8=fp8)
+        Sq, Sk = qc.shape[1], kc.shape[1]
+        kv_tile = 128 if fp8 else 64
+        q = O.QK(qc, qs, 0, 64)
+        out, lse, allow = O.attn(q, O.QK(kc, ks, 2, 64), v, fp8, vs, kv_tile=kv_tile, causal=True)
+        for i in (0, 1, 37, Sq - 1):
+            kend = i + Sk - Sq + 1
+            nk = O.scale_count(kend, 2, 64)
+            kt = O.QK(np.ascontiguousarray(kc[:, :kend]), np.ascontiguousarray(ks[:, :, :nk]), 2, 64)
+            o1, l1, a1 = O.attn(q, kt, np.ascontiguousarray(v[:, :kend]), fp8, vs, kv_tile=kv_tile,
+                                rows=np.array([i], np.int64))
+            np.testing.assert_array_equal(out[:, i], o1[:, 0])
+            np.testing.assert_array_equal(lse[:, :, i], l1[:, :, 0])
+            np.testing.assert_array_equal(allow[:, i], a1[:, 0])
+
+
+def test_sinks_join_the_denominator_only():
+    """[tq] USE_SINKS: out = sum exp(s_i) v_i / (exp(s_h) + sum exp(s_i)). A sink of -inf changes nothing; the
+    log-sum-exp with a sink is log2(2^lse + 2^(s_h log2 e)); out shrinks by 2^lse / (2^lse + 2^(s_h log2 e)) up
+    to the P rounding (bf16: relative 2^-8)."""
+    g = np.random.default_rng(62)
+    qc, qs, kc, ks, v, vs = _core_inputs(g, fp8=False)
+    q, k = O.QK(qc, qs, 0, 64), O.QK(kc, ks, 2, 64)
+    out, lse, _ = O.attn(q, k, v, False, None, kv_tile=64)
+    o2, l2, _ = O.attn(q, k, v, False, None, kv_tile=64, sinks=np.full(2, -np.inf, np.float32))
+    np.testing.assert_array_equal(out, o2)
+    np.testing.assert_array_equal(lse, l2)
+    sinks = np.array([float(lse.mean()) * np.log(2.0), float(lse.max()) * np.log(2.0) + 1.0], np.float32)
+    o3, l3, _ = O.attn(q, k, v, False, None, kv_tile=64, sinks=sinks)
+    sb = (sinks.astype(np.float32) * np.float32(1.44269504)).astype(np.float64)[None, :, None]
+    np.testing.assert_allclose(l3, np.log2(np.exp2(lse) + np.exp2(sb)), rtol=0, atol=2e-6)
+    f = (np.exp2(lse) / (np.exp2(lse) + np.exp2(sb))).transpose(0, 2, 1)[..., None]
+    assert np.abs(o3 - out * f).max() <= 2.0 ** -8 * np.abs(out).max()
+
+
+def test_paged_decode_sinks():
+    """Decode with per-head sinks against a softmax with the extra logit written out with numpy on the gathered
+    q8 values; a sink of -inf changes nothing."""
+    g = np.random.default_rng(63)
+    q, kc, ks, vc, vs, bt, lens = _paged_case(g)
+    scale = 0.125
+    sinks = g.standard_normal(8).astype(np.float32) * 2
+    out = O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale, sinks=sinks)
+    assert np.array_equal(O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale, sinks=np.full(8, -np.inf, np.float32)),
+                          O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale))
+    f16 = lambda a: a.view(np.float16).astype(np.float64)
+    qf = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for n, L in enumerate(lens):
+        pages = bt[n, :(L + 15) // 16]
+        kv = (kc[pages].astype(np.float64) * np.repeat(f16(ks[pages]), 32, -1)).reshape(-1, 2, 64)[:L]
+        vv = (vc[pages].astype(np.float64) * np.repeat(f16(vs[pages]), 32, -1)).reshape(-1, 2, 64)[:L]
+        for h in range(8):
+            s = kv[:, h // 4] @ qf[n, h] * scale
+            m = max(s.max(), float(sinks[h]))
+            p = np.exp(s - m)
+            ref = p @ vv[:, h // 4] / (p.sum() + np.exp(float(sinks[h]) - m))
+            np.testing.assert_allclose(out[n, h], ref, rtol=1e-12, atol=1e-12)
