@@ -7,6 +7,7 @@ stage in the library's HIP kernels:
     Sq=Sk=32760, 1% outlier channels x20 -> all-heads mean squares of q and k, k mean,
     fused norm + RoPE + INT8 quantization of q (THREAD_Q) and k (THREAD_K, k mean
     subtracted), V to FP8 per channel, attention core with FP8 P.V;
+  causal: the video pipeline with a causal mask and per-head sinks in the core;
   joint: the video recipe's projected pass at H=24, 8704 tokens (PER_BLOCK q 128 / k 64,
     bf16 P.V) plus the 4096-token q8 prefix pass merged by log-sum-exp;
   quantizer: k mean + the five quantizer runs of a 2 x 75600 x 40 x 128 tensor;
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video",
-                    choices=["video", "joint", "quantizer", "decode", "cachewrite", "merge", "copy"],
+                    choices=["video", "causal", "joint", "quantizer", "decode", "cachewrite", "merge", "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
@@ -98,8 +99,8 @@ class Timer:
 
 
 # ---------------------------------------------------------------------------------------------- workloads
-def video_like(args, torch, sq, gen, c, timer):
-    """Build the video-style pipeline (also the joint workload's projected pass)."""
+def video_like(args, torch, sq, gen, c, timer, causal=False, sinks=None):
+    """Build the video-style pipeline (also the joint workload's projected pass and the causal variant)."""
     import numpy as np
 
     dev = torch.device("cuda:0")
@@ -134,9 +135,11 @@ def video_like(args, torch, sq, gen, c, timer):
         k = timer("quant_k", lambda: sq.sq_quant_qk(kd, nk, rope, mu, 1.0, 1e-7, kl, kb, workspace=wsp["k"]))
         if c.pv == "fp8":
             v8, vs = timer("quant_v", lambda: sq.sq_quant_v_fp8(vd, workspace=wsp["v"]))
-            out, lse = timer("attn", lambda: sq.sq_attn(q, k, v8, vs, 1.0, c.kv_tile, workspace=wsp["attn"]))
+            out, lse = timer("attn", lambda: sq.sq_attn(q, k, v8, vs, 1.0, c.kv_tile, workspace=wsp["attn"],
+                                                        causal=causal, sinks=sinks))
         else:
-            out, lse = timer("attn", lambda: sq.sq_attn(q, k, vd, None, 1.0, c.kv_tile, workspace=wsp["attn"]))
+            out, lse = timer("attn", lambda: sq.sq_attn(q, k, vd, None, 1.0, c.kv_tile, workspace=wsp["attn"],
+                                                        causal=causal, sinks=sinks))
         return q, mu, out, lse
 
     bytes_ = {
@@ -167,6 +170,34 @@ def run_video(args, torch, sq, gen, timer):
         "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
         "stages_gbs": {n: b / (timer.avg_ms(n) * 1e-3) / 1e9 for n, b in bytes_.items()},
         "core_pct_of_int8_peak": 100.0 * achieved / PEAK_TFLOPS_INT8,
+    }
+    return res, line
+
+
+def run_causal(args, torch, sq, gen, timer):
+    """The video pipeline with a causal mask and per-head sinks in the core: query i sees keys 0 .. i, so the
+    work is 4 B H d S (S + 1) / 2 (the visible query-key pairs)."""
+    import numpy as np
+
+    c = gen.CFG2
+    sinks = torch.from_numpy(gen.rng(c.seed, gen.S_EXTRA).uniform(-1.0, 2.0, size=c.H).astype(np.float32)).cuda()
+    step, bytes_ = video_like(args, torch, sq, gen, c, timer, causal=True, sinks=sinks)
+    flops = 4.0 * c.B * c.H * c.D * c.Sq * (c.Sq + 1) / 2
+    res = time_steps(args, torch, step, timer)
+    attn_ms = timer.avg_ms("attn")
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    files = ["attn.hip", "device.h", "sq_internal.h"]
+    line = {
+        "metric": "causal quantized-attention TFLOPS (4*B*H*d*S*(S+1)/2 visible pairs) and % of INT8 MFMA peak",
+        "value": flops / (res["ms"] * 1e-3) / 1e12, "unit": "TFLOPS", "dtype": "i8",
+        "config": {"workload": "causal self-attention with per-head sinks, B=1 H=40 Sq=Sk=32760 d=128, "
+                               "THREAD_Q/THREAD_K INT8, FP8 P.V", "B": c.B, "H": c.H, "Sq": c.Sq, "Sk": c.Sk,
+                   "head_dim": c.D, "kv_tile": c.kv_tile, "causal": True, "sinks": True},
+        "roofline": {"bound": "mfma", "kernel": "k_attn", "achieved": achieved, "peak": PEAK_TFLOPS_INT8,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS_INT8,
+                     "traffic": traffic_for("k_attn_causal", files, flops),
+                     "avg_launch_ms": attn_ms, "flops_per_launch": flops},
+        "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
     }
     return res, line
 
@@ -436,7 +467,7 @@ def main():
         sys.exit("bench.py needs a GPU")
     sq.lib()
     timer = Timer(torch)
-    runners = {"video": run_video, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode,
+    runners = {"video": run_video, "causal": run_causal, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode,
                "cachewrite": run_cachewrite, "merge": run_merge, "copy": run_copy}
     if args.workload not in runners:
         sys.exit("workload %s is not benchmarked yet" % args.workload)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SQ_ABI_VERSION 1
+#define SQ_ABI_VERSION 2
 
 enum {
     SQ_OK = 0,
@@ -205,8 +205,8 @@ size_t sq_quant_v_fp8_workspace_bytes(const sq_rows* v);
 int sq_quant_v_fp8(const sq_rows* v, uint8_t* codes, int64_t ob, int64_t oh, int64_t od, float* vs, int64_t vsb,
                    int64_t vsh, void* ws, size_t ws_bytes, void* stream);
 
-/* ---- B. Quantized attention core (non-causal; kv head of q head h is
- * h / (H / Hk) [impl] _repeat_kv_for_heads). For each query row, over key tiles of
+/* ---- B. Quantized attention core (kv head of q head h is h / (H / Hk)
+ * [impl] _repeat_kv_for_heads). For each query row, over key tiles of
  * kv_tile keys ([tq] online softmax): a = integer q.k; c = RN(qs * ks) (times
  * score_scale if it is not 1); s = RN(a c); m' = max(m, tile max of s);
  * p = 2^fma(a, c, -m'); alpha = 2^(m - m'); l = l alpha + sum p; acc = acc alpha +
@@ -215,11 +215,18 @@ int sq_quant_v_fp8(const sq_rows* v, uint8_t* codes, int64_t ob, int64_t oh, int
  * q rows carry the softmax scale (log2(e)/sqrt(D) through sm_scale). q layouts:
  * PER_BLOCK, THREAD_Q, WARP_Q; k layouts: PER_BLOCK, THREAD_K. kv_tile: 64 or 128
  * (FP8 P.V: 128). out FP32 (B, Sq, H, D) at out[b*ob + i*ot + h*oh + c]; lse FP32
- * (B, H, Sq) at lse[b*lb + h*lh + i], or NULL. */
+ * (B, H, Sq) at lse[b*lb + h*lh + i], or NULL.
+ * causal (0 or 1) [impl] _sdpa_one's mask, [tq] unified attention's causal mask:
+ * query i sits at key position i + Sk - Sq (its context is the Sk - Sq keys before
+ * the queries) and sees keys 0 .. i + Sk - Sq; needs Sk >= Sq (SQ_ERR_SHAPE).
+ * sinks: NULL, or FP32 (H,) per-head sink logits in natural-log units [tq] USE_SINKS:
+ * the running max starts at m = RN(sink * log2(e)) (FP32) and the sum at l = 1, so
+ * the sink joins the denominator (and lse) but adds no value row. When two passes
+ * are merged (sq_lse_merge, sq_attn_prefix_lse_merge), give the sinks to one only. */
 size_t sq_attn_workspace_bytes(const sq_qk* q, const sq_qk* k, const sq_values* v);
-int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scale, int kv_tile, float* out,
-            int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh, void* ws, size_t ws_bytes,
-            void* stream);
+int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scale, int kv_tile, int causal,
+            const float* sinks, float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh,
+            void* ws, size_t ws_bytes, void* stream);
 
 /* ---- C. q8 prefix pass + log-sum-exp merge [kit] _attend_with_prefix,
  * dequantize_q8_into, _merge_lse_. The same q codes attend the prefix keys in a
@@ -263,13 +270,16 @@ int sq_lse_merge(float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int
  * 16-byte aligned, scale tensors 8-byte aligned (one row of 4 FP16 per slot and head).
  * Both products run on f16 matrix units with FP32 accumulation: q is carried as f16
  * after an exact power-of-two rescale per head, and the weight of a value row is
- * f16(p * value scale) (relative rounding <= 2^-11 per weight). */
+ * f16(p * value scale) (relative rounding <= 2^-11 per weight).
+ * sinks: NULL, or FP32 (Hq,) per-query-head sink logits in natural-log units
+ * [tq] USE_SINKS (the split kernel's first segment carries it): exp(sink) joins the
+ * softmax denominator once per (sequence, head) and adds no value row. */
 size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_len);
 int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
                     const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
-                    int max_seq_len, int Hq, int D, float softmax_scale, float* out, int64_t on, int64_t oh,
-                    void* ws, size_t ws_bytes, void* stream);
+                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, float* out, int64_t on,
+                    int64_t oh, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- D2. q8 paged-cache writer [kit] quantize_q8 (per token, head and group of 32
  * channels: scale = max(amax / 127, 1e-8) in FP32, code = x / scale (correctly

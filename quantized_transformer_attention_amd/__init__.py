@@ -68,6 +68,7 @@ class sq_q8prefix(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 2  # SQ_ABI_VERSION of the sq.h these argument lists follow
 
 EXPORTS = ["sq_scale_count", "sq_norm_stats", "sq_kmean_workspace_bytes", "sq_kmean", "sq_quant_qk_workspace_bytes",
            "sq_quant_qk", "sq_quant_v_fp8_workspace_bytes", "sq_quant_v_fp8", "sq_attn_workspace_bytes", "sq_attn",
@@ -96,8 +97,8 @@ def lib():
         L.sq_quant_v_fp8.argtypes = [P(sq_rows), _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _sz, _vp]
         L.sq_attn_workspace_bytes.argtypes = [P(sq_qk), P(sq_qk), P(sq_values)]
         L.sq_attn_workspace_bytes.restype = _sz
-        L.sq_attn.argtypes = [P(sq_qk), P(sq_qk), P(sq_values), _f32, _int, _vp, _i64, _i64, _i64, _vp, _i64, _i64,
-                              _vp, _sz, _vp]
+        L.sq_attn.argtypes = [P(sq_qk), P(sq_qk), P(sq_values), _f32, _int, _int, _vp, _vp, _i64, _i64, _i64, _vp,
+                              _i64, _i64, _vp, _sz, _vp]
         L.sq_attn_prefix_lse_merge_workspace_bytes.argtypes = [P(sq_qk), P(sq_q8prefix)]
         L.sq_attn_prefix_lse_merge_workspace_bytes.restype = _sz
         L.sq_attn_prefix_lse_merge.argtypes = [P(sq_qk), P(sq_q8prefix), _vp, _i64, _i64, _f32, _int, _vp, _i64, _i64,
@@ -105,7 +106,7 @@ def lib():
         L.sq_paged_decode_workspace_bytes.argtypes = [_int, _int, _int, _int]
         L.sq_paged_decode_workspace_bytes.restype = _sz
         L.sq_paged_decode.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
-                                      _int, _int, _int, _f32, _vp, _i64, _i64, _vp, _sz, _vp]
+                                      _int, _int, _int, _f32, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
         L.sq_lse_merge.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                    _i64, _i64, _i64, _vp]
         L.sq_q8_cache_write.argtypes = [_vp, _vp, _int, _i64, _int, _int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
@@ -113,6 +114,9 @@ def lib():
         L.sq_status_string.argtypes, L.sq_status_string.restype = [_int], ctypes.c_char_p
         L.sq_last_error.argtypes, L.sq_last_error.restype = [], ctypes.c_char_p
         L.sq_abi_version.restype = _int
+        if L.sq_abi_version() != ABI_VERSION:
+            raise ImportError("libsq.so has ABI version %d, this binding needs %d: rebuild it"
+                              % (L.sq_abi_version(), ABI_VERSION))
         _lib = L
     return _lib
 
@@ -289,8 +293,10 @@ def _values(v: torch.Tensor, v_scale: Optional[torch.Tensor]) -> sq_values:
 
 def sq_attn(q: QK, k: QK, v: torch.Tensor, v_scale: Optional[torch.Tensor] = None, score_scale: float = 1.0,
             kv_tile: int = 64, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            want_lse: bool = True, workspace: Optional[Workspace] = None):
+            want_lse: bool = True, workspace: Optional[Workspace] = None, causal: bool = False,
+            sinks: Optional[torch.Tensor] = None):
     """Quantized attention core. v: bf16 (B, Sk, Hk, D) token-major, or FP8 codes from sq_quant_v_fp8 with v_scale.
+    causal: query i sees keys 0 .. i + Sk - Sq; sinks: FP32 (H,) per-head sink logits (natural log) or None.
     Returns (out FP32 (B, Sq, H, D), lse FP32 (B, H, Sq) base 2 or None)."""
     B, Sq, H, D = q.codes.shape
     dev = q.codes.device
@@ -302,7 +308,10 @@ def sq_attn(q: QK, k: QK, v: torch.Tensor, v_scale: Optional[torch.Tensor] = Non
     L = lib()
     need = L.sq_attn_workspace_bytes(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc))
     ws, nb = workspace.get(need) if workspace is not None else _ws(need, dev)
-    _check(L.sq_attn(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), score_scale, kv_tile, _ptr(out),
+    if sinks is not None:
+        assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == H, "sinks: FP32 (H,)"
+    _check(L.sq_attn(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), score_scale, kv_tile, int(causal),
+                     _ptr(sinks), _ptr(out),
                      out.stride(0), out.stride(1), out.stride(2), _ptr(lse), lse.stride(0) if lse is not None else 0,
                      lse.stride(1) if lse is not None else 0, _ptr(ws), nb, _stream(dev)))
     return out, lse
@@ -344,12 +353,16 @@ def sq_attn_prefix_lse_merge(q: QK, prefix: Q8Prefix, k_mean: Optional[torch.Ten
 def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
                     v_scale: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                     softmax_scale: float, out: Optional[torch.Tensor] = None,
-                    workspace: Optional[Workspace] = None) -> torch.Tensor:
+                    workspace: Optional[Workspace] = None, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged GQA decode over a q8 cache. q bf16 (N, Hq, D); caches int8 [NB, bs, Hk, D] with FP16 scales
-    [NB, bs, Hk, D/32]; block_table int32 (N, max_blocks); seq_lens int32 (N,). Returns FP32 (N, Hq, D)."""
+    [NB, bs, Hk, D/32]; block_table int32 (N, max_blocks); seq_lens int32 (N,); sinks FP32 (Hq,) per-head sink
+    logits (natural log) or None. Returns FP32 (N, Hq, D)."""
     N, Hq, D = q.shape
     NB, bs, Hk, _ = k_cache.shape
     dev = q.device
+    if sinks is not None:
+        assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == Hq, "sinks: FP32 (Hq,)"
+
     if out is None:
         out = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
     L = lib()
@@ -357,7 +370,8 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
     ws, nb = workspace.get(need) if workspace is not None else _ws(need, dev)
     _check(L.sq_paged_decode(_ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                              _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0), _ptr(seq_lens), N,
-                             max_seq_len, Hq, D, softmax_scale, _ptr(out), out.stride(0), out.stride(1), _ptr(ws), nb,
+                             max_seq_len, Hq, D, softmax_scale, _ptr(sinks), _ptr(out), out.stride(0), out.stride(1),
+                             _ptr(ws), nb,
                              _stream(dev)))
     return out
 

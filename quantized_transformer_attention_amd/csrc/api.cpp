@@ -194,9 +194,9 @@ size_t sq_attn_workspace_bytes(const sq_qk* q, const sq_qk* k, const sq_values* 
     return round_up(sizeof(uint16_t) * static_cast<size_t>(k->B * k->H * k->D * padded_keys(k->S)));
 }
 
-int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scale, int kv_tile, float* out,
-            int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh, void* ws, size_t ws_bytes,
-            void* stream) {
+int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scale, int kv_tile, int causal,
+            const float* sinks, float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh,
+            void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     int st = check_pair(q, k, "sq_attn");
     if (st) return st;
@@ -208,6 +208,10 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
     if (kv_tile != 64 && kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "sq_attn: kv_tile must be 64 or 128");
     if (!(score_scale > 0.0f) || !std::isfinite(score_scale))
         return fail(SQ_ERR_SHAPE, "sq_attn: score_scale must be finite and > 0");
+    if (causal != 0 && causal != 1) return fail(SQ_ERR_SHAPE, "sq_attn: causal must be 0 or 1");
+    if (causal && k->S < q->S)
+        return fail(SQ_ERR_SHAPE, "sq_attn: causal needs at least as many keys as queries (Sk %lld < Sq %lld)",
+                    (long long)k->S, (long long)q->S);
     AttnArgs a{};
     a.q = q->codes; a.B = q->B; a.Sq = q->S; a.H = q->H; a.D = q->D;
     a.qsb = q->sb; a.qst = q->st; a.qsh = q->sh;
@@ -219,6 +223,8 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
     a.k_nscale = static_cast<int>(sq_scale_count(k->S, k->layout, k->block));
     a.score_scale = score_scale;
     a.kv_tile = kv_tile;
+    a.causal = causal;
+    a.sinks = sinks;
     a.out = out; a.ob = ob; a.ot = ot; a.oh = oh;
     a.lse = lse; a.lb = lb; a.lh = lh;
     // the key loop addresses one (b, kv head) slice of K and of V^T with 32-bit byte offsets
@@ -392,8 +398,8 @@ size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_
 int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
                     const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
-                    int max_seq_len, int Hq, int D, float softmax_scale, float* out, int64_t on, int64_t oh,
-                    void* ws, size_t ws_bytes, void* stream) {
+                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, float* out, int64_t on,
+                    int64_t oh, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     const char* what = "sq_paged_decode";
     if (num_seqs < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
@@ -431,6 +437,7 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     a.bt = block_table; a.bt_stride = bt_stride; a.lens = seq_lens;
     a.N = num_seqs; a.max_len = max_seq_len;
     a.scale = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);  // log2 units
+    a.sinks = sinks;
     a.out = out; a.on = on; a.oh = oh;
     a.part = static_cast<float*>(ws);
     a.segs = (max_seq_len + kDecodeSeg - 1) / kDecodeSeg;

@@ -138,9 +138,11 @@ __device__ __forceinline__ v4f_t load_kscales(__amdgpu_buffer_rsrc_t r, int kg0,
 
 // One key tile: S^T = K Q^T on INT8 MFMA, online softmax in base 2, acc += P V.
 // ks: this lane group's key scales for the tile (load_kscales).
+// TAIL: keys are masked per query, key kappa of query qi kept iff kappa < min(Sk, qend0 + qi - q0)
+// with qend0 the key end of the wave's first query (Sk when not causal).
 template <int D, int KT, bool FP8, bool TAIL>
 __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
-                                          const uint8_t* v_lds, int kbase, v4f_t ks, int lq, int g) {
+                                          const uint8_t* v_lds, int kbase, v4f_t ks, int lq, int g, int qend0) {
     using C = Cfg<D, KT, FP8>;
     // c = RN(qs ks) per k-scale group of this lane group's keys (times score_scale: exact for 1)
     const int kg0 = kbase + C::KQ * g;
@@ -172,10 +174,10 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
                 s[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, st.qop[n][ch], ch == 0 ? v4i{0, 0, 0, 0} : s[t], 0, 0, 0);
             }
         }
-        // keys of this lane group in the tile (all KQ but in the last one); opaque so that the
-        // masks of the last tile are not computed once before the key loop and kept (64
-        // scalar registers of lane masks)
-        int nval = static_cast<int>(a.Sk) - kg0;
+        // keys of this lane group in the tile that this lane's query sees (all KQ but in the last
+        // tile and, causal, the diagonal ones); opaque so that the masks are not computed once
+        // before the key loop and kept (64 scalar registers of lane masks)
+        int nval = min(static_cast<int>(a.Sk), qend0 + 16 * n + lq) - kg0;
         if (TAIL) asm volatile("" : "+v"(nval));
         int amx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
 #pragma unroll
@@ -268,10 +270,15 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const int64_t items = nqb * a.H * a.B;
     const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
     if (item >= items) return;  // uniform over the workgroup
-    const int64_t qb = item % nqb, h = (item / nqb) % a.H, b = item / (nqb * a.H);
+    // causal: the last query blocks see the most keys and are dealt first
+    const int64_t qb = a.causal ? nqb - 1 - item % nqb : item % nqb, h = (item / nqb) % a.H, b = item / (nqb * a.H);
     const int64_t hk = h / (a.H / a.Hk);
     const int64_t q0 = qb * C::QPB + w * (C::NQ * 16);
 
+    // a sink starts the running max at its logit (base 2) and the sum at 1, counted once: in lane
+    // group 0, whose sum the epilogue adds to the other three
+    const float m0 = a.sinks ? a.sinks[h] * 1.44269504f : -__builtin_inff();
+    const float l0 = (a.sinks && g == 0) ? 1.0f : 0.0f;
     WaveState<D, KT, FP8> st;
 #pragma unroll
     for (int n = 0; n < C::NQ; ++n) {
@@ -283,8 +290,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
             st.qop[n][ch] = ok ? *reinterpret_cast<const v4i*>(a.q + b * a.qsb + qi * a.qst + h * a.qsh + ch * 64 + 16 * g) : z;
         }
         st.qsc[n] = ok ? a.qs[b * a.qssb + h * a.qssh + scale_idx(qi, a.q_layout, a.q_block)] : 0.0f;
-        st.m_run[n] = -__builtin_inff();
-        st.l_run[n] = 0.0f;
+        st.m_run[n] = m0;
+        st.l_run[n] = l0;
 #pragma unroll
         for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -301,9 +308,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const float* ksp = a.ks + b * a.kssb + hk * a.kssh;
     const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ksp), 0, 4 * a.k_nscale, 0x00020000);
     const int kl_layout = a.k_layout, kl_shift = a.k_shift;
-    const bool tail = a.Sk % KT != 0;
-    const int ntiles = static_cast<int>((a.Sk + KT - 1) / KT);
-    const int last = ntiles - 1;
+    // Causal: query i sits at key position i + Sk - Sq and sees keys up to it. The workgroup
+    // reads the key tiles its last query sees; a wave masks the tiles past its first query's
+    // end (lo_end) and skips those past its last query's end (hi_end).
+    const int Sk = static_cast<int>(a.Sk), off = Sk - Sq;
+    const int kv_end = a.causal ? min(Sk, static_cast<int>(min(a.Sq, qb * C::QPB + C::QPB)) + off) : Sk;
+    const int ntiles = (kv_end + KT - 1) / KT;
+    const int qend0 = a.causal ? q0i + off + 1 : Sk;
+    const int lo_end = min(Sk, qend0), hi_end = a.causal ? min(Sk, q0i + C::NQ * 16 + off) : Sk;
     const int kst = static_cast<int>(a.kst), vrow = static_cast<int>(a.vsd) * C::VB;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kb), 0, static_cast<int>((a.Sk - 1) * a.kst + D), 0x00020000);
@@ -316,8 +328,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     // processed, so no wait on them ever waits for a copy in flight
     auto kscales = [&](int j) { return load_kscales(ksr, j * KT + C::KQ * g, kl_layout, kl_shift); };
     auto step = [&](int j, const uint8_t* buf, v4f_t ks) {
-        if (tail && j == last) tile_step<D, KT, FP8, true>(a, st, buf, buf + C::KBYTES, j * KT, ks, lq, g);
-        else tile_step<D, KT, FP8, false>(a, st, buf, buf + C::KBYTES, j * KT, ks, lq, g);
+        const int kbase = j * KT;
+        if (kbase >= hi_end) return;  // no query of the wave sees the tile: its state is unchanged
+        if (kbase + KT > lo_end) tile_step<D, KT, FP8, true>(a, st, buf, buf + C::KBYTES, kbase, ks, lq, g, qend0);
+        else tile_step<D, KT, FP8, false>(a, st, buf, buf + C::KBYTES, kbase, ks, lq, g, qend0);
     };
     v4f_t ks_next = kscales(0);
     copy(0, buf0);

@@ -315,9 +315,12 @@ __global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
     for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, shfl_xor(mg, off));
     if ((c & 63) == 0) red[c >> 6] = mg;
     __syncthreads();
-    mg = fmaxf(red[0], red[1]);
+    // a sink joins as one more term of the denominator, at its logit in base 2
+    const float sk = a.sinks ? a.sinks[hq] * 1.44269504f : -__builtin_inff();
+    mg = fmaxf(fmaxf(red[0], red[1]), sk);
     float tot = 0.0f, o = 0.0f;
     if (mg > -__builtin_inff()) {  // uniform over the workgroup
+        if (sk > -__builtin_inff()) tot = __builtin_amdgcn_exp2f(sk - mg);
         for (int s0 = 0; s0 < nseg; s0 += SB) {
             const int s = s0 + c;
             float wgt = 0.0f, ls = 0.0f;

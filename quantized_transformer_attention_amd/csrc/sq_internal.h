@@ -88,6 +88,8 @@ struct AttnArgs {
     int64_t vssb, vssh;
     float score_scale;
     int kv_tile;
+    int causal;                 // query i sees keys 0 .. i + Sk - Sq
+    const float* sinks;         // (H,) sink logits in natural-log units, or NULL
     float* out;
     int64_t ob, ot, oh;
     float* lse;
@@ -120,6 +122,8 @@ struct PrefixArgs {
     int64_t mb, mh;
     float score_scale;
     int kv_tile;
+    int causal;                 // query i sees keys 0 .. i + Sk - Sq
+    const float* sinks;         // (H,) sink logits in natural-log units, or NULL
     float* out;
     int64_t ob, ot, oh;
     float* lse;
@@ -169,6 +173,7 @@ struct DecodeArgs {
     const int32_t* lens;
     int N, max_len;
     float scale;
+    const float* sinks;         // (Hq,) sink logits in natural-log units, or NULL
     float* out;
     int64_t on, oh;
     float* part;                // split-KV partials (N, Hq, segs, D + 2): acc, max, exp-sum

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(sq.EXPORTS)
-    assert L.sq_abi_version() == 1
+    assert L.sq_abi_version() == sq.ABI_VERSION == 2
 
 
 def test_status_strings():
@@ -87,9 +87,9 @@ def test_attn_validation_errors():
     L = sq.lib()
     v = sq.sq_values(0x3000, sq.SQ_BF16, 10 * 2 * 128, 2 * 128, 128, 1, None, 0, 0)
 
-    def call(q, k, vv=v, tile=64, out=0x4000, scale=1.0, ws=None, wsb=0):
-        return L.sq_attn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vv), scale, tile, out, 0, 0, 0, None, 0, 0,
-                         ws, wsb, None)
+    def call(q, k, vv=v, tile=64, out=0x4000, scale=1.0, ws=None, wsb=0, causal=0):
+        return L.sq_attn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vv), scale, tile, causal, None, out, 0, 0, 0,
+                         None, 0, 0, ws, wsb, None)
 
     assert call(_qk(layout=2), _qk()) == -5                # THREAD_K is a key layout
     assert call(_qk(), _qk(layout=1, block=32)) == -5      # THREAD_Q is a query layout
@@ -107,6 +107,9 @@ def test_attn_validation_errors():
     v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 8, 0x5000, 0, 0)
     assert call(_qk(), _qk(), vv=v8, tile=128) == -3       # channel stride below the key count
     assert call(_qk(S=0), _qk()) == 0                      # no queries: no-op
+    assert call(_qk(), _qk(), causal=2) == -2              # causal is 0 or 1
+    assert call(_qk(S=11), _qk(S=10), causal=1) == -2      # causal needs Sk >= Sq
+    assert call(_qk(S=11), _qk(S=10), causal=0) == -6      # (non-causal: any Sk; then the workspace check)
 
 
 def _call_cache_write(dtype=0, n=4, Hk=2, D=128, k=0x1000, v=0x2000, kn=256, kh=128, slots=0x3000, kc=0x4000,
