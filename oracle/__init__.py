@@ -88,6 +88,8 @@ def _declare(L):
     L.orc_paged_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _f64, _vp,
                                    _vp]
     L.orc_attn_exact.argtypes = [P(_Rows), P(_Rows), _vp, P(_Prefix), _vp, _i64, _vp]
+    L.orc_paged_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
+                                    _f64, _vp, _vp, _i64, _vp]
 
 
 def _c(a, dtype):
@@ -347,6 +349,24 @@ def paged_decode(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, s
     sk_ = _c(sinks, np.float32) if sinks is not None else None
     lib().orc_paged_decode(_p(q), _p(kc), _p(ks), _p(vc), _p(vsc), bs, Hk, _p(bt), bt.shape[1], _p(sl), N, Hq, D,
                            float(scale), _p(sk_), _p(out))
+    return out
+
+
+def paged_prefill(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, query_start, scale, sinks=None,
+                  rows=None):
+    """Binary64 paged causal prefill over a q8 cache ([impl] _prefill_torch_from_cache): q bf16 (T, Hq, D) packed
+    by query_start (N + 1,); seq_lens (N,) keys per sequence (context + its queries). out (len(rows) or T, Hq, D)."""
+    q = _c(q, np.uint16)
+    kc, ks, vc, vsc = _c(k_cache, np.int8), _c(k_scale, np.uint16), _c(v_cache, np.int8), _c(v_scale, np.uint16)
+    bt, sl, qsl = _c(block_table, np.int32), _c(seq_lens, np.int32), _c(query_start, np.int32)
+    T, Hq, D = q.shape
+    bs, Hk = kc.shape[1], kc.shape[2]
+    rows_ = _c(rows, np.int64) if rows is not None else None
+    n = rows_.size if rows_ is not None else T
+    out = np.empty((n, Hq, D), np.float64)
+    sk_ = _c(sinks, np.float32) if sinks is not None else None
+    lib().orc_paged_prefill(_p(q), _p(kc), _p(ks), _p(vc), _p(vsc), bs, Hk, _p(bt), bt.shape[1], _p(sl), _p(qsl),
+                            sl.size, Hq, D, float(scale), _p(sk_), _p(rows_), n, _p(out))
     return out
 
 

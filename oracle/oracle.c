@@ -23,7 +23,7 @@
  *           _blocks / PADDED_ROWS, _rows, _norm_rope_quant, norm_rope_mean,
  *           norm_rope_quantize.
  *   [impl]  fastkernels L2/attention_impl.py: _repeat_kv_for_heads, _cache_seq,
- *           _sdpa_one, _decode_torch.
+ *           _sdpa_one, _decode_torch, _prefill_torch_from_cache.
  *   [tq]    vLLM triton_turboquant_unified_attention.py: the 2D kernel's online
  *           softmax (m_j, P, l_j, alpha, acc) and the 3D split-KV kernel.
  *
@@ -718,6 +718,62 @@ void orc_paged_decode(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
                 for (int64_t d = 0; d < D; ++d) acc[d] += p * ((double)vc[base * D + d] * f16_value(vsc[base * NG + d / 32]));
             }
             for (int64_t d = 0; d < D; ++d) out[(n * Hq + h) * D + d] = L > 0 ? acc[d] / l : 0.0;
+            free(s);
+        }
+}
+
+/* ------------------------------------------------------------------------------
+ * Paged (chunked) causal prefill over a q8 cache [impl] _prefill_torch_from_cache,
+ * _cache_seq, _sdpa_one, _repeat_kv_for_heads; [tq] unified 2D kernel (varlen queries
+ * by query_start_len, seq_lens = context + query length, sinks). Sequence n owns the
+ * query tokens [query_start[n], query_start[n+1]) (q_len of them) and the keys at
+ * positions 0..seq_lens[n]-1 of its paged cache; its query j sits at position
+ * key_offset + j, key_offset = seq_lens[n] - q_len, and attends the keys at positions
+ * 0..key_offset + j (the mask k_pos <= key_offset + q_pos). Keys and values are the exact
+ * q8 values code * fp16 scale; binary64 softmax of (q . k) * scale; a sink adds exp(sink)
+ * to the denominator only. rows: the query tokens to compute (NULL: all T of them);
+ * out (nrows, Hq, D). q (T, Hq, D) bf16 contiguous.
+ * ---------------------------------------------------------------------------- */
+void orc_paged_prefill(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
+                       const int8_t* vc, const uint16_t* vsc, int64_t bs, int64_t Hk,
+                       const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                       const int32_t* query_start, int64_t N, int64_t Hq, int64_t D, double scale,
+                       const float* sinks, const int64_t* rows, int64_t nrows, double* out) {
+    const int64_t G = Hq / Hk, NG = D / 32;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t t = rows ? rows[r] : r;
+            int64_t n = 0;
+            while (n + 1 < N && query_start[n + 1] <= t) ++n;     /* the sequence that owns token t */
+            const int64_t q_len = query_start[n + 1] - query_start[n];
+            const int64_t k_len = seq_lens[n];
+            const int64_t key_offset = k_len - q_len;
+            const int64_t j = t - query_start[n];
+            const int64_t last = key_offset + j;                  /* keys 0..last are visible */
+            const int64_t hk = h / G;
+            double* s = (double*)malloc(sizeof(double) * (size_t)(last + 1));
+            double m = -INFINITY, l = 0.0, acc[512];
+            for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t pos = 0; pos <= last; ++pos) {
+                int64_t phys = block_table[n * bt_stride + pos / bs], slot = pos % bs;
+                int64_t base = (phys * bs + slot) * Hk + hk;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += (double)bf16_f32(q[(t * Hq + h) * D + d]) * ((double)kc[base * D + d] * f16_value(ks[base * NG + d / 32]));
+                s[pos] = dot * scale;
+                m = fmax(m, s[pos]);
+            }
+            if (sinks) m = fmax(m, (double)sinks[h]);
+            if (sinks) l = exp((double)sinks[h] - m);
+            for (int64_t pos = 0; pos <= last; ++pos) {
+                int64_t phys = block_table[n * bt_stride + pos / bs], slot = pos % bs;
+                int64_t base = (phys * bs + slot) * Hk + hk;
+                double p = exp(s[pos] - m);
+                l += p;
+                for (int64_t d = 0; d < D; ++d) acc[d] += p * ((double)vc[base * D + d] * f16_value(vsc[base * NG + d / 32]));
+            }
+            for (int64_t d = 0; d < D; ++d) out[(r * Hq + h) * D + d] = acc[d] / l;
             free(s);
         }
 }

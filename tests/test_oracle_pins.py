@@ -705,3 +705,107 @@ def test_paged_decode_sinks():
             p = np.exp(s - m)
             ref = p @ vv[:, h // 4] / (p.sum() + np.exp(float(sinks[h]) - m))
             np.testing.assert_allclose(out[n, h], ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- paged prefill
+def _prefill_case(g, ctx=(0, 23, 40), qlen=(5, 17, 1), Hq=8, Hk=2, D=64, bs=16, extra=2):
+    """A varlen batch over a paged q8 cache: sequence n has ctx[n] cached keys before its qlen[n] queries, whose
+    own keys are in the cache too (seq_lens = ctx + qlen), pages dealt from a seeded permutation."""
+    lens = np.array(ctx, np.int32) + np.array(qlen, np.int32)
+    pages = [(int(L) + bs - 1) // bs for L in lens]
+    NB = sum(pages) + extra
+    kc, ks = O.q8_quantize(g.standard_normal((NB, bs, Hk, D)).astype(np.float32))
+    vc, vs = O.q8_quantize(g.standard_normal((NB, bs, Hk, D)).astype(np.float32))
+    perm = g.permutation(NB)
+    bt = np.full((len(lens), max(pages) + 1), -1, np.int32)
+    o = 0
+    for n, p in enumerate(pages):
+        bt[n, :p] = perm[o:o + p]
+        o += p
+    qs = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    q = gen.normal_bf16((int(qs[-1]), 1, Hq, D), g).reshape(-1, Hq, D)
+    return q, kc, ks, vc, vs, bt, lens, qs
+
+
+def _gather(c, s, bt_row, L, Hk, D):
+    """Dense (L, Hk, D) binary64 q8 values of one sequence gathered through its block-table row."""
+    f16 = s.view(np.float16).astype(np.float64)
+    pages = bt_row[:(L + 15) // 16]
+    return (c[pages].astype(np.float64) * np.repeat(f16[pages], 32, -1)).reshape(-1, Hk, D)[:L]
+
+
+def test_paged_prefill_matches_torch_sdpa_with_the_pages_mask():
+    """Against torch's own scaled_dot_product_attention in float64 on the CPU, called as [impl] _sdpa_one calls it:
+    GQA by repeat_interleave, the boolean mask k_pos <= key_offset + q_pos, key_offset = k_len - q_len."""
+    import torch
+    import torch.nn.functional as F
+    g = np.random.default_rng(71)
+    Hq, Hk, D = 8, 2, 64
+    q, kc, ks, vc, vs, bt, lens, qs = _prefill_case(g, Hq=Hq, Hk=Hk, D=D)
+    scale = 1 / math.sqrt(D)
+    out = O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale)
+    qf = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for n in range(len(lens)):
+        L, a, b = int(lens[n]), int(qs[n]), int(qs[n + 1])
+        kseq = torch.from_numpy(_gather(kc, ks, bt[n], L, Hk, D)).repeat_interleave(Hq // Hk, dim=1)
+        vseq = torch.from_numpy(_gather(vc, vs, bt[n], L, Hk, D)).repeat_interleave(Hq // Hk, dim=1)
+        qseq = torch.from_numpy(qf[a:b])
+        qpos = (L - (b - a)) + torch.arange(b - a)
+        mask = torch.arange(L)[None, :] <= qpos[:, None]
+        ref = F.scaled_dot_product_attention(qseq.transpose(0, 1)[None], kseq.transpose(0, 1)[None],
+                                             vseq.transpose(0, 1)[None], attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(out[a:b], ref[0].transpose(0, 1).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_paged_prefill_rows_are_decode_and_chunking_invariant():
+    """A query's row depends only on the keys it sees: the last query of a sequence equals the paged decode over
+    the whole sequence, a one-query sequence is a decode, and splitting a sequence's queries into a cached context
+    and a later chunk leaves every later row unchanged, bit for bit."""
+    g = np.random.default_rng(72)
+    q, kc, ks, vc, vs, bt, lens, qs = _prefill_case(g)
+    scale = 0.125
+    out = O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale)
+    last = qs[1:] - 1
+    dec = O.paged_decode(q[last], kc, ks, vc, vs, bt, lens, scale)
+    np.testing.assert_array_equal(out[last], dec)
+    # sequence 1 (23 cached + 17 queries) as 30 cached + the last 10 queries: those rows are unchanged
+    qs2 = np.array([0, 10], np.int32)
+    out2 = O.paged_prefill(q[qs[1] + 7:qs[2]], kc, ks, vc, vs, bt[1:2], lens[1:2], qs2, scale)
+    np.testing.assert_array_equal(out2, out[qs[1] + 7:qs[2]])
+    # rows= computes the same rows alone
+    rows = np.array([0, 4, 6, 21], np.int64)
+    np.testing.assert_array_equal(O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale, rows=rows), out[rows])
+    # physical blocks relabelled with the table: bit-identical
+    NB = kc.shape[0]
+    perm = g.permutation(NB)
+    inv = np.argsort(perm)
+    bt2 = np.where(bt >= 0, inv[np.maximum(bt, 0)], -1).astype(np.int32)
+    np.testing.assert_array_equal(O.paged_prefill(q, kc[perm], ks[perm], vc[perm], vs[perm], bt2, lens, qs, scale), out)
+
+
+def test_paged_prefill_equal_keys_give_running_means():
+    """With every key equal all visible scores tie, so query j of a sequence with key_offset o returns the mean of
+    the values at positions 0..o + j (a running mean, written with numpy's cumsum); a sink of logit z adds
+    exp(z - s0) to the count, s0 the common score."""
+    g = np.random.default_rng(73)
+    Hq, Hk, D = 4, 2, 64
+    q, kc, ks, vc, vs, bt, lens, qs = _prefill_case(g, Hq=Hq, Hk=Hk, D=D)
+    kc[:] = 3
+    ks[:] = gen.to_f16_bits(np.full(ks.shape, 0.5, np.float32))
+    scale = 0.1
+    sinks = np.array([0.5, -1.0, 2.0, -np.inf], np.float32)
+    out = O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale)
+    outs = O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale, sinks=sinks)
+    qf = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for n in range(len(lens)):
+        L, a, b = int(lens[n]), int(qs[n]), int(qs[n + 1])
+        vseq = _gather(vc, vs, bt[n], L, Hk, D)
+        csum = np.cumsum(vseq, axis=0)
+        for j in range(b - a):
+            last = L - (b - a) + j
+            for h in range(Hq):
+                ref = csum[last, h // 2] / (last + 1)
+                np.testing.assert_allclose(out[a + j, h], ref, rtol=1e-12, atol=1e-14)
+                s0 = float(qf[a + j, h].sum() * 1.5) * scale
+                cnt = (last + 1) + np.exp(float(sinks[h]) - s0)
+                np.testing.assert_allclose(outs[a + j, h], csum[last, h // 2] / cnt, rtol=1e-10, atol=1e-14)
