@@ -11,7 +11,8 @@ stage in the library's HIP kernels:
   joint: the video recipe's projected pass at H=24, 8704 tokens (PER_BLOCK q 128 / k 64,
     bf16 P.V) plus the 4096-token q8 prefix pass merged by log-sum-exp;
   quantizer: k mean + the five quantizer runs of a 2 x 75600 x 40 x 128 tensor;
-  decode: paged GQA decode of 64 sequences over a q8 cache.
+  decode: paged GQA decode of 64 sequences over a q8 cache;
+  prefill: paged causal chunked prefill of 16 sequences (1024-token chunks) over a q8 cache.
 value = the workload's algorithmic work / the step time (TFLOPS = 4 B H Sq Sk D for the
 attention workloads; GB/s of algorithmic bytes for the quantizer and decode).
 
@@ -34,7 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS_INT8 = 5000.0        # dense INT8 (and FP8) MFMA, POP/s -> TFLOP/s units
-PEAK_TFLOPS_BF16 = 2500.0
+PEAK_TFLOPS_BF16 = 2500.0        # dense bf16 and f16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "quantized_transformer_attention_amd", "csrc")
@@ -46,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video",
-                    choices=["video", "causal", "joint", "quantizer", "decode", "cachewrite", "merge", "copy"],
+                    choices=["video", "causal", "joint", "quantizer", "decode", "prefill", "cachewrite", "merge",
+                             "copy"],
                     help="copy: a plain 1 GiB device copy, the reference for scaling HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time for the baseline")
@@ -324,6 +326,45 @@ def run_decode(args, torch, sq, gen, timer):
     return res, line
 
 
+def run_prefill(args, torch, sq, gen, timer):
+    """Paged causal chunked prefill: 16 sequences with cached contexts ~U{0..8192} and 1024-token chunks each,
+    Hq 32 / Hk 8, d 128, block 16, q8 cache. Work = 4 Hq d x the visible (query, key) pairs."""
+    import numpy as np
+
+    c = gen.PREFILL
+    dev = torch.device("cuda:0")
+    q, kc, ks, vc, vs, bt, lens, qs = gen.prefill_case(c)
+    f16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.float16).to(dev)
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to(dev)
+    kd, vd = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+    ksd, vsd = f16(ks), f16(vs)
+    btd, ld, qsd = torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev), torch.from_numpy(qs).to(dev)
+    out = torch.empty((q.shape[0], c.Hq, c.D), dtype=torch.float32, device=dev)
+
+    def step():
+        timer("prefill", lambda: sq.sq_paged_prefill(qd, kd, ksd, vd, vsd, btd, ld, qsd, c.max_len, c.scale, out=out))
+
+    ctx = lens.astype(np.float64) - c.chunk
+    pairs = float(np.sum(c.chunk * ctx + c.chunk * (c.chunk + 1) / 2))
+    flops = 4.0 * c.Hq * c.D * pairs
+    res = time_steps(args, torch, step, timer)
+    ms = timer.avg_ms("prefill")
+    achieved = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "paged causal prefill TFLOPS (4*Hq*d x visible query-key pairs) and % of f16 MFMA peak",
+        "value": flops / (res["ms"] * 1e-3) / 1e12, "unit": "TFLOPS", "dtype": "f16",
+        "config": {"workload": "paged chunked prefill, 16 sequences, contexts ~U(0,8192) + 1024-token chunks, "
+                               "32 q / 8 kv heads, d=128, block 16, q8 cache", "num_seqs": c.N, "chunk": c.chunk,
+                   "Hq": c.Hq, "Hk": c.Hk, "head_dim": c.D, "sum_len": int(lens.sum())},
+        "roofline": {"bound": "mfma", "kernel": "k_paged_prefill", "achieved": achieved, "peak": PEAK_TFLOPS_BF16,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS_BF16,
+                     "traffic": traffic_for("k_paged_prefill_prefill", ["prefill.hip", "device.h", "sq_internal.h"],
+                                            flops),
+                     "avg_launch_ms": ms, "flops_per_launch": flops},
+    }
+    return res, line
+
+
 def run_cachewrite(args, torch, sq, gen, timer):
     """q8 paged-cache writer: a 131072-token prefill chunk of new K/V rows (Hk 8, d 128, bf16; 537 MB read, more
     than the 256 MiB MALL, so the rows come from HBM) quantized and scattered to a random permutation of the slots of
@@ -468,6 +509,7 @@ def main():
     sq.lib()
     timer = Timer(torch)
     runners = {"video": run_video, "causal": run_causal, "joint": run_joint, "quantizer": run_quantizer, "decode": run_decode,
+               "prefill": run_prefill,
                "cachewrite": run_cachewrite, "merge": run_merge, "copy": run_copy}
     if args.workload not in runners:
         sys.exit("workload %s is not benchmarked yet" % args.workload)

@@ -255,3 +255,55 @@ def decode_fp32(c: DecodeConfig, NB: int):
 def decode_query(c: DecodeConfig, N: Optional[int] = None):
     N = c.N if N is None else N
     return normal_bf16((N, 1, c.Hq, c.D), rng(c.seed, S_DQ)).reshape(N, c.Hq, c.D)
+
+
+# ----------------------------------------------------------------------------- paged prefill workload
+@dataclass
+class PrefillConfig:
+    """Chunked prefill over the decode workload's cache shape: N sequences, each with a cached context of
+    ~U{0..ctx_max} keys and a chunk of `chunk` new queries whose keys and values are in the cache too."""
+    name: str = "paged_prefill"
+    cfg: int = 6
+    N: int = 16
+    chunk: int = 1024
+    ctx_max: int = 8192
+    Hq: int = 32
+    Hk: int = 8
+    D: int = 128
+    bs: int = 16
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.cfg
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def max_len(self) -> int:
+        return self.ctx_max + self.chunk
+
+
+PREFILL = PrefillConfig()
+
+
+def prefill_case(c: PrefillConfig):
+    """q bf16 (N * chunk, Hq, D); q8-format caches (random codes and scales, q8_like) for every slot; block table
+    (N, ceil(max_len / bs)) whose used entries are a seeded permutation of the NB physical blocks (-1 elsewhere);
+    seq_lens = context + chunk; query_start = 0, chunk, 2 chunk, ..."""
+    ctx = rng(c.seed, S_LENS).integers(0, c.ctx_max + 1, size=c.N).astype(np.int32)
+    lens = (ctx + c.chunk).astype(np.int32)
+    pages = (lens + c.bs - 1) // c.bs
+    NB = int(pages.sum())
+    perm = rng(c.seed, S_PERM).permutation(NB).astype(np.int32)
+    bt = np.full((c.N, (c.max_len + c.bs - 1) // c.bs), -1, np.int32)
+    o = 0
+    for n in range(c.N):
+        bt[n, :pages[n]] = perm[o:o + pages[n]]
+        o += pages[n]
+    kc, ks = q8_like((NB, c.bs, c.Hk, c.D), rng(c.seed, S_KC))
+    vc, vs = q8_like((NB, c.bs, c.Hk, c.D), rng(c.seed, S_VC))
+    q = normal_bf16((c.N * c.chunk, 1, c.Hq, c.D), rng(c.seed, S_DQ)).reshape(-1, c.Hq, c.D)
+    qs = (np.arange(c.N + 1) * c.chunk).astype(np.int32)
+    return q, kc, ks, vc, vs, bt, lens, qs

@@ -9,7 +9,8 @@
  *      (sq_attn);
  *   3. a pass over a cached q8 key/value prefix merged with the projected keys by
  *      log-sum-exp (sq_attn_prefix_lse_merge);
- *   4. paged, GQA-stacked decode over a q8 KV cache (sq_paged_decode).
+ *   4. paged, GQA-stacked decode over a q8 KV cache (sq_paged_decode), causal
+ *      chunked prefill over it (sq_paged_prefill) and its writer (sq_q8_cache_write).
  *
  * Sources, cited by page title and the section or identifier on the page:
  *   [kit]   WanGP shared/attention_kit.py
@@ -280,6 +281,29 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
                     int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, float* out, int64_t on,
                     int64_t oh, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- D3. Paged causal prefill over a q8 cache [impl] _prefill_torch_from_cache,
+ * _cache_seq, _sdpa_one (per sequence, mask k_pos <= key_offset + q_pos); [tq] unified
+ * 2D kernel (varlen q blocks by query_start_len, context_len = seq_len - query_len,
+ * USE_SINKS). Sequence n owns the packed query tokens [query_start[n], query_start[n+1])
+ * of q (bf16 (num_tokens, Hq, D) at q[t*qt + h*qh + c]; query_start int32 (num_seqs + 1,),
+ * nondecreasing, query_start[0] = 0, query_start[num_seqs] = num_tokens) and the keys at
+ * positions 0 .. L-1 of its paged cache, L = seq_lens[n] (the context plus its own
+ * queries, whose keys and values must already be in the cache, e.g. by
+ * sq_q8_cache_write; q_len <= L <= max_seq_len). Its query j sits at position L - q_len + j
+ * and attends positions 0 .. L - q_len + j. Caches, scales, block table and softmax_scale
+ * as sq_paged_decode (block_size 16, D 128, Hq / Hk in {1, 2, 4, 8}); sinks NULL or FP32
+ * (Hq,). out FP32 (num_tokens, Hq, D) at out[t*ot + h*oh + c]. Both products run on f16
+ * matrix units with FP32 accumulation: q as f16 after an exact power-of-two rescale per
+ * (token, head), keys and values dequantized to f16 (code * scale rounded once), P as f16
+ * (relative rounding <= 2^-11 each); cached keys and values must stay below 65504 in
+ * magnitude (the f16 range). A block-table entry outside [0, num_blocks) is read as block 0
+ * (no fault; that sequence's rows are then undefined). No workspace; only enqueues. */
+int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, const int8_t* k_cache,
+                     const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
+                     int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                     const int32_t* query_start, int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale,
+                     const float* sinks, float* out, int64_t ot, int64_t oh, void* stream);
 
 /* ---- D2. q8 paged-cache writer [kit] quantize_q8 (per token, head and group of 32
  * channels: scale = max(amax / 127, 1e-8) in FP32, code = x / scale (correctly

@@ -6,7 +6,7 @@ memory (output and workspace allocation) and the current HIP stream. There is no
 fallback: if the library is missing the import of any entry point raises.
 
 Functions carry the C names: ``sq_norm_stats``, ``sq_kmean``, ``sq_quant_qk``,
-``sq_quant_v_fp8``, ``sq_attn``, ``sq_attn_prefix_lse_merge``, ``sq_paged_decode``.
+``sq_quant_v_fp8``, ``sq_attn``, ``sq_attn_prefix_lse_merge``, ``sq_paged_decode``, ``sq_paged_prefill``.
 """
 from __future__ import annotations
 
@@ -73,7 +73,7 @@ ABI_VERSION = 2  # SQ_ABI_VERSION of the sq.h these argument lists follow
 EXPORTS = ["sq_scale_count", "sq_norm_stats", "sq_kmean_workspace_bytes", "sq_kmean", "sq_quant_qk_workspace_bytes",
            "sq_quant_qk", "sq_quant_v_fp8_workspace_bytes", "sq_quant_v_fp8", "sq_attn_workspace_bytes", "sq_attn",
            "sq_attn_prefix_lse_merge_workspace_bytes", "sq_attn_prefix_lse_merge", "sq_paged_decode_workspace_bytes",
-           "sq_paged_decode", "sq_q8_cache_write", "sq_lse_merge", "sq_status_string", "sq_last_error", "sq_abi_version"]
+           "sq_paged_decode", "sq_paged_prefill", "sq_q8_cache_write", "sq_lse_merge", "sq_status_string", "sq_last_error", "sq_abi_version"]
 
 
 def lib():
@@ -107,6 +107,8 @@ def lib():
         L.sq_paged_decode_workspace_bytes.restype = _sz
         L.sq_paged_decode.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
                                       _int, _int, _int, _f32, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+        L.sq_paged_prefill.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
+                                       _vp, _int, _int, _int, _int, _f32, _vp, _vp, _i64, _i64, _vp]
         L.sq_lse_merge.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                    _i64, _i64, _i64, _vp]
         L.sq_q8_cache_write.argtypes = [_vp, _vp, _int, _i64, _int, _int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
@@ -373,6 +375,28 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
                              max_seq_len, Hq, D, softmax_scale, _ptr(sinks), _ptr(out), out.stride(0), out.stride(1),
                              _ptr(ws), nb,
                              _stream(dev)))
+    return out
+
+
+def sq_paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
+                     v_scale: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                     query_start: torch.Tensor, max_seq_len: int, softmax_scale: float,
+                     out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged causal (chunked) prefill over a q8 cache. q bf16 (num_tokens, Hq, D), packed by query_start int32
+    (N + 1,); seq_lens int32 (N,) keys per sequence (context + its queries, already in the cache); caches and
+    block_table as sq_paged_decode; sinks FP32 (Hq,) or None. Returns FP32 (num_tokens, Hq, D)."""
+    T, Hq, D = q.shape
+    NB, bs, Hk, _ = k_cache.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    if sinks is not None:
+        assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == Hq, "sinks: FP32 (Hq,)"
+    L = lib()
+    _check(L.sq_paged_prefill(_ptr(q), q.stride(0), q.stride(1), T, _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                              _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+                              _ptr(query_start), seq_lens.numel(), max_seq_len, Hq, D, softmax_scale, _ptr(sinks),
+                              _ptr(out), out.stride(0), out.stride(1), _stream(dev)))
     return out
 
 

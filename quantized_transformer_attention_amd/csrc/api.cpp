@@ -444,4 +444,57 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     return launch_decode(a, stream);
 }
 
+
+// ---------------------------------------------------------------------------- D3. paged causal prefill
+int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, const int8_t* k_cache,
+                     const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
+                     int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                     const int32_t* query_start, int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale,
+                     const float* sinks, float* out, int64_t ot, int64_t oh, void* stream) {
+    clear_error();
+    const char* what = "sq_paged_prefill";
+    if (num_seqs < 0 || num_tokens < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
+        return fail(SQ_ERR_SHAPE, "%s: bad sizes (num_seqs %d, num_tokens %lld, Hq %d, Hk %d)", what, num_seqs,
+                    (long long)num_tokens, Hq, Hk);
+    if (D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", what, D);
+    if (block_size != 16) return fail(SQ_ERR_UNSUPPORTED, "%s: block_size %d (only 16)", what, block_size);
+    if (Hq % Hk) return fail(SQ_ERR_SHAPE, "%s: Hq %d not a multiple of Hk %d", what, Hq, Hk);
+    const int G = Hq / Hk;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: Hq / Hk = %d (1, 2, 4 or 8)", what, G);
+    if (num_seqs == 0 || num_tokens == 0) return SQ_OK;
+    if (max_seq_len < 1) return fail(SQ_ERR_SHAPE, "%s: max_seq_len must be >= 1", what);
+    if (num_blocks < 1) return fail(SQ_ERR_SHAPE, "%s: the cache has no blocks", what);
+    if (num_tokens >= (int64_t(1) << 31) / 2)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: %lld query tokens (fewer than 2^30)", what, (long long)num_tokens);
+    if (!q || !k_cache || !k_scale || !v_cache || !v_scale || !block_table || !seq_lens || !query_start || !out)
+        return fail(SQ_ERR_NULL, "%s: a required pointer is NULL", what);
+    if (bt_stride < (max_seq_len + block_size - 1) / block_size)
+        return fail(SQ_ERR_STRIDE, "%s: block-table rows (%lld entries) shorter than max_seq_len needs", what,
+                    (long long)bt_stride);
+    if ((reinterpret_cast<uintptr_t>(q) & 15) || qt % 8 || qh % 8 || qt < 0 || qh < 0)
+        return fail(SQ_ERR_ALIGN, "%s: q rows must start on 16-byte boundaries", what);
+    if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15))
+        return fail(SQ_ERR_ALIGN, "%s: caches must be 16-byte aligned", what);
+    if ((reinterpret_cast<uintptr_t>(k_scale) & 7) || (reinterpret_cast<uintptr_t>(v_scale) & 7))
+        return fail(SQ_ERR_ALIGN, "%s: FP16 scale rows must be 8-byte aligned", what);
+    if (ot < 0 || oh < 0) return fail(SQ_ERR_STRIDE, "%s: negative output stride", what);
+    if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+        return fail(SQ_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", what);
+    PrefillArgs a{};
+    a.q = static_cast<const uint16_t*>(q); a.qt = qt; a.qh = qh;
+    a.kc = k_cache; a.ks = k_scale; a.vc = v_cache; a.vs = v_scale;
+    a.num_blocks = num_blocks; a.Hk = Hk; a.Hq = Hq;
+    a.bt = block_table; a.bt_stride = bt_stride;
+    a.lens = seq_lens; a.qstart = query_start;
+    a.N = num_seqs; a.max_len = max_seq_len;
+    a.nqb = num_tokens / (128 / G) + num_seqs;
+    a.T = static_cast<int>(num_tokens);
+    a.scale = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);  // log2 units
+    a.sinks = sinks;
+    a.out = out; a.ot = ot; a.oh = oh;
+    if (a.nqb * Hk >= (int64_t(1) << 31)) return fail(SQ_ERR_UNSUPPORTED, "%s: too many query blocks", what);
+    return launch_prefill(a, stream);
+}
+
 }  // extern "C"

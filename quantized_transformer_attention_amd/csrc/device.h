@@ -127,6 +127,21 @@ __device__ __forceinline__ int swz(int row, int slot) {
     else return slot ^ (row & 15);
 }
 
+// 8 int8 (byte k = element k) -> 8 f16, exact: byte b ^ 0x80 = b + 128 goes under the f16
+// exponent byte 0x64 (f16 0x64uu = 1024 + uu), then 1152 comes off in packed f16
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8h_t i8x8_to_f16(uint32_t w0, uint32_t w1) {
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+    const h2_t bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    h2_t r[4];
+    r[0] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) - bias;
+    r[1] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) - bias;
+    r[2] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) - bias;
+    r[3] = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) - bias;
+    return __builtin_bit_cast(v8h_t, r);
+}
+
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
 

@@ -1,0 +1,323 @@
+// Paged causal prefill over a q8 KV cache on gfx950: varlen query chunks attend their
+// sequence's cached keys (the context) and their own, causally, GQA heads stacked.
+//
+// Method: [impl] fastkernels L2/attention_impl.py _prefill_torch_from_cache (per sequence:
+// _cache_seq gathers the keys through the block table, _sdpa_one masks k_pos <= key_offset +
+// q_pos with key_offset = k_len - q_len), laid out as [tq] vLLM
+// triton_turboquant_unified_attention.py kernel_tq_unified_attention_2d lays it out: q
+// blocks of the packed tokens found by _find_seq_idx's binary search over query_start_len,
+// the Hq / Hk query heads of a kv head stacked into one block of rows, context_len =
+// seq_len - query_len, online softmax, sinks (USE_SINKS: M = sink logit, L = 1).
+//
+// Design (one workgroup = 4 waves = 128 rows = 128 / G tokens x G heads of one kv head;
+// 64-key tiles = 4 pages):
+//  * K and V tiles are dequantized once per workgroup: the int8 codes of a slot row are
+//    widened exactly to f16 and multiplied by their FP16 group scale (one f16 rounding),
+//    then written to LDS key-major (256 bytes per key, 16-byte slots XOR-swizzled). The
+//    next tile's codes and scales are loaded into registers while the current tile is
+//    processed; the block-table entries of the tile after it are read (scalar) one step
+//    earlier still.
+//  * q is carried as f16 after an exact power-of-two rescale per row (its largest |q| in
+//    [2^14, 2^15)), undone exactly in the row's score scale.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_f16: K rows are permuted in LDS (key kappa = 16 G +
+//    4 t + i to row 16 t + 4 G + i) so that lane group g ends up holding the 16 consecutive
+//    keys [16 g, 16 g + 16) of one query row: those registers, as f16, are the A operand of
+//    P.V, whose B operand (8 keys of one channel per lane) is read from the key-major V
+//    tile by two transposing ds_read_b64_tr_b16.
+//  * causal: a workgroup reads the tiles up to its last row's end; a wave masks only the
+//    tiles that cross its rows' diagonal and skips those past its last row.
+// HBM: each (sequence, kv head) key/value row is read by every q block of the sequence
+// that sees it; the q blocks of one kv head are dealt to one XCD in a row, so most of
+// those reads hit its L2.
+#include "device.h"
+#include "sq_internal.h"
+
+namespace sq {
+namespace {
+
+constexpr int kD = 128, kBS = 16, kKT = 64, kRows = 128;
+constexpr int kNQ = 2, kNT = kKT / 16, kNC = kD / 32, kNCT = kD / 16;
+constexpr int kRowB = 2 * kD;               // one f16 key row in LDS
+constexpr int kTileB = kKT * kRowB;         // 16 KB per tile and tensor
+constexpr int kBufB = 2 * kTileB;           // K tile then V tile
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lv4s_p;
+
+// LDS row of key kappa in the K tile, and the 16-byte slot swizzles: K is read as 16 rows x one
+// slot per lane group (row & 15 spreads the 16 rows over all banks); V as 16 keys 16 g + 8 u +
+// 4 h + k (k, g = 0..3) x two slots, spread by k | g << 2.
+__device__ __forceinline__ int k_row(int kappa) { return 16 * ((kappa >> 2) & 3) + 4 * (kappa >> 4) + (kappa & 3); }
+__device__ __forceinline__ int k_slot(int row, int slot) { return slot ^ (row & 15); }
+__device__ __forceinline__ int v_slot(int key, int slot) { return slot ^ ((key & 3) | ((key >> 2) & 12)); }
+
+__device__ __forceinline__ v8h scale8(v8h x, _Float16 s) {
+    const v8h sv = {s, s, s, s, s, s, s, s};
+    return x * sv;
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
+    constexpr int BQ = kRows / G;                       // query tokens per workgroup
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufB];
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lq = l & 15, g = l >> 4;
+
+    // ---- work item: (kv head, q block); the q blocks of a kv head run on one XCD, last first
+    const int64_t items = a.nqb * a.Hk;
+    const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
+    if (item >= items) return;  // uniform over the workgroup
+    const int hk = static_cast<int>(item / a.nqb);
+    const int qblk = static_cast<int>(a.nqb - 1 - item % a.nqb);
+    // the sequence whose q blocks hold qblk: sequence n's first block is query_start[n] / BQ + n
+    int lo = 0, hi = a.N;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a.qstart[mid] / BQ + mid <= qblk) lo = mid + 1;
+        else hi = mid;
+    }
+    const int seq = lo - 1;
+    if (seq < 0) return;
+    const int qs0 = a.qstart[seq], qlen = a.qstart[seq + 1] - qs0;
+    const int local = qblk - (qs0 / BQ + seq);
+    if (local * BQ >= qlen) return;
+    const int L = min(a.lens[seq], a.max_len);
+    const int ctx = L - qlen;                           // keys before the first query
+    const int j0 = local * BQ;                          // first query (in the sequence) of the block
+    const int kv_end = min(L, ctx + min(qlen, j0 + BQ));
+    const int ntiles = (kv_end + kKT - 1) / kKT;
+    if (ntiles <= 0) return;
+    // this wave's rows are tokens j0 + 32 w / G .. j0 + (32 w + 31) / G
+    const int lo_end = min(L, ctx + j0 + (32 * w) / G + 1);
+    const int hi_end = min(L, ctx + j0 + (32 * w + 31) / G + 1);
+    const int32_t* bt = a.bt + static_cast<int64_t>(seq) * a.bt_stride;
+    const int last_page = (L - 1) / kBS;
+
+    // ---- q rows: row r = 32 w + 16 n + lq is token r / G, head r % G; per-row power-of-two rescale
+    v8h qop[kNQ][kNC];
+    float cr[kNQ], m_run[kNQ], l_run[kNQ];
+    v4f o[kNQ][kNCT];
+#pragma unroll
+    for (int n = 0; n < kNQ; ++n) {
+        const int r = 32 * w + 16 * n + lq;
+        const int j = j0 + r / G, h = hk * G + r % G;
+        const bool ok = j < qlen && qs0 + j >= 0 && qs0 + j < a.T;
+        v4u raw[kNC];
+        const uint16_t* qp = a.q + static_cast<int64_t>(qs0 + (ok ? j : 0)) * a.qt + static_cast<int64_t>(h) * a.qh;
+#pragma unroll
+        for (int c = 0; c < kNC; ++c)
+            raw[c] = ok ? *reinterpret_cast<const v4u*>(qp + 32 * c + 8 * g) : v4u{0u, 0u, 0u, 0u};
+        float f[kNC][8];
+        float mx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kNC; ++c) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[c][2 * e] = bf16_lo(raw[c][e]);
+                f[c][2 * e + 1] = bf16_hi(raw[c][e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[c][e]));
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const int sh = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+#pragma unroll
+        for (int c = 0; c < kNC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qop[n][c][e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[c][e], sh));
+        cr[n] = __builtin_amdgcn_ldexpf(a.scale, -sh);
+        m_run[n] = a.sinks ? a.sinks[h] * 1.44269504f : -__builtin_inff();
+        l_run[n] = (a.sinks && g == 0) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct) o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // ---- staging: thread tid takes 16 channels (part) of keys kappa_u = tid / 8 + 32 u of a tile;
+    // the pages of those keys are wave-uniform: tile page w / 2 and 2 + w / 2
+    const int part = tid & 7, key0 = tid >> 3;
+    const int64_t rowstride = a.Hk;                     // cache rows per slot
+    auto page_block = [&](int tile, int u) {
+        const int page = min(tile * (kKT / kBS) + 2 * u + (w >> 1), last_page);
+        const int b = bt[page];
+        return (b >= 0 && b < a.num_blocks) ? b : 0;    // a bad entry reads block 0 (no fault)
+    };
+    v4u kraw[2], vraw[2];
+    uint32_t ksr[2], vsr[2];
+    auto load_tile = [&](int blk0, int blk1) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t row = (static_cast<int64_t>(u == 0 ? blk0 : blk1) * kBS + ((key0 + 32 * u) & 15)) * rowstride + hk;
+            kraw[u] = *reinterpret_cast<const v4u*>(a.kc + row * kD + 16 * part);
+            vraw[u] = *reinterpret_cast<const v4u*>(a.vc + row * kD + 16 * part);
+            ksr[u] = a.ks[row * (kD / 32) + (part >> 1)];
+            vsr[u] = a.vs[row * (kD / 32) + (part >> 1)];
+        }
+    };
+    // keys at or past L (unused slots, clamped pages) get zero scales: their scores are masked and their
+    // values must not carry a NaN or inf of memory nobody wrote into the P.V sums
+    auto store_tile = [&](uint8_t* buf, int kbase) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int kappa = key0 + 32 * u;
+            const bool live = kbase + kappa < L;
+            const _Float16 ks = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(ksr[u])) : static_cast<_Float16>(0.0f);
+            const _Float16 vs = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsr[u])) : static_cast<_Float16>(0.0f);
+            const v8h k0 = scale8(i8x8_to_f16(kraw[u][0], kraw[u][1]), ks), k1 = scale8(i8x8_to_f16(kraw[u][2], kraw[u][3]), ks);
+            const v8h v0 = scale8(i8x8_to_f16(vraw[u][0], vraw[u][1]), vs), v1 = scale8(i8x8_to_f16(vraw[u][2], vraw[u][3]), vs);
+            const int kr = k_row(kappa);
+            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part) * 16) = k0;
+            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part + 1) * 16) = k1;
+            *reinterpret_cast<v8h*>(buf + kTileB + kappa * kRowB + v_slot(kappa, 2 * part) * 16) = v0;
+            *reinterpret_cast<v8h*>(buf + kTileB + kappa * kRowB + v_slot(kappa, 2 * part + 1) * 16) = v1;
+        }
+    };
+
+    // one tile: S^T = K Q^T, online softmax (base 2), acc += P V
+    auto tile_step = [&](const uint8_t* buf, int kbase, bool masked) {
+        v8h pf[kNQ][2];
+        float alpha[kNQ];
+        int lane = l;
+#pragma unroll
+        for (int n = 0; n < kNQ; ++n) {
+            // fresh lane offsets per n: the first tile's K reads are not kept in registers for the second
+            asm volatile("" : "+v"(lane));
+            const int klq = lane & 15, kg = lane >> 4;
+            v4f s[kNT];
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) {
+                const int row = 16 * t + klq;
+#pragma unroll
+                for (int c = 0; c < kNC; ++c) {
+                    const v8h kop = *reinterpret_cast<const v8h*>(buf + row * kRowB + k_slot(row, 4 * c + kg) * 16);
+                    s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[n][c], c == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t],
+                                                                  0, 0, 0);
+                }
+            }
+            if (masked) {
+                // keys of this lane group (16 g + 4 t + i) this row sees: below min(L, ctx + j + 1)
+                const int r = 32 * w + 16 * n + lq;
+                int nval = min(L, ctx + j0 + r / G + 1) - kbase - 16 * g;
+                asm volatile("" : "+v"(nval));
+#pragma unroll
+                for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * t + i >= nval) s[t][i] = -__builtin_inff();
+            }
+            float mt = -__builtin_inff();
+#pragma unroll
+            for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[t][i]);
+            mt = fmaxf(mt, shfl_xor(mt, 16));
+            mt = fmaxf(mt, shfl_xor(mt, 32));
+            const float mo = m_run[n];
+            const float mn = fmaxf(mo, mt * cr[n]);
+            alpha[n] = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+            m_run[n] = mn;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], cr[n], -mn));
+                    if (masked && s[t][i] == -__builtin_inff()) p = 0.0f;
+                    lsum += p;
+                    pf[n][t >> 1][4 * (t & 1) + i] = static_cast<_Float16>(p);
+                }
+            l_run[n] = l_run[n] * alpha[n] + lsum;
+        }
+        // rescale the accumulator rows (row 4 g + i of tile n) by alpha
+#pragma unroll
+        for (int n = 0; n < kNQ; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha[n], 4 * g + i, kWave);
+#pragma unroll
+                for (int ct = 0; ct < kNCT; ++ct) o[n][ct][i] *= ai;
+            }
+        // acc += P V: B operand = keys 16 g + 8 u + 4 h + k (k = lq / 4) of channels 16 ct + 4 (lq % 4) ..
+        // + 3, transposed so that lane lq receives channel 16 ct + lq of those 4 keys
+        const uint8_t* vt = buf + kTileB;
+#pragma unroll
+        for (int ct = 0; ct < kNCT; ++ct)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                v4h half[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int key = 16 * g + 8 * u + 4 * h + (lq >> 2), m = lq & 3;
+                    const uint8_t* p = vt + key * kRowB + v_slot(key, 2 * ct + (m >> 1)) * 16 + 8 * (m & 1);
+                    half[h] = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s_p)(p)));
+                }
+                const v8h vop = {half[0][0], half[0][1], half[0][2], half[0][3], half[1][0], half[1][1], half[1][2], half[1][3]};
+#pragma unroll
+                for (int n = 0; n < kNQ; ++n)
+                    o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], vop, o[n][ct], 0, 0, 0);
+            }
+    };
+
+    // ---- key loop: tile j is processed from buffer j % 2 while tile j + 1's codes are in flight;
+    // the table entries of tile j + 2 are read meanwhile
+    int nb0 = page_block(0, 0), nb1 = page_block(0, 1);
+    load_tile(nb0, nb1);
+    nb0 = page_block(min(1, ntiles - 1), 0);
+    nb1 = page_block(min(1, ntiles - 1), 1);
+    store_tile(lds, 0);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        uint8_t* cur = lds + (j & 1) * kBufB;
+        uint8_t* nxt = lds + ((j + 1) & 1) * kBufB;
+        load_tile(nb0, nb1);                            // tile j + 1 (the last tile again past the end)
+        const int t2 = min(j + 2, ntiles - 1);
+        nb0 = page_block(t2, 0);
+        nb1 = page_block(t2, 1);
+        __builtin_amdgcn_sched_barrier(0);              // the loads go out before the tile's arithmetic
+        const int kbase = j * kKT;
+        if (kbase < hi_end) tile_step(cur, kbase, kbase + kKT > lo_end);
+        store_tile(nxt, (j + 1) * kKT);
+        __syncthreads();
+    }
+
+    // ---- epilogue: l over the 4 lane groups, out = acc / l
+#pragma unroll
+    for (int n = 0; n < kNQ; ++n) {
+        float lt = l_run[n];
+        lt = lt + shfl_xor(lt, 16);
+        lt = lt + shfl_xor(lt, 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float inv = 1.0f / __shfl(lt, 4 * g + i, kWave);
+            const int r = 32 * w + 16 * n + 4 * g + i;
+            const int j = j0 + r / G;
+            if (j >= qlen || qs0 + j < 0 || qs0 + j >= a.T) continue;
+            float* op = a.out + static_cast<int64_t>(qs0 + j) * a.ot + static_cast<int64_t>(hk * G + r % G) * a.oh;
+#pragma unroll
+            for (int ct = 0; ct < kNCT; ++ct) op[16 * ct + lq] = o[n][ct][i] * inv;
+        }
+    }
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillArgs& a, void* stream) {
+    const int64_t items = a.nqb * a.Hk;
+    if (items == 0) return SQ_OK;
+    dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (a.Hq / a.Hk) {
+        case 1: hipLaunchKernelGGL(k_paged_prefill<1>, grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(k_paged_prefill<2>, grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(k_paged_prefill<4>, grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(k_paged_prefill<8>, grid, dim3(256), 0, s, a); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_paged_prefill: kernel launch failed: %s", hipGetErrorString(e));
+    return SQ_OK;
+}
+
+}  // namespace sq

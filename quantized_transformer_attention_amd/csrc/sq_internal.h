@@ -180,6 +180,28 @@ struct DecodeArgs {
     int segs;                   // segments per sequence: ceil(max_len / kDecodeSeg)
 };
 
+struct PrefillArgs {
+    const uint16_t* q;          // bf16 (T, Hq, D) at q[t*qt + h*qh + c]
+    int64_t qt, qh;
+    const int8_t* kc;
+    const uint16_t* ks;
+    const int8_t* vc;
+    const uint16_t* vs;
+    int64_t num_blocks;
+    int Hk, Hq;
+    const int32_t* bt;
+    int64_t bt_stride;
+    const int32_t* lens;        // keys per sequence (context + its queries)
+    const int32_t* qstart;      // (N + 1,) first query token of each sequence
+    int N, max_len;
+    int64_t nqb;                // q blocks: num_tokens / rows-per-block + N (an upper bound)
+    int T;                      // num_tokens: rows outside [0, T) are neither read nor written
+    float scale;                // softmax_scale * log2 e
+    const float* sinks;         // (Hq,) sink logits in natural-log units, or NULL
+    float* out;
+    int64_t ot, oh;
+};
+
 // ---------------------------------------------------------------- launchers (*.hip)
 int launch_norm_stats(const NormStatsArgs& a, void* stream);
 int launch_kmean(const KmeanArgs& a, void* stream);
@@ -191,6 +213,7 @@ int launch_prefix(const PrefixArgs& a, void* stream);
 int launch_lse_merge(const MergeArgs& a, void* stream);
 int launch_cache_write(const CacheWriteArgs& a, bool f32, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
+int launch_prefill(const PrefillArgs& a, void* stream);
 
 // ---------------------------------------------------------------- validation (validate.cpp)
 int check_rows(const sq_rows* x, const char* what);

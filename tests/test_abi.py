@@ -149,3 +149,27 @@ def test_lse_merge_validation_errors():
     assert _call_merge(lh=-1) == -3
     assert _call_merge(out=0x1004) == -4                    # rows 16-byte aligned
     assert _call_merge(oh=130) == -4
+
+
+def _call_prefill(T=10, NB=4, bs=16, Hk=2, Hq=8, D=128, q=0x1000, qt=1024, qh=128, kc=0x2000, ks=0x3000, vc=0x4000,
+                  vs=0x5000, bt=0x6000, bts=4, lens=0x7000, qs=0x8000, N=2, max_len=64, scale=0.125, out=0x9000):
+    L = sq.lib()
+    return L.sq_paged_prefill(q, qt, qh, T, kc, ks, vc, vs, NB, bs, Hk, bt, bts, lens, qs, N, max_len, Hq, D, scale,
+                              None, out, Hq * D, D, None)
+
+
+def test_paged_prefill_validation_errors():
+    assert _call_prefill(D=64) == -5                       # head dim 128 only
+    assert _call_prefill(bs=32) == -5                      # block size 16 only
+    assert _call_prefill(Hq=6, Hk=4) == -2                 # heads not a multiple
+    assert _call_prefill(Hq=32, Hk=2) == -5                # Hq / Hk = 16
+    assert _call_prefill(T=0, q=None) == 0                 # no tokens: nothing read
+    assert _call_prefill(N=0, q=None) == 0
+    assert _call_prefill(NB=0) == -2                       # the queries' keys live in the cache
+    assert _call_prefill(max_len=0) == -2
+    assert _call_prefill(qs=None) == -1
+    assert _call_prefill(bts=3) == -3                      # table rows shorter than max_len needs
+    assert _call_prefill(q=0x1008) == -4
+    assert _call_prefill(qh=132) == -4
+    assert _call_prefill(ks=0x3002) == -4
+    assert _call_prefill(scale=0.0) == -2
