@@ -488,7 +488,7 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
     a.bt = block_table; a.bt_stride = bt_stride;
     a.lens = seq_lens; a.qstart = query_start;
     a.N = num_seqs; a.max_len = max_seq_len;
-    a.nqb = num_tokens / (128 / G) + num_seqs;
+    a.nqb = num_tokens / (32 * kPrefillWaves / G) + num_seqs;
     a.T = static_cast<int>(num_tokens);
     a.scale = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);  // log2 units
     a.sinks = sinks;

@@ -9,7 +9,7 @@
 // the Hq / Hk query heads of a kv head stacked into one block of rows, context_len =
 // seq_len - query_len, online softmax, sinks (USE_SINKS: M = sink logit, L = 1).
 //
-// Design (one workgroup = 4 waves = 128 rows = 128 / G tokens x G heads of one kv head;
+// Design (one workgroup = NW waves = 32 NW rows = 32 NW / G tokens x G heads of one kv head;
 // 64-key tiles = 4 pages):
 //  * K and V tiles are dequantized once per workgroup: the int8 codes of a slot row are
 //    widened exactly to f16 and multiplied by their FP16 group scale (one f16 rounding),
@@ -26,6 +26,9 @@
 //    tile by two transposing ds_read_b64_tr_b16.
 //  * causal: a workgroup reads the tiles up to its last row's end; a wave masks only the
 //    tiles that cross its rows' diagonal and skips those past its last row.
+//  * the reference max of a row trails its running max by at most 8 (base 2): the
+//    accumulator is rescaled only when a tile raises some row's max beyond that, so p <= 2^8
+//    (the f16 P rounds relative to itself whatever the reference; l and acc are FP32).
 // HBM: each (sequence, kv head) key/value row is read by every q block of the sequence
 // that sees it; the q blocks of one kv head are dealt to one XCD in a row, so most of
 // those reads hit its L2.
@@ -35,7 +38,8 @@
 namespace sq {
 namespace {
 
-constexpr int kD = 128, kBS = 16, kKT = 64, kRows = 128;
+constexpr int kD = 128, kBS = 16, kKT = 64;
+constexpr float kLag = 8.0f;                // how far a row's reference max may trail its max
 constexpr int kNQ = 2, kNT = kKT / 16, kNC = kD / 32, kNCT = kD / 16;
 constexpr int kRowB = 2 * kD;               // one f16 key row in LDS
 constexpr int kTileB = kKT * kRowB;         // 16 KB per tile and tensor
@@ -60,9 +64,11 @@ __device__ __forceinline__ v8h scale8(v8h x, _Float16 s) {
     return x * sv;
 }
 
-template <int G>
-__global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
+template <int G, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a) {
+    constexpr int kRows = 32 * NW;                      // rows per workgroup
     constexpr int BQ = kRows / G;                       // query tokens per workgroup
+    constexpr int U = 8 / NW;                           // 16-byte K (and V) chunks per thread and tile
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufB];
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lq = l & 15, g = l >> 4;
 
@@ -93,7 +99,10 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
     // this wave's rows are tokens j0 + 32 w / G .. j0 + (32 w + 31) / G
     const int lo_end = min(L, ctx + j0 + (32 * w) / G + 1);
     const int hi_end = min(L, ctx + j0 + (32 * w + 31) / G + 1);
-    const int32_t* bt = a.bt + static_cast<int64_t>(seq) * a.bt_stride;
+    // the block table is read through the constant address space: its wave-uniform reads become scalar
+    // loads, whose counter is not the one the code loads are waited on with
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    const cint32* bt = reinterpret_cast<const cint32*>(reinterpret_cast<uintptr_t>(a.bt + static_cast<int64_t>(seq) * a.bt_stride));
     const int last_page = (L - 1) / kBS;
 
     // ---- q rows: row r = 32 w + 16 n + lq is token r / G, head r % G; per-row power-of-two rescale
@@ -136,21 +145,21 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
         for (int ct = 0; ct < kNCT; ++ct) o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // ---- staging: thread tid takes 16 channels (part) of keys kappa_u = tid / 8 + 32 u of a tile;
-    // the pages of those keys are wave-uniform: tile page w / 2 and 2 + w / 2
+    // ---- staging: thread tid takes 16 channels (part) of keys kappa_u = tid / 8 + 8 NW u of a tile;
+    // the pages of those keys are wave-uniform: tile page w / 2 + NW u / 2
     const int part = tid & 7, key0 = tid >> 3;
     const int64_t rowstride = a.Hk;                     // cache rows per slot
     auto page_block = [&](int tile, int u) {
-        const int page = min(tile * (kKT / kBS) + 2 * u + (w >> 1), last_page);
+        const int page = __builtin_amdgcn_readfirstlane(min(tile * (kKT / kBS) + (NW / 2) * u + (w >> 1), last_page));
         const int b = bt[page];
         return (b >= 0 && b < a.num_blocks) ? b : 0;    // a bad entry reads block 0 (no fault)
     };
-    v4u kraw[2], vraw[2];
-    uint32_t ksr[2], vsr[2];
-    auto load_tile = [&](int blk0, int blk1) {
+    v4u kraw[U], vraw[U];
+    uint32_t ksr[U], vsr[U];
+    auto load_tile = [&](const int* blk) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int64_t row = (static_cast<int64_t>(u == 0 ? blk0 : blk1) * kBS + ((key0 + 32 * u) & 15)) * rowstride + hk;
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = (static_cast<int64_t>(blk[u]) * kBS + ((key0 + 8 * NW * u) & 15)) * rowstride + hk;
             kraw[u] = *reinterpret_cast<const v4u*>(a.kc + row * kD + 16 * part);
             vraw[u] = *reinterpret_cast<const v4u*>(a.vc + row * kD + 16 * part);
             ksr[u] = a.ks[row * (kD / 32) + (part >> 1)];
@@ -161,13 +170,14 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
     // values must not carry a NaN or inf of memory nobody wrote into the P.V sums
     auto store_tile = [&](uint8_t* buf, int kbase) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int kappa = key0 + 32 * u;
+        for (int u = 0; u < U; ++u) {
+            const int kappa = key0 + 8 * NW * u;
             const bool live = kbase + kappa < L;
             const _Float16 ks = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(ksr[u])) : static_cast<_Float16>(0.0f);
             const _Float16 vs = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsr[u])) : static_cast<_Float16>(0.0f);
-            const v8h k0 = scale8(i8x8_to_f16(kraw[u][0], kraw[u][1]), ks), k1 = scale8(i8x8_to_f16(kraw[u][2], kraw[u][3]), ks);
-            const v8h v0 = scale8(i8x8_to_f16(vraw[u][0], vraw[u][1]), vs), v1 = scale8(i8x8_to_f16(vraw[u][2], vraw[u][3]), vs);
+            const v4u kr4 = kraw[u], vr4 = vraw[u];
+            const v8h k0 = scale8(i8x8_to_f16(kr4[0], kr4[1]), ks), k1 = scale8(i8x8_to_f16(kr4[2], kr4[3]), ks);
+            const v8h v0 = scale8(i8x8_to_f16(vr4[0], vr4[1]), vs), v1 = scale8(i8x8_to_f16(vr4[2], vr4[3]), vs);
             const int kr = k_row(kappa);
             *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part) * 16) = k0;
             *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part + 1) * 16) = k1;
@@ -179,7 +189,6 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
     // one tile: S^T = K Q^T, online softmax (base 2), acc += P V
     auto tile_step = [&](const uint8_t* buf, int kbase, bool masked) {
         v8h pf[kNQ][2];
-        float alpha[kNQ];
         int lane = l;
 #pragma unroll
         for (int n = 0; n < kNQ; ++n) {
@@ -215,31 +224,36 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
                 for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[t][i]);
             mt = fmaxf(mt, shfl_xor(mt, 16));
             mt = fmaxf(mt, shfl_xor(mt, 32));
-            const float mo = m_run[n];
-            const float mn = fmaxf(mo, mt * cr[n]);
-            alpha[n] = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-            m_run[n] = mn;
+            const float ms = mt * cr[n];
+            // the reference max moves (and the accumulator rows with it) only when some row of the
+            // wave would see p > 2^kLag against it
+            if (__builtin_amdgcn_ballot_w64(ms > m_run[n] + kLag) != 0) {
+                const float mo = m_run[n];
+                const float mn = fmaxf(mo, ms);
+                const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+                m_run[n] = mn;
+                l_run[n] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+                    for (int ct = 0; ct < kNCT; ++ct) o[n][ct][i] *= ai;
+                }
+            }
+            // every row sees key 0 in the first tile, so mref is finite from there on and a masked
+            // score (-inf) gives p = 2^-inf = 0 exactly
+            const float mref = m_run[n];
             float lsum = 0.0f;
 #pragma unroll
             for (int t = 0; t < kNT; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], cr[n], -mn));
-                    if (masked && s[t][i] == -__builtin_inff()) p = 0.0f;
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], cr[n], -mref));
                     lsum += p;
                     pf[n][t >> 1][4 * (t & 1) + i] = static_cast<_Float16>(p);
                 }
-            l_run[n] = l_run[n] * alpha[n] + lsum;
+            l_run[n] += lsum;
         }
-        // rescale the accumulator rows (row 4 g + i of tile n) by alpha
-#pragma unroll
-        for (int n = 0; n < kNQ; ++n)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha[n], 4 * g + i, kWave);
-#pragma unroll
-                for (int ct = 0; ct < kNCT; ++ct) o[n][ct][i] *= ai;
-            }
         // acc += P V: B operand = keys 16 g + 8 u + 4 h + k (k = lq / 4) of channels 16 ct + 4 (lq % 4) ..
         // + 3, transposed so that lane lq receives channel 16 ct + lq of those 4 keys
         const uint8_t* vt = buf + kTileB;
@@ -263,19 +277,21 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill(PrefillArgs a) {
 
     // ---- key loop: tile j is processed from buffer j % 2 while tile j + 1's codes are in flight;
     // the table entries of tile j + 2 are read meanwhile
-    int nb0 = page_block(0, 0), nb1 = page_block(0, 1);
-    load_tile(nb0, nb1);
-    nb0 = page_block(min(1, ntiles - 1), 0);
-    nb1 = page_block(min(1, ntiles - 1), 1);
+    int nb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) nb[u] = page_block(0, u);
+    load_tile(nb);
+#pragma unroll
+    for (int u = 0; u < U; ++u) nb[u] = page_block(min(1, ntiles - 1), u);
     store_tile(lds, 0);
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
         uint8_t* cur = lds + (j & 1) * kBufB;
         uint8_t* nxt = lds + ((j + 1) & 1) * kBufB;
-        load_tile(nb0, nb1);                            // tile j + 1 (the last tile again past the end)
+        load_tile(nb);                                  // tile j + 1 (the last tile again past the end)
         const int t2 = min(j + 2, ntiles - 1);
-        nb0 = page_block(t2, 0);
-        nb1 = page_block(t2, 1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) nb[u] = page_block(t2, u);
         __builtin_amdgcn_sched_barrier(0);              // the loads go out before the tile's arithmetic
         const int kbase = j * kKT;
         if (kbase < hi_end) tile_step(cur, kbase, kbase + kKT > lo_end);
@@ -308,12 +324,13 @@ int launch_prefill(const PrefillArgs& a, void* stream) {
     const int64_t items = a.nqb * a.Hk;
     if (items == 0) return SQ_OK;
     dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
+    const dim3 block(64 * kPrefillWaves);
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (a.Hq / a.Hk) {
-        case 1: hipLaunchKernelGGL(k_paged_prefill<1>, grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_paged_prefill<2>, grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(k_paged_prefill<4>, grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL(k_paged_prefill<8>, grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_paged_prefill<1, kPrefillWaves>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_paged_prefill<2, kPrefillWaves>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_paged_prefill<4, kPrefillWaves>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_paged_prefill<8, kPrefillWaves>), grid, block, 0, s, a); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_paged_prefill: kernel launch failed: %s", hipGetErrorString(e));

@@ -214,6 +214,7 @@ int launch_lse_merge(const MergeArgs& a, void* stream);
 int launch_cache_write(const CacheWriteArgs& a, bool f32, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_prefill(const PrefillArgs& a, void* stream);
+constexpr int kPrefillWaves = 8;            // waves per prefill workgroup (32 rows each)
 
 // ---------------------------------------------------------------- validation (validate.cpp)
 int check_rows(const sq_rows* x, const char* what);
