@@ -352,6 +352,24 @@ def sq_attn_prefix_lse_merge(q: QK, prefix: Q8Prefix, k_mean: Optional[torch.Ten
     return out, lse
 
 
+
+def _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, query_start=None):
+    """Host-side dtype and layout checks of the paged entry points' tensors (the C ABI takes raw pointers)."""
+    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.stride(2) == 1, "q: bf16 (tokens, Hq, D), channels contiguous"
+    for c in (k_cache, v_cache):
+        assert c.dtype == torch.int8 and c.dim() == 4 and c.is_contiguous(), "caches: contiguous int8 [NB, bs, Hk, D]"
+    for sc in (k_scale, v_scale):
+        assert sc.dtype == torch.float16 and sc.dim() == 4 and sc.is_contiguous(), \
+            "cache scales: contiguous FP16 [NB, bs, Hk, D/32]"
+    assert v_cache.shape == k_cache.shape and k_scale.shape == v_scale.shape == k_cache.shape[:3] + (k_cache.shape[3] // 32,)
+    assert block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.stride(1) == 1, \
+        "block_table: int32 (num_seqs, max_blocks), rows contiguous"
+    assert seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens: contiguous int32 (num_seqs,)"
+    if query_start is not None:
+        assert query_start.dtype == torch.int32 and query_start.is_contiguous() and \
+            query_start.numel() == seq_lens.numel() + 1, "query_start: contiguous int32 (num_seqs + 1,)"
+
+
 def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
                     v_scale: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                     softmax_scale: float, out: Optional[torch.Tensor] = None,
@@ -359,6 +377,7 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
     """Paged GQA decode over a q8 cache. q bf16 (N, Hq, D); caches int8 [NB, bs, Hk, D] with FP16 scales
     [NB, bs, Hk, D/32]; block_table int32 (N, max_blocks); seq_lens int32 (N,); sinks FP32 (Hq,) per-head sink
     logits (natural log) or None. Returns FP32 (N, Hq, D)."""
+    _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens)
     N, Hq, D = q.shape
     NB, bs, Hk, _ = k_cache.shape
     dev = q.device
@@ -385,6 +404,7 @@ def sq_paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tens
     """Paged causal (chunked) prefill over a q8 cache. q bf16 (num_tokens, Hq, D), packed by query_start int32
     (N + 1,); seq_lens int32 (N,) keys per sequence (context + its queries, already in the cache); caches and
     block_table as sq_paged_decode; sinks FP32 (Hq,) or None. Returns FP32 (num_tokens, Hq, D)."""
+    _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, query_start)
     T, Hq, D = q.shape
     NB, bs, Hk, _ = k_cache.shape
     dev = q.device

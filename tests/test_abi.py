@@ -173,3 +173,27 @@ def test_paged_prefill_validation_errors():
     assert _call_prefill(qh=132) == -4
     assert _call_prefill(ks=0x3002) == -4
     assert _call_prefill(scale=0.0) == -2
+
+
+def test_paged_bindings_reject_wrong_dtypes():
+    """The Python binding checks the paged entry points' tensors before any library call (CPU tensors suffice):
+    int64 lengths or a float32 q would otherwise be read as int32 / bf16 by the kernels."""
+    import torch
+    q = torch.zeros((3, 8, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((4, 16, 2, 128), dtype=torch.int8)
+    ks = torch.zeros((4, 16, 2, 4), dtype=torch.float16)
+    bt = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.tensor([5, 9], dtype=torch.int32)
+    qs = torch.tensor([0, 1, 3], dtype=torch.int32)
+    cases = [
+        dict(q=q.float()), dict(kc=kc.to(torch.int16)), dict(ks=ks.float()), dict(bt=bt.long()),
+        dict(lens=lens.long()), dict(qs=qs.long()), dict(qs=qs[:2]),
+    ]
+    for bad in cases:
+        a = dict(q=q, kc=kc, ks=ks, bt=bt, lens=lens, qs=qs)
+        a.update(bad)
+        with pytest.raises(AssertionError):
+            sq.sq_paged_prefill(a["q"], a["kc"], a["ks"], a["kc"], a["ks"], a["bt"], a["lens"], a["qs"], 64, 0.125)
+        if "qs" not in bad:
+            with pytest.raises(AssertionError):
+                sq.sq_paged_decode(a["q"], a["kc"], a["ks"], a["kc"], a["ks"], a["bt"], a["lens"], 64, 0.125)
