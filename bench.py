@@ -482,17 +482,28 @@ def cpu_baseline_video(args):
                                                                                        dtype=np.uint8) << 7)
     vs = np.full((1, c.H, c.D), 0.01, np.float32)
     q, k = O.QK(qc, qs, 1, 32), O.QK(kc, ks, 2, 64)
-    rows_done, t_used, chunk = 0, 0.0, 8
-    while t_used < args.cpu_seconds and rows_done < c.Sq:
-        rows = np.arange(rows_done, rows_done + chunk, dtype=np.int64)
-        t0 = time.perf_counter()
-        O.attn(q, k, v8, True, vs, kv_tile=c.kv_tile, rows=rows, want_allow=False)
-        t_used += time.perf_counter() - t0
-        rows_done += chunk
+
+    def timed(seconds, chunk):
+        rows_done, t_used = 0, 0.0
+        while t_used < seconds and rows_done < c.Sq:
+            rows = np.arange(rows_done, rows_done + chunk, dtype=np.int64)
+            t0 = time.perf_counter()
+            O.attn(q, k, v8, True, vs, kv_tile=c.kv_tile, rows=rows, want_allow=False)
+            t_used += time.perf_counter() - t0
+            rows_done += chunk
+        return rows_done, t_used
+
+    cores = O.num_threads()
+    rows_done, t_used = timed(args.cpu_seconds, 8)
+    O.set_num_threads(1)                      # the same oracle on one core, a shorter sample
+    rows_1, t_1 = timed(args.cpu_seconds / 3, 1)
+    O.set_num_threads(cores)
     flops = 4.0 * rows_done * c.H * c.Sk * c.D
-    return {"value": flops / t_used / 1e12, "unit": "TFLOPS", "cores": O.num_threads(), "kind": "oracle",
+    return {"value": flops / t_used / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
             "sample": "quantized core (INT8 Q.K^T, FP32 softmax, FP8 P.V) on %d query rows x 40 heads x 32760 keys "
-                      "of the video workload, %.1f s" % (rows_done, t_used)}
+                      "of the video workload, %.1f s" % (rows_done, t_used),
+            "value_1core": 4.0 * rows_1 * c.H * c.Sk * c.D / t_1 / 1e12,
+            "sample_1core": "%d query rows on one thread, %.1f s" % (rows_1, t_1)}
 
 
 # ---------------------------------------------------------------------------------------------- main

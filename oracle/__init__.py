@@ -74,6 +74,7 @@ def _declare(L):
     L.orc_f32_to_e4m3.argtypes, L.orc_f32_to_e4m3.restype = [_f32], ctypes.c_uint8
     L.orc_e4m3_value.argtypes, L.orc_e4m3_value.restype = [ctypes.c_uint8], _f64
     L.orc_num_threads.restype = _int
+    L.orc_set_num_threads.argtypes = [_int]
     L.orc_mean_sq_all_heads.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp]
     L.orc_prologue_rows.argtypes = [P(_Rows), _vp]
     L.orc_kmean.argtypes = [P(_Rows), _vp]
@@ -103,6 +104,10 @@ def _p(a):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------------------- formats

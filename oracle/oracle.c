@@ -127,6 +127,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* threads of the OpenMP loops from now on (timing of the oracle on one core and on all) */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------------
  * Row prologue [quant] _rows: weighted RMSNorm in FP32 rounded to bf16, RoPE in
  * FP32 with one fused multiply-add per channel, minus the head mean, times the
