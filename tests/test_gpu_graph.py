@@ -41,6 +41,7 @@ def _step(c, t):
     nq = sq.Norm(sq.NORM_HEAD, t["wq"], None, None, c.eps)
     nk = sq.Norm(sq.NORM_HEAD, t["wk"], None, None, c.eps)
     r = sq.Rope(sq.ROPE_SPLIT_HALF, t["table"])
+    ms = sq.sq_norm_stats(t["k"])
     mu = sq.sq_kmean(t["k"], nk, r)
     q = sq.sq_quant_qk(t["q"], nq, r, None, gen.sm_scale_q(c.D), 1e-7, sq.LAYOUT_PER_BLOCK, 64)
     k = sq.sq_quant_qk(t["k"], nk, r, mu, 1.0, 1e-7, sq.LAYOUT_PER_BLOCK, 64)
@@ -54,7 +55,7 @@ def _step(c, t):
     od = sq.sq_paged_decode(t["qd"], t["kc"], t["ks"], t["vc"], t["vs"], t["bt"], t["lens"], 37, 1.0 / np.sqrt(128))
     op = sq.sq_paged_prefill(t["qp"], t["kc"], t["ks"], t["vc"], t["vs"], t["bt"], t["lens"], t["qs"], 37,
                              1.0 / np.sqrt(128))
-    return [mu, q.codes, q.scales, k.codes, k.scales, v8, vs, o1, l1, o2, l2, om, lm, t["kc"], t["ks"], od, op]
+    return [ms, mu, q.codes, q.scales, k.codes, k.scales, v8, vs, o1, l1, o2, l2, om, lm, t["kc"], t["ks"], od, op]
 
 
 def _bits(x):
@@ -83,5 +84,5 @@ def test_whole_path_replays_in_a_hip_graph():
             assert np.array_equal(a, _bits(b)), "replay %d differs from eager in output %d" % (rep, i)
         # eager work between replays: other kernels on the same stream, and a synchronisation
         scratch.normal_()
-        sq.sq_norm_stats(t["q"])
+        sq.sq_quant_v_fp8(t["v"])
         torch.cuda.synchronize()
