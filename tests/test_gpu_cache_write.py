@@ -128,3 +128,15 @@ def test_cache_write_then_decode():
     got = host(out).astype(np.float64)
     rms = float(np.sqrt(np.mean(ref * ref)))
     assert np.abs(got - ref).max() <= 2e-3 * rms
+
+
+def test_cache_write_at_size():
+    """The benchmarked shape: 131072 new bf16 tokens (Hk 8, d 128) scattered to a random permutation of the slots
+    of an 8192 x 16 block cache; every code, scale and untouched row compared bit for bit."""
+    n, Hk, D, NB, bs = 131072, 8, 128, 8192, 16
+    g = gen.rng(2500, 1)
+    kb, kf = _bf16_rows((n, Hk, D), g, 1.0)
+    vb, vf = _bf16_rows((n, Hk, D), g, 1.0)
+    slots = g.permutation(NB * bs)[:n].astype(np.int64)
+    print("cache write at size n %d" % n, flush=True)
+    _run(kb, vb, kf, vf, slots, NB, bs, False, 9)

@@ -36,6 +36,35 @@ def test_lse_merge_parity(B, S, H, D):
     assert (l[~fin] == -np.inf).all()
 
 
+def test_lse_merge_at_size_sampled_rows():
+    """The benchmarked shape (two video-size outputs, B=1 Sq=32760 H=40 d=128, FP32), with empty sets on some
+    queries; 1024 sampled queries (all heads) against the oracle, every other query checked to be a convex
+    combination of its two inputs."""
+    B, S, H, D = 1, 32760, 40, 128
+    g = gen.rng(3100, 0)
+    out = g.standard_normal((B, S, H, D), dtype=np.float32)
+    other = g.standard_normal((B, S, H, D), dtype=np.float32) * np.float32(3)
+    lse = (g.standard_normal((B, H, S), dtype=np.float32) * np.float32(8))
+    olse = (g.standard_normal((B, H, S), dtype=np.float32) * np.float32(8))
+    olse[:, :, 5::997] = -np.inf
+    lse[:, :, 7::991] = -np.inf
+    rows = np.unique(np.concatenate([g.integers(0, S, size=1000), [0, 5, 7, S - 1]]))
+    ref, rlse = O.lse_merge(out[:, rows], lse[:, :, rows], other[:, rows], olse[:, :, rows])
+    d_out, d_lse = dev(out), dev(lse)
+    print("merge at size B %d S %d H %d D %d" % (B, S, H, D), flush=True)
+    sq.sq_lse_merge(d_out, d_lse, dev(other), dev(olse))
+    torch.cuda.synchronize()
+    o = host(d_out)
+    l = host(d_lse)
+    np.testing.assert_allclose(o[:, rows], ref, rtol=0, atol=1e-5 * float(np.abs(ref).max()))
+    fin = np.isfinite(rlse)
+    np.testing.assert_allclose(l[:, :, rows][fin], rlse[fin], rtol=0, atol=1e-5)
+    # every query: each channel lies between its two inputs (a convex combination), within rounding
+    lo = np.minimum(out, other) - 1e-5
+    hi = np.maximum(out, other) + 1e-5
+    assert ((o >= lo) & (o <= hi)).all()
+
+
 def test_native_prefix_attention():
     c = gen.CFG1
     inp = gen.attn_inputs(c)
