@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SQ_ABI_VERSION 2
+#define SQ_ABI_VERSION 3
 
 enum {
     SQ_OK = 0,
@@ -215,8 +215,10 @@ int sq_quant_v_fp8(const sq_rows* v, uint8_t* codes, int64_t ob, int64_t oh, int
  * or acc * vs / (256 l) (FP8 v); lse = m + log2 l (base 2, the scores' log2 units).
  * q rows carry the softmax scale (log2(e)/sqrt(D) through sm_scale). q layouts:
  * PER_BLOCK, THREAD_Q, WARP_Q; k layouts: PER_BLOCK, THREAD_K. kv_tile: 64 or 128
- * (FP8 P.V: 128). out FP32 (B, Sq, H, D) at out[b*ob + i*ot + h*oh + c]; lse FP32
- * (B, H, Sq) at lse[b*lb + h*lh + i], or NULL.
+ * (FP8 P.V: 128). out (B, Sq, H, D) at out[b*ob + i*ot + h*oh + c] in elements of
+ * out_dtype: SQ_F32, or SQ_BF16 (the FP32 result rounded to nearest even; an option for
+ * callers that keep activations in bf16), aligned to its element size (SQ_ERR_ALIGN;
+ * another dtype SQ_ERR_UNSUPPORTED); lse FP32 (B, H, Sq) at lse[b*lb + h*lh + i], or NULL.
  * causal (0 or 1) [impl] _sdpa_one's mask, [tq] unified attention's causal mask:
  * query i sits at key position i + Sk - Sq (its context is the Sk - Sq keys before
  * the queries) and sees keys 0 .. i + Sk - Sq; needs Sk >= Sq (SQ_ERR_SHAPE).
@@ -226,8 +228,8 @@ int sq_quant_v_fp8(const sq_rows* v, uint8_t* codes, int64_t ob, int64_t oh, int
  * are merged (sq_lse_merge, sq_attn_prefix_lse_merge), give the sinks to one only. */
 size_t sq_attn_workspace_bytes(const sq_qk* q, const sq_qk* k, const sq_values* v);
 int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scale, int kv_tile, int causal,
-            const float* sinks, float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh,
-            void* ws, size_t ws_bytes, void* stream);
+            const float* sinks, void* out, sq_dtype out_dtype, int64_t ob, int64_t ot, int64_t oh, float* lse,
+            int64_t lb, int64_t lh, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- C. q8 prefix pass + log-sum-exp merge [kit] _attend_with_prefix,
  * dequantize_q8_into, _merge_lse_. The same q codes attend the prefix keys in a
@@ -265,7 +267,8 @@ int sq_lse_merge(float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int
  * pos lives in physical block block_table[n*bt_stride + pos / block_size], slot
  * pos % block_size. Caches [num_blocks, block_size, Hk, D] int8 (contiguous), FP16
  * scales [num_blocks, block_size, Hk, D/32]; keys and values are code * scale.
- * Softmax of (q . k) * softmax_scale; out FP32 (N, Hq, D) at out[n*on + h*oh + c].
+ * Softmax of (q . k) * softmax_scale; out (N, Hq, D) at out[n*on + h*oh + c] in elements
+ * of out_dtype (SQ_F32, or SQ_BF16 rounded to nearest even, as sq_attn).
  * max_seq_len is a host bound for the workspace and the grid (no device read).
  * block_size 16; D 128; Hq / Hk in {1, 2, 4, 8}. q 16-byte aligned rows, caches
  * 16-byte aligned, scale tensors 8-byte aligned (one row of 4 FP16 per slot and head).
@@ -279,8 +282,8 @@ size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_
 int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
                     const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
-                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, float* out, int64_t on,
-                    int64_t oh, void* ws, size_t ws_bytes, void* stream);
+                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
+                    sq_dtype out_dtype, int64_t on, int64_t oh, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- D3. Paged causal prefill over a q8 cache [impl] _prefill_torch_from_cache,
  * _cache_seq, _sdpa_one (per sequence, mask k_pos <= key_offset + q_pos); [tq] unified
@@ -293,7 +296,8 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
  * sq_q8_cache_write; q_len <= L <= max_seq_len). Its query j sits at position L - q_len + j
  * and attends positions 0 .. L - q_len + j. Caches, scales, block table and softmax_scale
  * as sq_paged_decode (block_size 16, D 128, Hq / Hk in {1, 2, 4, 8}); sinks NULL or FP32
- * (Hq,). out FP32 (num_tokens, Hq, D) at out[t*ot + h*oh + c]. Both products run on f16
+ * (Hq,). out (num_tokens, Hq, D) at out[t*ot + h*oh + c] in elements of out_dtype (SQ_F32,
+ * or SQ_BF16 rounded to nearest even, as sq_attn). Both products run on f16
  * matrix units with FP32 accumulation: q as f16 after an exact power-of-two rescale per
  * (token, head), keys and values dequantized to f16 (code * scale rounded once), P as f16
  * (relative rounding <= 2^-11 each); cached keys and values must stay below 65504 in
@@ -303,7 +307,7 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
                      const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
                      int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                      const int32_t* query_start, int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale,
-                     const float* sinks, float* out, int64_t ot, int64_t oh, void* stream);
+                     const float* sinks, void* out, sq_dtype out_dtype, int64_t ot, int64_t oh, void* stream);
 
 /* ---- D2. q8 paged-cache writer [kit] quantize_q8 (per token, head and group of 32
  * channels: scale = max(amax / 127, 1e-8) in FP32, code = x / scale (correctly

@@ -68,7 +68,7 @@ class sq_q8prefix(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 2  # SQ_ABI_VERSION of the sq.h these argument lists follow
+ABI_VERSION = 3  # SQ_ABI_VERSION of the sq.h these argument lists follow
 
 EXPORTS = ["sq_scale_count", "sq_norm_stats", "sq_kmean_workspace_bytes", "sq_kmean", "sq_quant_qk_workspace_bytes",
            "sq_quant_qk", "sq_quant_v_fp8_workspace_bytes", "sq_quant_v_fp8", "sq_attn_workspace_bytes", "sq_attn",
@@ -97,8 +97,8 @@ def lib():
         L.sq_quant_v_fp8.argtypes = [P(sq_rows), _vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _sz, _vp]
         L.sq_attn_workspace_bytes.argtypes = [P(sq_qk), P(sq_qk), P(sq_values)]
         L.sq_attn_workspace_bytes.restype = _sz
-        L.sq_attn.argtypes = [P(sq_qk), P(sq_qk), P(sq_values), _f32, _int, _int, _vp, _vp, _i64, _i64, _i64, _vp,
-                              _i64, _i64, _vp, _sz, _vp]
+        L.sq_attn.argtypes = [P(sq_qk), P(sq_qk), P(sq_values), _f32, _int, _int, _vp, _vp, _int, _i64, _i64, _i64,
+                              _vp, _i64, _i64, _vp, _sz, _vp]
         L.sq_attn_prefix_lse_merge_workspace_bytes.argtypes = [P(sq_qk), P(sq_q8prefix)]
         L.sq_attn_prefix_lse_merge_workspace_bytes.restype = _sz
         L.sq_attn_prefix_lse_merge.argtypes = [P(sq_qk), P(sq_q8prefix), _vp, _i64, _i64, _f32, _int, _vp, _i64, _i64,
@@ -106,9 +106,9 @@ def lib():
         L.sq_paged_decode_workspace_bytes.argtypes = [_int, _int, _int, _int]
         L.sq_paged_decode_workspace_bytes.restype = _sz
         L.sq_paged_decode.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
-                                      _int, _int, _int, _f32, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+                                      _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp, _sz, _vp]
         L.sq_paged_prefill.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
-                                       _vp, _int, _int, _int, _int, _f32, _vp, _vp, _i64, _i64, _vp]
+                                       _vp, _int, _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp]
         L.sq_lse_merge.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                    _i64, _i64, _i64, _vp]
         L.sq_q8_cache_write.argtypes = [_vp, _vp, _int, _i64, _int, _int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
@@ -293,17 +293,25 @@ def _values(v: torch.Tensor, v_scale: Optional[torch.Tensor]) -> sq_values:
                      v_scale.stride(0), v_scale.stride(1))
 
 
+def _out_dtype(out: torch.Tensor) -> int:
+    """The sq_dtype of an attention output tensor: FP32 or bf16."""
+    dt = {torch.float32: SQ_F32, torch.bfloat16: SQ_BF16}.get(out.dtype)
+    assert dt is not None, "out: torch.float32 or torch.bfloat16, got %s" % out.dtype
+    return dt
+
+
 def sq_attn(q: QK, k: QK, v: torch.Tensor, v_scale: Optional[torch.Tensor] = None, score_scale: float = 1.0,
             kv_tile: int = 64, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             want_lse: bool = True, workspace: Optional[Workspace] = None, causal: bool = False,
-            sinks: Optional[torch.Tensor] = None):
+            sinks: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32):
     """Quantized attention core. v: bf16 (B, Sk, Hk, D) token-major, or FP8 codes from sq_quant_v_fp8 with v_scale.
     causal: query i sees keys 0 .. i + Sk - Sq; sinks: FP32 (H,) per-head sink logits (natural log) or None.
-    Returns (out FP32 (B, Sq, H, D), lse FP32 (B, H, Sq) base 2 or None)."""
+    out_dtype: torch.float32 or torch.bfloat16 (rounded to nearest even; a given out sets it).
+    Returns (out (B, Sq, H, D), lse FP32 (B, H, Sq) base 2 or None)."""
     B, Sq, H, D = q.codes.shape
     dev = q.codes.device
     if out is None:
-        out = torch.empty((B, Sq, H, D), dtype=torch.float32, device=dev)
+        out = torch.empty((B, Sq, H, D), dtype=out_dtype, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     qc, kc, vc = q.c(), k.c(), _values(v, v_scale)
@@ -313,7 +321,7 @@ def sq_attn(q: QK, k: QK, v: torch.Tensor, v_scale: Optional[torch.Tensor] = Non
     if sinks is not None:
         assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == H, "sinks: FP32 (H,)"
     _check(L.sq_attn(ctypes.byref(qc), ctypes.byref(kc), ctypes.byref(vc), score_scale, kv_tile, int(causal),
-                     _ptr(sinks), _ptr(out),
+                     _ptr(sinks), _ptr(out), _out_dtype(out),
                      out.stride(0), out.stride(1), out.stride(2), _ptr(lse), lse.stride(0) if lse is not None else 0,
                      lse.stride(1) if lse is not None else 0, _ptr(ws), nb, _stream(dev)))
     return out, lse
@@ -373,10 +381,11 @@ def _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, q
 def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
                     v_scale: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                     softmax_scale: float, out: Optional[torch.Tensor] = None,
-                    workspace: Optional[Workspace] = None, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    workspace: Optional[Workspace] = None, sinks: Optional[torch.Tensor] = None,
+                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """Paged GQA decode over a q8 cache. q bf16 (N, Hq, D); caches int8 [NB, bs, Hk, D] with FP16 scales
     [NB, bs, Hk, D/32]; block_table int32 (N, max_blocks); seq_lens int32 (N,); sinks FP32 (Hq,) per-head sink
-    logits (natural log) or None. Returns FP32 (N, Hq, D)."""
+    logits (natural log) or None. Returns (N, Hq, D) in out_dtype (FP32 or bf16)."""
     _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens)
     N, Hq, D = q.shape
     NB, bs, Hk, _ = k_cache.shape
@@ -385,13 +394,14 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
         assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == Hq, "sinks: FP32 (Hq,)"
 
     if out is None:
-        out = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
+        out = torch.empty((N, Hq, D), dtype=out_dtype, device=dev)
     L = lib()
     need = L.sq_paged_decode_workspace_bytes(N, Hq, D, max_seq_len)
     ws, nb = workspace.get(need) if workspace is not None else _ws(need, dev)
     _check(L.sq_paged_decode(_ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                              _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0), _ptr(seq_lens), N,
-                             max_seq_len, Hq, D, softmax_scale, _ptr(sinks), _ptr(out), out.stride(0), out.stride(1),
+                             max_seq_len, Hq, D, softmax_scale, _ptr(sinks), _ptr(out), _out_dtype(out),
+                             out.stride(0), out.stride(1),
                              _ptr(ws), nb,
                              _stream(dev)))
     return out
@@ -400,23 +410,25 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
 def sq_paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
                      v_scale: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                      query_start: torch.Tensor, max_seq_len: int, softmax_scale: float,
-                     out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """Paged causal (chunked) prefill over a q8 cache. q bf16 (num_tokens, Hq, D), packed by query_start int32
     (N + 1,); seq_lens int32 (N,) keys per sequence (context + its queries, already in the cache); caches and
-    block_table as sq_paged_decode; sinks FP32 (Hq,) or None. Returns FP32 (num_tokens, Hq, D)."""
+    block_table as sq_paged_decode; sinks FP32 (Hq,) or None. Returns (num_tokens, Hq, D) in out_dtype (FP32 or
+    bf16)."""
     _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, query_start)
     T, Hq, D = q.shape
     NB, bs, Hk, _ = k_cache.shape
     dev = q.device
     if out is None:
-        out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=dev)
     if sinks is not None:
         assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == Hq, "sinks: FP32 (Hq,)"
     L = lib()
     _check(L.sq_paged_prefill(_ptr(q), q.stride(0), q.stride(1), T, _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                               _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
                               _ptr(query_start), seq_lens.numel(), max_seq_len, Hq, D, softmax_scale, _ptr(sinks),
-                              _ptr(out), out.stride(0), out.stride(1), _stream(dev)))
+                              _ptr(out), _out_dtype(out), out.stride(0), out.stride(1), _stream(dev)))
     return out
 
 

@@ -24,6 +24,14 @@ int check_ws(void* ws, size_t have, size_t need, const char* what) {
     return SQ_OK;
 }
 
+// An attention output is FP32 or bf16 (rounded to nearest even), aligned to its element size.
+int check_out(const void* out, sq_dtype dtype, const char* what) {
+    if (dtype != SQ_F32 && dtype != SQ_BF16) return fail(SQ_ERR_UNSUPPORTED, "%s: out_dtype must be F32 or BF16", what);
+    if (reinterpret_cast<uintptr_t>(out) % (dtype == SQ_F32 ? 4 : 2))
+        return fail(SQ_ERR_ALIGN, "%s: out must be aligned to its element size", what);
+    return SQ_OK;
+}
+
 // Runs A1 into the workspace when the all-heads norm has no precomputed statistics.
 int prepare_all_heads(const sq_rows* x, RowArgs& r, void* ws, void* stream) {
     if (r.norm != SQ_NORM_ALL_HEADS || r.ms) return SQ_OK;
@@ -195,8 +203,8 @@ size_t sq_attn_workspace_bytes(const sq_qk* q, const sq_qk* k, const sq_values* 
 }
 
 int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scale, int kv_tile, int causal,
-            const float* sinks, float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh,
-            void* ws, size_t ws_bytes, void* stream) {
+            const float* sinks, void* out, sq_dtype out_dtype, int64_t ob, int64_t ot, int64_t oh, float* lse,
+            int64_t lb, int64_t lh, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     int st = check_pair(q, k, "sq_attn");
     if (st) return st;
@@ -204,6 +212,8 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
     if (k->S < 1) return fail(SQ_ERR_SHAPE, "sq_attn: no keys");
     if (!v || !v->data) return fail(SQ_ERR_NULL, "sq_attn: values are NULL");
     if (!out) return fail(SQ_ERR_NULL, "sq_attn: out is NULL");
+    st = check_out(out, out_dtype, "sq_attn");
+    if (st) return st;
     if (ob < 0 || ot < 0 || oh < 0 || lb < 0 || lh < 0) return fail(SQ_ERR_STRIDE, "sq_attn: negative stride");
     if (kv_tile != 64 && kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "sq_attn: kv_tile must be 64 or 128");
     if (!(score_scale > 0.0f) || !std::isfinite(score_scale))
@@ -225,7 +235,8 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
     a.kv_tile = kv_tile;
     a.causal = causal;
     a.sinks = sinks;
-    a.out = out; a.ob = ob; a.ot = ot; a.oh = oh;
+    a.out = static_cast<float*>(out); a.out_bf16 = out_dtype == SQ_BF16;
+    a.ob = ob; a.ot = ot; a.oh = oh;
     a.lse = lse; a.lb = lb; a.lh = lh;
     // the key loop addresses one (b, kv head) slice of K and of V^T with 32-bit byte offsets
     constexpr int64_t kLim = int64_t(1) << 31;
@@ -398,8 +409,8 @@ size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_
 int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
                     const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
-                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, float* out, int64_t on,
-                    int64_t oh, void* ws, size_t ws_bytes, void* stream) {
+                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
+                    sq_dtype out_dtype, int64_t on, int64_t oh, void* ws, size_t ws_bytes, void* stream) {
     clear_error();
     const char* what = "sq_paged_decode";
     if (num_seqs < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
@@ -427,6 +438,10 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
         return fail(SQ_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", what);
     {
+        const int st = check_out(out, out_dtype, what);
+        if (st) return st;
+    }
+    {
         const int st = check_ws(ws, ws_bytes, sq_paged_decode_workspace_bytes(num_seqs, Hq, D, max_seq_len), what);
         if (st) return st;
     }
@@ -438,7 +453,8 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     a.N = num_seqs; a.max_len = max_seq_len;
     a.scale = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);  // log2 units
     a.sinks = sinks;
-    a.out = out; a.on = on; a.oh = oh;
+    a.out = static_cast<float*>(out); a.out_bf16 = out_dtype == SQ_BF16;
+    a.on = on; a.oh = oh;
     a.part = static_cast<float*>(ws);
     a.segs = (max_seq_len + kDecodeSeg - 1) / kDecodeSeg;
     return launch_decode(a, stream);
@@ -450,7 +466,7 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
                      const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
                      int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                      const int32_t* query_start, int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale,
-                     const float* sinks, float* out, int64_t ot, int64_t oh, void* stream) {
+                     const float* sinks, void* out, sq_dtype out_dtype, int64_t ot, int64_t oh, void* stream) {
     clear_error();
     const char* what = "sq_paged_prefill";
     if (num_seqs < 0 || num_tokens < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
@@ -481,6 +497,10 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
     if (ot < 0 || oh < 0) return fail(SQ_ERR_STRIDE, "%s: negative output stride", what);
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
         return fail(SQ_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", what);
+    {
+        const int st = check_out(out, out_dtype, what);
+        if (st) return st;
+    }
     PrefillArgs a{};
     a.q = static_cast<const uint16_t*>(q); a.qt = qt; a.qh = qh;
     a.kc = k_cache; a.ks = k_scale; a.vc = v_cache; a.vs = v_scale;
@@ -492,7 +512,8 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
     a.T = static_cast<int>(num_tokens);
     a.scale = static_cast<float>(static_cast<double>(softmax_scale) * 1.4426950408889634);  // log2 units
     a.sinks = sinks;
-    a.out = out; a.ot = ot; a.oh = oh;
+    a.out = static_cast<float*>(out); a.out_bf16 = out_dtype == SQ_BF16;
+    a.ot = ot; a.oh = oh;
     if (a.nqb * Hk >= (int64_t(1) << 31)) return fail(SQ_ERR_UNSUPPORTED, "%s: too many query blocks", what);
     return launch_prefill(a, stream);
 }

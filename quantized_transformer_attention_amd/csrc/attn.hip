@@ -297,7 +297,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     }
 
     // what the epilogue needs, folded to a few values before the key loop (fewer live scalars)
-    float* const obase = a.out + b * a.ob + h * a.oh;
+    const int64_t obase = b * a.ob + h * a.oh;   // element offset of (b, h) in out
+    const bool obf = a.out_bf16 != 0;
     const int64_t ot = a.ot;
     float* const lbase = a.lse ? a.lse + b * a.lb + h * a.lh : nullptr;
     const float* const vsbase = FP8 ? a.vscale + b * a.vssb + hk * a.vssh : nullptr;
@@ -371,13 +372,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
             const float inv = 1.0f / li;
             const int qr = q0i + n * 16 + 4 * g + i;
             if (qr >= Sq) continue;
-            float* op = obase + qr * ot;
+            const int64_t orow = obase + qr * ot;
 #pragma unroll
             for (int ct = 0; ct < C::NCT; ++ct) {
                 const int c = ct * 16 + lq;
                 float val = st.o[n][ct][i] * inv;
                 if constexpr (FP8) val = val * (vsbase[c] * 0.00390625f);
-                op[c] = val;
+                store_out(a.out, orow + c, val, obf);
             }
         }
     }

@@ -333,7 +333,8 @@ __global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
             }
         }
     }
-    a.out[static_cast<int64_t>(n) * a.on + static_cast<int64_t>(hq) * a.oh + c] = tot > 0.0f ? o / tot : 0.0f;
+    store_out(a.out, static_cast<int64_t>(n) * a.on + static_cast<int64_t>(hq) * a.oh + c, tot > 0.0f ? o / tot : 0.0f,
+              a.out_bf16 != 0);
 }
 
 inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }

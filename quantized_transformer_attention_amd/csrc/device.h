@@ -21,6 +21,13 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
     f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
 }
 
+// Stores element idx of an output tensor: FP32, or bfloat16 rounded to nearest even when bf16
+// (idx counts elements of the stored type).
+__device__ __forceinline__ void store_out(float* out, int64_t idx, float v, bool bf16) {
+    if (bf16) reinterpret_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);
+    else out[idx] = v;
+}
+
 // Round to bfloat16, nearest even (v_cvt_pk_bf16_f32), back to float.
 __device__ __forceinline__ float bf16_round(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
 

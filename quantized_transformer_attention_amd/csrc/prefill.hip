@@ -311,9 +311,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
             const int r = 32 * w + 16 * n + 4 * g + i;
             const int j = j0 + r / G;
             if (j >= qlen || qs0 + j < 0 || qs0 + j >= a.T) continue;
-            float* op = a.out + static_cast<int64_t>(qs0 + j) * a.ot + static_cast<int64_t>(hk * G + r % G) * a.oh;
+            const int64_t orow = static_cast<int64_t>(qs0 + j) * a.ot + static_cast<int64_t>(hk * G + r % G) * a.oh;
 #pragma unroll
-            for (int ct = 0; ct < kNCT; ++ct) op[16 * ct + lq] = o[n][ct][i] * inv;
+            for (int ct = 0; ct < kNCT; ++ct) store_out(a.out, orow + 16 * ct + lq, o[n][ct][i] * inv, a.out_bf16 != 0);
         }
     }
 }

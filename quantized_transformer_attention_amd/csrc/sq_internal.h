@@ -90,7 +90,8 @@ struct AttnArgs {
     int kv_tile;
     int causal;                 // query i sees keys 0 .. i + Sk - Sq
     const float* sinks;         // (H,) sink logits in natural-log units, or NULL
-    float* out;
+    float* out;                 // FP32 elements, or bf16 ones when out_bf16 (strides count elements)
+    int out_bf16;
     int64_t ob, ot, oh;
     float* lse;
     int64_t lb, lh;
@@ -124,7 +125,8 @@ struct PrefixArgs {
     int kv_tile;
     int causal;                 // query i sees keys 0 .. i + Sk - Sq
     const float* sinks;         // (H,) sink logits in natural-log units, or NULL
-    float* out;
+    float* out;                 // FP32 elements, or bf16 ones when out_bf16 (strides count elements)
+    int out_bf16;
     int64_t ob, ot, oh;
     float* lse;
     int64_t lb, lh;
@@ -174,7 +176,8 @@ struct DecodeArgs {
     int N, max_len;
     float scale;
     const float* sinks;         // (Hq,) sink logits in natural-log units, or NULL
-    float* out;
+    float* out;                 // FP32 elements, or bf16 ones when out_bf16
+    int out_bf16;
     int64_t on, oh;
     float* part;                // split-KV partials (N, Hq, segs, D + 2): acc, max, exp-sum
     int segs;                   // segments per sequence: ceil(max_len / kDecodeSeg)
@@ -198,7 +201,8 @@ struct PrefillArgs {
     int T;                      // num_tokens: rows outside [0, T) are neither read nor written
     float scale;                // softmax_scale * log2 e
     const float* sinks;         // (Hq,) sink logits in natural-log units, or NULL
-    float* out;
+    float* out;                 // FP32 elements, or bf16 ones when out_bf16
+    int out_bf16;
     int64_t ot, oh;
 };
 

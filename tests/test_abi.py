@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(sq.EXPORTS)
-    assert L.sq_abi_version() == sq.ABI_VERSION == 2
+    assert L.sq_abi_version() == sq.ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -87,9 +87,9 @@ def test_attn_validation_errors():
     L = sq.lib()
     v = sq.sq_values(0x3000, sq.SQ_BF16, 10 * 2 * 128, 2 * 128, 128, 1, None, 0, 0)
 
-    def call(q, k, vv=v, tile=64, out=0x4000, scale=1.0, ws=None, wsb=0, causal=0):
-        return L.sq_attn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vv), scale, tile, causal, None, out, 0, 0, 0,
-                         None, 0, 0, ws, wsb, None)
+    def call(q, k, vv=v, tile=64, out=0x4000, scale=1.0, ws=None, wsb=0, causal=0, odt=sq.SQ_F32):
+        return L.sq_attn(ctypes.byref(q), ctypes.byref(k), ctypes.byref(vv), scale, tile, causal, None, out, odt, 0, 0,
+                         0, None, 0, 0, ws, wsb, None)
 
     assert call(_qk(layout=2), _qk()) == -5                # THREAD_K is a key layout
     assert call(_qk(), _qk(layout=1, block=32)) == -5      # THREAD_Q is a query layout
@@ -97,6 +97,9 @@ def test_attn_validation_errors():
     assert call(_qk(D=64), _qk()) == -2                   # head dims differ
     assert call(_qk(), _qk(), tile=32) == -5
     assert call(_qk(), _qk(), out=0) == -1
+    assert call(_qk(), _qk(), odt=sq.SQ_F16) == -5          # out FP32 or bf16
+    assert call(_qk(), _qk(), out=0x4002) == -4             # FP32 out on 4-byte boundaries
+    assert call(_qk(), _qk(), out=0x4001, odt=sq.SQ_BF16) == -4
     assert call(_qk(), _qk(), scale=0.0) == -2
     assert call(_qk(), _qk(S=0)) == -2                     # no keys
     assert call(_qk(), _qk()) == -6                        # bf16 values are staged in a workspace
@@ -152,10 +155,11 @@ def test_lse_merge_validation_errors():
 
 
 def _call_prefill(T=10, NB=4, bs=16, Hk=2, Hq=8, D=128, q=0x1000, qt=1024, qh=128, kc=0x2000, ks=0x3000, vc=0x4000,
-                  vs=0x5000, bt=0x6000, bts=4, lens=0x7000, qs=0x8000, N=2, max_len=64, scale=0.125, out=0x9000):
+                  vs=0x5000, bt=0x6000, bts=4, lens=0x7000, qs=0x8000, N=2, max_len=64, scale=0.125, out=0x9000,
+                  odt=sq.SQ_F32):
     L = sq.lib()
     return L.sq_paged_prefill(q, qt, qh, T, kc, ks, vc, vs, NB, bs, Hk, bt, bts, lens, qs, N, max_len, Hq, D, scale,
-                              None, out, Hq * D, D, None)
+                              None, out, odt, Hq * D, D, None)
 
 
 def test_paged_prefill_validation_errors():
@@ -173,6 +177,33 @@ def test_paged_prefill_validation_errors():
     assert _call_prefill(qh=132) == -4
     assert _call_prefill(ks=0x3002) == -4
     assert _call_prefill(scale=0.0) == -2
+    assert _call_prefill(odt=sq.SQ_I8) == -5               # out FP32 or bf16
+    assert _call_prefill(out=0x9002) == -4
+
+
+def _call_decode(N=2, NB=4, bs=16, Hk=2, Hq=8, D=128, q=0x1000, qn=1024, qh=128, kc=0x2000, ks=0x3000, vc=0x4000,
+                 vs=0x5000, bt=0x6000, bts=4, lens=0x7000, max_len=64, scale=0.125, out=0x9000, odt=sq.SQ_F32,
+                 ws=0x10000, wsb=1 << 20):
+    L = sq.lib()
+    return L.sq_paged_decode(q, qn, qh, kc, ks, vc, vs, NB, bs, Hk, bt, bts, lens, N, max_len, Hq, D, scale, None,
+                             out, odt, Hq * D, D, ws, wsb, None)
+
+
+def test_paged_decode_validation_errors():
+    assert _call_decode(D=64) == -5                        # head dim 128 only
+    assert _call_decode(bs=32) == -5                       # block size 16 only
+    assert _call_decode(Hq=6, Hk=4) == -2
+    assert _call_decode(Hq=32, Hk=2) == -5                 # Hq / Hk = 16
+    assert _call_decode(N=0, q=None) == 0                  # no sequences: nothing read
+    assert _call_decode(max_len=0) == -2
+    assert _call_decode(lens=None) == -1
+    assert _call_decode(bts=3) == -3                       # table rows shorter than max_len needs
+    assert _call_decode(q=0x1008) == -4
+    assert _call_decode(vs=0x5004) == -4
+    assert _call_decode(scale=float("inf")) == -2
+    assert _call_decode(odt=sq.SQ_FP8E4M3) == -5           # out FP32 or bf16
+    assert _call_decode(out=0x9001, odt=sq.SQ_BF16) == -4
+    assert _call_decode(ws=None) == -6                     # the segment partials need a workspace
 
 
 def test_paged_bindings_reject_wrong_dtypes():
