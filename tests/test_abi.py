@@ -228,3 +228,18 @@ def test_paged_bindings_reject_wrong_dtypes():
         if "qs" not in bad:
             with pytest.raises(AssertionError):
                 sq.sq_paged_decode(a["q"], a["kc"], a["ks"], a["kc"], a["ks"], a["bt"], a["lens"], 64, 0.125)
+
+
+def test_paged_bindings_reject_wrong_out_dtype():
+    """A given output tensor sets out_dtype: only FP32 and bf16 reach the library."""
+    import torch
+    q = torch.zeros((3, 8, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((4, 16, 2, 128), dtype=torch.int8)
+    ks = torch.zeros((4, 16, 2, 4), dtype=torch.float16)
+    bt = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.tensor([5, 9], dtype=torch.int32)
+    qs = torch.tensor([0, 1, 3], dtype=torch.int32)
+    with pytest.raises(AssertionError):
+        sq.sq_paged_prefill(q, kc, ks, kc, ks, bt, lens, qs, 64, 0.125, out=torch.zeros((3, 8, 128), dtype=torch.float16))
+    with pytest.raises(AssertionError):
+        sq.sq_paged_decode(q[:2], kc, ks, kc, ks, bt, lens, 64, 0.125, out=torch.zeros((2, 8, 128), dtype=torch.float64))
