@@ -44,6 +44,9 @@
 extern "C" {
 #endif
 
+/* Raised whenever an argument list changes: 2 added causal masking and sinks (sq_attn,
+ * sq_paged_decode) and sq_paged_prefill; 3 added out_dtype (FP32 or bf16 outputs) to
+ * sq_attn, sq_paged_decode and sq_paged_prefill. sq_abi_version() returns it. */
 #define SQ_ABI_VERSION 3
 
 enum {
