@@ -243,3 +243,13 @@ def test_paged_bindings_reject_wrong_out_dtype():
         sq.sq_paged_prefill(q, kc, ks, kc, ks, bt, lens, qs, 64, 0.125, out=torch.zeros((3, 8, 128), dtype=torch.float16))
     with pytest.raises(AssertionError):
         sq.sq_paged_decode(q[:2], kc, ks, kc, ks, bt, lens, 64, 0.125, out=torch.zeros((2, 8, 128), dtype=torch.float64))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libsq.so every entry point raises: there is no CPU fallback."""
+    monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "libsq.so"))
+    monkeypatch.setattr(sq, "_lib", None)
+    with pytest.raises(ImportError):
+        sq.lib()
+    with pytest.raises(ImportError):
+        sq.sq_scale_count(100, sq.LAYOUT_PER_BLOCK, 64)
