@@ -82,7 +82,9 @@ def _declare(L):
     L.orc_scale_index.argtypes, L.orc_scale_index.restype = [_i64, _int, _int], _i64
     L.orc_quant_qk.argtypes = [P(_Rows), _int, _int, _f32, _vp, _vp]
     L.orc_quant_v_fp8.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _vp]
-    L.orc_attn.argtypes = [P(_QK), P(_QK), _vp, _int, _vp, _f32, _int, _f64, _int, _vp, _vp, _i64, _vp, _vp, _vp]
+    L.orc_run_truncation_bound.argtypes, L.orc_run_truncation_bound.restype = [_vp, _i64], _f64
+    L.orc_attn.argtypes = [P(_QK), P(_QK), _vp, _int, _vp, _f32, _int, _f64, _int, _vp, _vp, _i64, _vp, _vp, _vp,
+                           _vp]
     L.orc_prefix_merge.argtypes = [P(_QK), P(_Prefix), _vp, _f32, _int, _f64, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                    _vp, _vp]
     L.orc_q8_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp]
@@ -225,6 +227,13 @@ def quant_v_fp8(v: np.ndarray):
     return codes, vs
 
 
+def run_truncation_bound(prod: np.ndarray) -> float:
+    """What the FP8 P.V allowance admits for one run of exact products (the reading of an FP8 dot product that
+    adds a run of 8 products on a grid of 2^(E - 13), E the exponent of the run's largest magnitude)."""
+    prod = _c(prod, np.float64)
+    return float(lib().orc_run_truncation_bound(_p(prod), prod.size))
+
+
 # ----------------------------------------------------------------------------- attention
 @dataclass
 class QK:
@@ -241,9 +250,10 @@ def _qk_struct(t: QK):
 
 
 def attn(q: QK, k: QK, v: np.ndarray, fp8: bool, vs=None, score_scale=1.0, kv_tile=64, rows=None,
-         flip_rel=2.0 ** -22, want_allow=True, causal=False, sinks=None):
+         flip_rel=2.0 ** -22, want_allow=True, causal=False, sinks=None, want_run_allow=False):
     """Quantized-mode attention core: out (B, rows, H, D), lse (B, H, rows), allow. causal: query i attends keys
-    0 .. i + Sk - Sq; sinks: FP32 (H,) per-head sink logits ([tq] USE_SINKS) or None."""
+    0 .. i + Sk - Sq; sinks: FP32 (H,) per-head sink logits ([tq] USE_SINKS) or None. want_run_allow: also return
+    the part of allow that the FP8 dot-product reading adds (zero for bf16 P.V) as a fourth result."""
     qs, kq = _qk_struct(q)
     ks, kk = _qk_struct(k)
     v = _c(v, np.uint8 if fp8 else np.uint16)
@@ -254,9 +264,12 @@ def attn(q: QK, k: QK, v: np.ndarray, fp8: bool, vs=None, score_scale=1.0, kv_ti
     out = np.empty((B, n, H, D), np.float64)
     lse = np.empty((B, H, n), np.float64)
     allow = np.empty((B, n, H, D), np.float64) if want_allow else None
+    run = np.empty((B, n, H, D), np.float64) if (want_allow and want_run_allow) else None
     sk_ = _c(sinks, np.float32) if sinks is not None else None
     lib().orc_attn(ctypes.byref(qs), ctypes.byref(ks), _p(v), int(fp8), _p(vs_), score_scale, kv_tile, flip_rel,
-                   int(causal), _p(sk_), _p(rows), n, _p(out), _p(lse), _p(allow))
+                   int(causal), _p(sk_), _p(rows), n, _p(out), _p(lse), _p(allow), _p(run))
+    if want_run_allow:
+        return out, lse, allow, run
     return out, lse, allow
 
 

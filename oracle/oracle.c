@@ -470,6 +470,9 @@ static double run_truncation_bound(const double* prod, int64_t n) {
     return lost;
 }
 
+/* exported for the pin of the FP8 dot-product reading (a run of products given directly) */
+double orc_run_truncation_bound(const double* prod, int64_t n) { return run_truncation_bound(prod, n); }
+
 static double pt_flip(float p, int fp8, double flip_rel) {
     double base = pt_value(p, fp8);
     double lo = pt_value((double)p * (1.0 - flip_rel), fp8);
@@ -483,7 +486,8 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
               int causal, const float* sinks /* (H,) natural-log logits or NULL */,
               const int64_t* rows, int64_t nrows,
               double* out /* (B, nrows, H, D) */, double* lse /* (B, H, nrows) */,
-              double* allow /* (B, nrows, H, D) or NULL */) {
+              double* allow /* (B, nrows, H, D) or NULL */,
+              double* allow_run /* (B, nrows, H, D) or NULL: the FP8 run part of allow alone */) {
     const int64_t B = q->B, H = q->H, D = q->D, Sk = k->S, Hk = k->H, G = H / Hk;
     const int64_t off = Sk - q->S;   /* causal: query i sees keys 0 .. i + Sk - Sq */
     const int64_t nq = orc_scale_count(q->S, q->layout, q->block);
@@ -495,11 +499,11 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                 const int64_t i = rows[ri], hk = h / G;
                 const int8_t* qc = q->codes + ((b * q->S + i) * H + h) * D;
                 const float qs = q->scales[(b * H + h) * nq + orc_scale_index(i, q->layout, q->block)];
-                double acc[512], al[512];
+                double acc[512], al[512], ar[512];
                 float* a = (float*)malloc(sizeof(float) * (size_t)kv_tile);
                 float* c = (float*)malloc(sizeof(float) * (size_t)kv_tile);
                 double* ptv = (double*)malloc(sizeof(double) * (size_t)kv_tile);
-                for (int64_t d = 0; d < D; ++d) acc[d] = al[d] = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc[d] = al[d] = ar[d] = 0.0;
                 /* [tq] sinks: the softmax starts from M = the head's sink logit (base 2 here:
                  * RN(s_h * log2 e) in FP32), L = 1, so the sink joins the denominator only */
                 float m = sinks ? sinks[h] * 1.44269504f : -INFINITY;
@@ -523,7 +527,7 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                     }
                     float mn = fmaxf(m, mt);
                     double alpha = (m == -INFINITY) ? 0.0 : (double)(float)exp2((double)(m - mn));
-                    for (int64_t d = 0; d < D; ++d) { acc[d] *= alpha; al[d] *= alpha; }
+                    for (int64_t d = 0; d < D; ++d) { acc[d] *= alpha; al[d] *= alpha; ar[d] *= alpha; }
                     l *= alpha;
                     for (int64_t jj = 0; jj < n; ++jj) {
                         int64_t j = j0 + jj;
@@ -549,7 +553,9 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                                     int64_t vi = ((b * Sk + j0 + r0 + u) * Hk + hk) * D + d;
                                     prod[u] = ptv[r0 + u] * e4m3_value(((const uint8_t*)v)[vi]);
                                 }
-                                al[d] += run_truncation_bound(prod, rn);
+                                const double lost = run_truncation_bound(prod, rn);
+                                al[d] += lost;
+                                ar[d] += lost;
                             }
                     }
                     m = mn;
@@ -558,6 +564,7 @@ void orc_attn(const orc_qk* q, const orc_qk* k,
                     double f = fp8 ? (double)vs[(b * Hk + hk) * D + d] / (256.0 * l) : 1.0 / l;
                     out[((b * nrows + ri) * H + h) * D + d] = acc[d] * f;
                     if (allow) allow[((b * nrows + ri) * H + h) * D + d] = al[d] * f;
+                    if (allow_run) allow_run[((b * nrows + ri) * H + h) * D + d] = ar[d] * f;
                 }
                 lse[(b * H + h) * nrows + ri] = (double)m + log2(l);
                 free(a);

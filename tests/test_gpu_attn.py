@@ -61,14 +61,16 @@ def test_core_parity_ragged(case):
     kc, ks = _rand_codes(g, 1, Sk, Hk, D, kl, kb)
     v = gen.normal_bf16((1, Sk, Hk, D), g, outliers=3)
     fp8 = pv == "fp8"
+    run = None
     if fp8:
         v8, vs = O.quant_v_fp8(v)
-        ref, rlse, allow = O.attn(O.QK(qc, qs, ql, qb), O.QK(kc, ks, kl, kb), v8, True, vs, kv_tile=kvt)
+        ref, rlse, allow, run = O.attn(O.QK(qc, qs, ql, qb), O.QK(kc, ks, kl, kb), v8, True, vs, kv_tile=kvt,
+                                       want_run_allow=True)
         out, lse = _run_core(qc, qs, ql, qb, kc, ks, kl, kb, v8, True, vs, kvt)
     else:
         ref, rlse, allow = O.attn(O.QK(qc, qs, ql, qb), O.QK(kc, ks, kl, kb), v, False, kv_tile=kvt)
         out, lse = _run_core(qc, qs, ql, qb, kc, ks, kl, kb, v, False, None, kvt)
-    check_float(out, ref, allow, what="out")
+    check_float(out, ref, allow, what="out", run=run)
     np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
 
 
@@ -117,14 +119,16 @@ def _pipeline_oracle(c, inp, rows):
     mu = O.kmean(inp.k, pk)
     qc, qs = O.quant_qk(inp.q, pq, ql, qb, sm_scale=gen.sm_scale_q(c.D))
     kc, ks = O.quant_qk(inp.k, pk, kl, kb, mean=mu)
+    run = None
     if c.pv == "fp8":
         v8, vs = O.quant_v_fp8(inp.v)
-        out, lse, allow = O.attn(O.QK(qc, qs, ql, qb), O.QK(kc, ks, kl, kb), v8, True, vs, kv_tile=c.kv_tile, rows=rows)
+        out, lse, allow, run = O.attn(O.QK(qc, qs, ql, qb), O.QK(kc, ks, kl, kb), v8, True, vs, kv_tile=c.kv_tile,
+                                      rows=rows, want_run_allow=True)
     else:
         out, lse, allow = O.attn(O.QK(qc, qs, ql, qb), O.QK(kc, ks, kl, kb), inp.v, False, kv_tile=c.kv_tile,
                                  rows=rows)
     exact = O.attn_exact(inp.q, pq, inp.k, pk, inp.v, rows=rows)
-    return out, lse, allow, exact, (qc, qs, kc, ks, mu)
+    return out, lse, (allow, run), exact, (qc, qs, kc, ks, mu)
 
 
 def _sample_rows(S, n, seed, tile=128):
@@ -139,11 +143,11 @@ def test_cfg1_tiny_end_to_end():
     c = gen.CFG1
     inp = gen.attn_inputs(c)
     out, lse, q, k, mu = _pipeline_gpu(c, inp)
-    ref, rlse, allow, exact, (qc, qs, kc, ks, mu_o) = _pipeline_oracle(c, inp, None)
+    ref, rlse, (allow, run), exact, (qc, qs, kc, ks, mu_o) = _pipeline_oracle(c, inp, None)
     np.testing.assert_array_equal(host(q.codes), qc)
     np.testing.assert_array_equal(host(k.codes), kc)
     o = host(out)
-    err = check_float(o, ref, allow, what="cfg1 out")
+    err = check_float(o, ref, allow, what="cfg1 out", run=run)
     np.testing.assert_allclose(host(lse), rlse, atol=1e-4)
     cs = cosine(o, exact)
     print("cfg1 max err/rms %.3g cos %.6f" % (err, cs))
@@ -159,13 +163,14 @@ def test_full_size_sampled_rows(c):
     out, lse, q, k, mu = _pipeline_gpu(c, inp)
     rows = _sample_rows(c.Sq, 24, c.seed)
     print("gpu done; oracle on %d rows" % rows.size, flush=True)
-    ref, rlse, allow, exact, (qc, qs, kc, ks, mu_o) = _pipeline_oracle(c, inp, rows)
+    ref, rlse, (allow, run), exact, (qc, qs, kc, ks, mu_o) = _pipeline_oracle(c, inp, rows)
     np.testing.assert_array_equal(host(mu).view(np.uint32), mu_o.view(np.uint32))
     np.testing.assert_array_equal(host(k.codes), kc)
     np.testing.assert_array_equal(host(q.codes)[:, rows], qc[:, rows])
     np.testing.assert_array_equal(host(q.scales).view(np.uint32), qs.view(np.uint32))
     o = host(out)[:, rows]
-    err = check_float(o, ref, allow, what="%s out" % c.name)
+    # the video workload (FP8 P.V) is accepted partly through the FP8 run allowance: the count is printed
+    err = check_float(o, ref, allow, what="%s out" % c.name, run=run)
     np.testing.assert_allclose(host(lse)[:, :, rows], rlse, atol=1e-4)
     cs = cosine(o, exact)
     print("%s max err/rms %.3g cos %.6f" % (c.name, err, cs))

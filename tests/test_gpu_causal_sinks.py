@@ -110,10 +110,10 @@ def test_causal_at_size_sampled_rows():
     sinks = np.array([0.5, -1.0, 2.0, 1.0], np.float32)
     g = np.random.default_rng(80)
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, S - 1], g.choice(S, 40, replace=False)])).astype(np.int64)
-    ref, rlse, allow = O.attn(O.QK(qc, qs, 1, 32), O.QK(kc, ks, 2, 64), v, True, vs, kv_tile=128, rows=rows,
-                              causal=True, sinks=sinks)
+    ref, rlse, allow, run = O.attn(O.QK(qc, qs, 1, 32), O.QK(kc, ks, 2, 64), v, True, vs, kv_tile=128, rows=rows,
+                                   causal=True, sinks=sinks, want_run_allow=True)
     out, lse = _gpu(qc, qs, 1, 32, kc, ks, 2, 64, v, vs, 128, True, sinks)
-    check_float(out[:, rows], ref, allow, what="out")
+    check_float(out[:, rows], ref, allow, what="out", run=run)
     np.testing.assert_allclose(lse[:, :, rows], rlse, rtol=0, atol=1e-4)
 
 

@@ -242,7 +242,13 @@ def test_kmean_matches_fp64_mean():
     mu = O.kmean(x, pro)
     z = O.prologue_rows(x, pro).astype(np.float64)
     ref = z.mean(axis=1)
-    np.testing.assert_allclose(mu, ref, rtol=1e-5, atol=1e-7)
+    # within 1e-6 of the FP64 mean, relative to the mean magnitude of the summed rows (a mean near zero has no
+    # relative precision of its own), and within 1e-6 relative wherever the mean is not small
+    scale = np.abs(z).mean(axis=1)
+    assert (np.abs(mu - ref) <= 1e-6 * scale).all(), float((np.abs(mu - ref) / scale).max())
+    big = np.abs(ref) >= 0.05 * scale
+    assert big.sum() > 20
+    np.testing.assert_allclose(mu[big], ref[big], rtol=1e-6, atol=0)
     # the mean subtracted by the quantizer: quantizing (x, mean) equals quantizing the centred rows
     codes, _ = O.quant_qk(x, pro, 0, 64, mean=mu, scale_eps=0.0)
     zc = O.prologue_rows(x, pro, mean=mu)
@@ -315,6 +321,130 @@ def test_attention_exact_on_grid_fp8():
     # p = 2^-n is e4m3-exact while 256 p >= 2^-9, i.e. n <= 17: scores span 8
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(lse, rlse, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- V to FP8
+def test_v_fp8_scales_and_codes_by_brute_force():
+    """Per (b, h, channel): vs = max(RN(amax over tokens / 448), 1e-8) in FP32, codes = e4m3fn(RN(v / vs)) as torch
+    converts FP32 (round to nearest even); a zero channel, a channel of -0, a channel below the 1e-8 floor and a
+    channel whose maximum reaches the largest code."""
+    g = gen.rng(30, 0)
+    B, T, H, D = 2, 53, 3, 64
+    bits = gen.normal_bf16((B, T, H, D), g, outliers=3)
+    bits[0, :, 0, 5] = 0x0000                                        # zeros
+    bits[0, :, 1, 7] = 0x8000                                        # all -0: codes keep the sign
+    tiny = (g.standard_normal(T) * 1e-7).astype(np.float32)
+    bits[1, :, 2, 9] = gen.to_bf16_bits(tiny)                          # amax / 448 < 1e-8: the floor
+    bits[1, 11, 0, 3] = gen.to_bf16_bits(np.array([-300.0], np.float32))[0]   # one large negative entry
+    codes, vs = O.quant_v_fp8(bits)
+    x = f32(bits)                                                    # FP32 values (B, T, H, D)
+    amax = np.abs(x).max(axis=1)                                     # over tokens only
+    want_vs = np.maximum(amax / np.float32(448.0), np.float32(1e-8)).astype(np.float32)
+    np.testing.assert_array_equal(vs.view(np.uint32), want_vs.view(np.uint32))
+    quot = (x / want_vs[:, None]).astype(np.float32)                 # IEEE FP32 division
+    want = torch.from_numpy(quot).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes, want)
+    assert (codes[0, :, 1, 7] == 0x80).all() and (codes[0, :, 0, 5] == 0).all()
+    assert vs[1, 2, 9] == np.float32(1e-8) and codes[1, 11, 0, 3] == 0xFE   # -448: the channel's maximum
+    # vs rounded down can put a quotient an ulp above 448: it still rounds to the largest code, never to NaN
+    assert np.abs(quot).max() <= 448.0 * (1 + 2.0 ** -22)
+    assert not np.isin(codes, (0x7F, 0xFF)).any()
+    # the plausible slips fail: a 127 divisor, or the maximum over channels instead of tokens
+    assert not np.array_equal(vs, np.maximum(amax / np.float32(127.0), np.float32(1e-8)))
+    assert not np.array_equal(vs, np.broadcast_to(np.maximum(np.abs(x).max(axis=(1, 3)) / np.float32(448.0),
+                                                             np.float32(1e-8))[..., None], vs.shape))
+
+
+# ----------------------------------------------------------------------------- FP8 dot-product reading
+def _run_on_grid(prod, rounding):
+    """A run of exact products added on the grid of 2^(E - 13), E the exponent of its largest magnitude (numpy
+    emulation of the reading the FP8 P.V allowance follows); rounding 'trunc' (toward zero) or 'nearest'."""
+    prod = np.asarray(prod, np.float64)
+    mx = np.abs(prod).max()
+    if mx == 0.0:
+        return 0.0
+    _, e = np.frexp(mx)                       # mx = f 2^e, f in [0.5, 1): leading bit 2^(e - 1)
+    u = 2.0 ** (int(e) - 1 - 13)
+    q = np.trunc(prod / u) if rounding == "trunc" else np.rint(prod / u)
+    return float((q * u).sum())
+
+
+def _e4m3_values():
+    return np.array([O.e4m3_value(b) for b in range(256) if b not in (0x7F, 0xFF)], np.float64)
+
+
+def test_fp8_run_bound_covers_grid_emulation_and_is_tight():
+    """run_truncation_bound >= what a run loses on the grid (either rounding), on random and adversarial runs of 8
+    e4m3 x e4m3 products; for runs of one large product and seven below the grid it equals the loss."""
+    g = np.random.default_rng(31)
+    vals = _e4m3_values()
+    ratios = []
+    for it in range(3000):
+        kind = it % 4
+        if kind == 0:      # random codes
+            prod = g.choice(vals, 8) * g.choice(vals, 8)
+        elif kind == 1:    # one large product, seven small of random sign
+            prod = np.concatenate([[448.0 * 448.0], g.choice(vals[np.abs(vals) < 2.0], 7) * g.choice([-1.0, 1.0], 7)])
+        elif kind == 2:    # the products of P (~ 256 p) and V codes of one channel, p over two decades
+            pt = np.array([O.e4m3_value(O.f32_to_e4m3(float(v))) for v in 256.0 * 2.0 ** -g.uniform(0, 7, 8)])
+            prod = pt * g.choice(vals, 8)
+        else:              # subnormal codes beside normal ones
+            prod = g.choice(vals[np.abs(vals) < 2.0 ** -6], 8) * g.choice(vals, 8)
+            prod[g.integers(0, 8)] = g.choice(vals) * 448.0
+        g.shuffle(prod)
+        exact = float(prod.sum())
+        bound = O.run_truncation_bound(prod)
+        for rnd in ("trunc", "nearest"):
+            loss = abs(_run_on_grid(prod, rnd) - exact)
+            assert loss <= bound * (1 + 1e-12), (it, rnd, prod, loss, bound)
+        lt = abs(_run_on_grid(prod, "trunc") - exact)
+        if lt > 0:
+            ratios.append(bound / lt)
+    ratios = np.array(ratios)
+    assert ratios.size > 500
+    assert np.median(ratios) <= 4.0, np.median(ratios)          # not slack by orders of magnitude
+    # adversarial: seven products just below the grid step u beside the largest: loss == bound exactly
+    big = 448.0 * 256.0                                          # 1.75 2^16: u = 2^3
+    for small in (7.5, 7.0, 4.0, 1.0, -6.5, 2.0 ** -9):
+        prod = np.array([big] + [small] * 7)
+        loss = abs(_run_on_grid(prod, "trunc") - prod.sum())
+        assert loss == O.run_truncation_bound(prod) == 7 * abs(small)
+    # products on the grid lose nothing and the bound is zero
+    prod = np.array([big, 8.0, -16.0, 24.0, 0.0, 8.0, 8.0, -8.0])
+    assert _run_on_grid(prod, "trunc") == prod.sum() and O.run_truncation_bound(prod) == 0.0
+
+
+def test_fp8_attention_allowance_covers_grid_emulation_end_to_end():
+    """Through the attention oracle: with q = 0 every p is 1 and Pt = e4m3(256) = 256, so the FP8 P.V of channel c is
+    a sum of 256 Vt over runs of 8 keys; the emulated grid sum lies within the oracle's allowance of its exact sum,
+    and on channels built to lose the most the allowance is attained."""
+    g = np.random.default_rng(32)
+    B, Sq, Sk, H, D = 1, 3, 128, 1, 64
+    q = O.QK(np.zeros((B, Sq, H, D), np.int8), np.full((B, H, 1), 0.01, np.float32), 0, 64)
+    k = O.QK(g.integers(-127, 128, size=(B, Sk, H, D)).astype(np.int8), np.full((B, H, 2), 0.02, np.float32), 0, 64)
+    vals = _e4m3_values()
+    vt = g.choice(vals, size=(B, Sk, H, D))
+    # channels 0..7: every run = one 448 and seven small values of one sign below its grid step (2^-5 at 448);
+    # channels 8..15 the same with mixed signs (the truncations then partly cancel)
+    small = vals[(vals > 0) & (vals < 2.0 ** -5)]
+    for c in range(16):
+        for r0 in range(0, Sk, 8):
+            vt[0, r0, 0, c] = 448.0
+            sign = (1.0 if c < 4 else -1.0) if c < 8 else g.choice([-1.0, 1.0], 7)
+            vt[0, r0 + 1:r0 + 8, 0, c] = g.choice(small, 7) * sign
+    codes = np.vectorize(O.f32_to_e4m3)(vt.astype(np.float32)).astype(np.uint8)
+    assert np.array_equal(np.vectorize(O.e4m3_value)(codes), vt)
+    vs = np.full((B, H, D), 0.5, np.float32)
+    out, lse, allow = O.attn(q, k, codes, fp8=True, vs=vs, kv_tile=128, flip_rel=0.0)
+    f = 0.5 / (256.0 * Sk)
+    exact = vt[0, :, 0, :].sum(axis=0) * 256.0 * f
+    np.testing.assert_allclose(out[0, 0, 0], exact, rtol=1e-13, atol=1e-15)
+    emu = np.array([sum(_run_on_grid(256.0 * vt[0, r0:r0 + 8, 0, c], "trunc") for r0 in range(0, Sk, 8))
+                    for c in range(D)]) * f
+    err = np.abs(emu - out[0, 0, 0])
+    assert (err <= allow[0, 0, 0] * (1 + 1e-12) + 1e-18).all()
+    np.testing.assert_allclose(err[:8], allow[0, 0, 0, :8], rtol=1e-12)   # attained where built to be
+    assert err[:8].min() > 0
 
 
 def test_attention_special_cases():
