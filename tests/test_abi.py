@@ -245,6 +245,31 @@ def test_paged_bindings_reject_wrong_out_dtype():
         sq.sq_paged_decode(q[:2], kc, ks, kc, ks, bt, lens, 64, 0.125, out=torch.zeros((2, 8, 128), dtype=torch.float64))
 
 
+def test_prefix_merge_binding_rejects_wrong_tensors():
+    """The q8 prefix merge reads and writes FP32 (out, lse): a bf16 out (the core's bf16 output mode) or a mis-shaped
+    lse, mean or scale tensor is rejected by the binding before any library call (CPU tensors suffice)."""
+    import torch
+    B, S, H, Hk, D, P = 1, 10, 4, 2, 128, 32
+    q = sq.QK(torch.zeros((B, S, H, D), dtype=torch.int8), torch.zeros((B, H, 1), dtype=torch.float32), 0, 64)
+    pf = sq.Q8Prefix(torch.zeros((1, P, Hk, D), dtype=torch.int8), torch.zeros((1, P, Hk, D // 32), dtype=torch.float16),
+                     torch.zeros((1, P, Hk, D), dtype=torch.int8), torch.zeros((1, P, Hk, D // 32), dtype=torch.float16))
+    out = torch.zeros((B, S, H, D), dtype=torch.float32)
+    lse = torch.zeros((B, H, S), dtype=torch.float32)
+    mu = torch.zeros((B, Hk, D), dtype=torch.float32)
+    bad = [
+        dict(out=out.to(torch.bfloat16)), dict(out=out[:, :5]), dict(lse=lse.to(torch.float16)), dict(lse=lse[:, :2]),
+        dict(mu=mu.double()), dict(mu=mu[:, :1]),
+        dict(pf=sq.Q8Prefix(pf.k, pf.k_scale.float(), pf.v, pf.v_scale)),
+        dict(pf=sq.Q8Prefix(pf.k, pf.k_scale, pf.v.to(torch.uint8), pf.v_scale)),
+        dict(pf=sq.Q8Prefix(pf.k[:, :, :1], pf.k_scale, pf.v, pf.v_scale)),
+    ]
+    for b in bad:
+        a = dict(out=out, lse=lse, mu=mu, pf=pf)
+        a.update(b)
+        with pytest.raises(ValueError):
+            sq.sq_attn_prefix_lse_merge(q, a["pf"], a["mu"], a["out"], a["lse"])
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """Without libsq.so every entry point raises: there is no CPU fallback."""
     monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "libsq.so"))

@@ -72,8 +72,9 @@ def test_prefix_merge_empty_prefix_keeps_projected_pass():
     e8 = np.zeros((1, 0, 2, 128), np.int8)
     e16 = np.zeros((1, 0, 2, 4), np.uint16)
     out, lse = dev(out_in.copy()), dev(lse_in.copy())
-    sq.sq_attn_prefix_lse_merge(sq.QK(dev(qc), dev(qs), 0, 64), sq.Q8Prefix(dev(e8), dev(e16.view(np.int16)),
-                                dev(e8), dev(e16.view(np.int16))), None, out, lse)
+    f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
+    sq.sq_attn_prefix_lse_merge(sq.QK(dev(qc), dev(qs), 0, 64), sq.Q8Prefix(dev(e8), f16(e16), dev(e8), f16(e16)),
+                                None, out, lse)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(out), out_in)
     np.testing.assert_array_equal(host(lse), lse_in)
