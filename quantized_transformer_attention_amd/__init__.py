@@ -349,21 +349,24 @@ def sq_attn_prefix_lse_merge(q: QK, prefix: Q8Prefix, k_mean: Optional[torch.Ten
     """The q8 prefix pass merged in place into (out, lse) of the projected-key pass: out FP32 (B, Sq, H, D) and lse
     FP32 (B, H, Sq), both read and written (the merge keeps FP32); k_mean FP32 (B, Hk, D) or None."""
     B, Sq, H, D = q.codes.shape
-    if out.dtype != torch.float32 or out.dim() != 4 or tuple(out.shape) != (B, Sq, H, D) or out.stride(3) != 1:
+    def _inner(t, d):   # contiguous along dim d (an empty tensor has no strides to speak of)
+        return t.numel() == 0 or t.stride(d) == 1
+
+    if out.dtype != torch.float32 or out.dim() != 4 or tuple(out.shape) != (B, Sq, H, D) or not _inner(out, 3):
         raise ValueError("out: FP32 (B, Sq, H, D) of the queries, channels contiguous (the merge reads and writes FP32)")
-    if lse.dtype != torch.float32 or lse.dim() != 3 or tuple(lse.shape) != (B, H, Sq) or lse.stride(2) != 1:
+    if lse.dtype != torch.float32 or lse.dim() != 3 or tuple(lse.shape) != (B, H, Sq) or not _inner(lse, 2):
         raise ValueError("lse: FP32 (B, H, Sq), queries contiguous")
     Bp, P, Hk, Dp = prefix.k.shape
     if Dp != D or H % Hk != 0 or Bp not in (1, B):
         raise ValueError("prefix: (1|B, P, Hk, D) with the queries' D and H a multiple of Hk")
     for t, name in ((prefix.k, "k"), (prefix.v, "v")):
-        if t.dtype != torch.int8 or tuple(t.shape) != (Bp, P, Hk, D) or t.stride(3) != 1:
+        if t.dtype != torch.int8 or tuple(t.shape) != (Bp, P, Hk, D) or not _inner(t, 3):
             raise ValueError("prefix %s: int8 (1|B, P, Hk, D), channels contiguous" % name)
     for t, name in ((prefix.k_scale, "k_scale"), (prefix.v_scale, "v_scale")):
-        if t.dtype != torch.float16 or tuple(t.shape) != (Bp, P, Hk, D // 32) or t.stride(3) != 1:
+        if t.dtype != torch.float16 or tuple(t.shape) != (Bp, P, Hk, D // 32) or not _inner(t, 3):
             raise ValueError("prefix %s: FP16 (1|B, P, Hk, D/32), groups contiguous" % name)
     if k_mean is not None and (k_mean.dtype != torch.float32 or tuple(k_mean.shape) != (B, Hk, D) or
-                               k_mean.stride(2) != 1):
+                               not _inner(k_mean, 2)):
         raise ValueError("k_mean: FP32 (B, Hk, D), channels contiguous")
     dev = q.codes.device
     qc, pc = q.c(), prefix.c()

@@ -20,8 +20,10 @@
 //    overflows); one MFMA per 32-channel q8 group, whose dot then meets its FP16 key scale
 //    in FP32. Scores (log2 units) go to LDS.
 //  * P.V: p = 2^(s - M) against the segment max M (no rescaling in the loop); the value
-//    scale is folded into the weight, P' = f16(p * vs) per 32-channel group, and V codes
-//    are staged in LDS and read back transposed (ds_read_b64_tr_b8:
+//    scale is folded into the weight, P' = f16(p * vs * 2^e) per 32-channel group, with 2^e
+//    per wave putting the wave's largest value scale in [2^14, 2^15) (small values would
+//    otherwise give weights in f16's subnormal range) and undone exactly on the FP32
+//    accumulator; V codes are staged in LDS and read back transposed (ds_read_b64_tr_b8:
 //    8 positions of one channel per lane), widened exactly to f16.
 //  * every load of a wave is issued up front and unconditionally (no per-lane guard, which
 //    would make each load wait for the one before).
@@ -177,12 +179,24 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     // sequence or on an unread page)
 #pragma unroll
     for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(vst[w] + 1024 * r + 16 * l) = vraw[r];
+    // value scales times 2^esh: the wave's largest |scale| lands in [2^14, 2^15), so the f16 weights
+    // p vs 2^esh <= 2^15 stay normal for the keys that matter; o is multiplied by 2^-esh after the loop
+    int esh = 0;
     {
         const bool okv = rowbase[l >> 4] >= 0 && wp0 + l < s1;
         const h2 s01 = __builtin_bit_cast(h2, vsr.x), s23 = __builtin_bit_cast(h2, vsr.y);
-        vsf[w][l] = okv ? make_float4(static_cast<float>(s01[0]), static_cast<float>(s01[1]), static_cast<float>(s23[0]),
+        float4 sf = okv ? make_float4(static_cast<float>(s01[0]), static_cast<float>(s01[1]), static_cast<float>(s23[0]),
                                       static_cast<float>(s23[1]))
                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float mx = fmaxf(fmaxf(fabsf(sf.x), fabsf(sf.y)), fmaxf(fabsf(sf.z), fabsf(sf.w)));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+        esh = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+        sf.x = __builtin_amdgcn_ldexpf(sf.x, esh);
+        sf.y = __builtin_amdgcn_ldexpf(sf.y, esh);
+        sf.z = __builtin_amdgcn_ldexpf(sf.z, esh);
+        sf.w = __builtin_amdgcn_ldexpf(sf.w, esh);
+        vsf[w][l] = sf;
     }
     __syncthreads();
 
@@ -244,6 +258,11 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     }
     lsum += shfl_xor(lsum, 16);
     lsum += shfl_xor(lsum, 32);
+    // undo the value-scale factor (exact: a power of two on FP32)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[ct][i] = __builtin_amdgcn_ldexpf(o[ct][i], -esh);
 
     // ---- the 4 waves' partials (same max) summed; lane (j, lc) of o[ct] holds heads 4 j + i, channel 16 ct + lc
     float* red = reinterpret_cast<float*>(vst[w]);   // this wave's own rows: read by nobody else

@@ -11,19 +11,24 @@
 //
 // Design (one workgroup = NW waves = 32 NW rows = 32 NW / G tokens x G heads of one kv head;
 // 64-key tiles = 4 pages):
-//  * K and V tiles are dequantized once per workgroup: the int8 codes of a slot row are
-//    widened exactly to f16 and multiplied by their FP16 group scale (one f16 rounding),
-//    then written to LDS key-major (256 bytes per key, 16-byte slots XOR-swizzled). The
-//    next tile's codes and scales are loaded into registers while the current tile is
-//    processed; the block-table entries of the tile after it are read (scalar) one step
-//    earlier still.
+//  * K and V tiles are staged once per workgroup, key-major in LDS (256 bytes per key, 16-byte
+//    slots XOR-swizzled): K as its int8 codes widened exactly to f16, with its FP16 group
+//    scales as FP32 beside them; V as an exact pair of f16 values per element, hi = f16(code
+//    vs) and lo = code vs - hi (one fused multiply-add: the remainder fits in f16), so that
+//    neither K nor V is rounded. The next tile's codes and scales are loaded into registers
+//    while the current tile is processed; the block-table entries of the tile after it are
+//    read (scalar) one step earlier still.
 //  * q is carried as f16 after an exact power-of-two rescale per row (its largest |q| in
 //    [2^14, 2^15)), undone exactly in the row's score scale.
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_f16: K rows are permuted in LDS (key kappa = 16 G +
-//    4 t + i to row 16 t + 4 G + i) so that lane group g ends up holding the 16 consecutive
-//    keys [16 g, 16 g + 16) of one query row: those registers, as f16, are the A operand of
-//    P.V, whose B operand (8 keys of one channel per lane) is read from the key-major V
-//    tile by two transposing ds_read_b64_tr_b16.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_f16, one product per 32-channel q8 group (exact
+//    f16 products, FP32 sums) meeting its key scale in FP32: s = sum_g dot_g ks_g. K rows are
+//    permuted in LDS (key kappa = 16 G + 4 t + i to row 16 t + 4 G + i) so that lane group g
+//    ends up holding the 16 consecutive keys [16 g, 16 g + 16) of one query row: those
+//    registers, as f16, are the A operand of P.V, whose B operands (8 keys of one channel per
+//    lane, hi and lo) are read from the key-major V tiles by transposing ds_read_b64_tr_b16.
+//  * the softmax denominator is accumulated by the same matrix units from the same f16 P: one
+//    more P.V product against a column of ones, so out = acc / l is a weighted mean whose
+//    weights are exactly the P that multiplied the values (a one-key row returns its value).
 //  * causal: a workgroup reads the tiles up to its last row's end; a wave masks only the
 //    tiles that cross its rows' diagonal and skips those past its last row.
 //  * the reference max of a row trails its running max by at most 8 (base 2): the
@@ -42,8 +47,9 @@ constexpr int kD = 128, kBS = 16, kKT = 64;
 constexpr float kLag = 8.0f;                // how far a row's reference max may trail its max
 constexpr int kNQ = 2, kNT = kKT / 16, kNC = kD / 32, kNCT = kD / 16;
 constexpr int kRowB = 2 * kD;               // one f16 key row in LDS
-constexpr int kTileB = kKT * kRowB;         // 16 KB per tile and tensor
-constexpr int kBufB = 2 * kTileB;           // K tile then V tile
+constexpr int kTileB = kKT * kRowB;         // 16 KB per tile and f16 tensor
+constexpr int kVHi = kTileB, kVLo = 2 * kTileB, kKs = 3 * kTileB;   // buffer: K codes, V hi, V lo, K scales
+constexpr int kBufB = 3 * kTileB + kKT * kNC * 4;
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -59,9 +65,12 @@ __device__ __forceinline__ int k_row(int kappa) { return 16 * ((kappa >> 2) & 3)
 __device__ __forceinline__ int k_slot(int row, int slot) { return slot ^ (row & 15); }
 __device__ __forceinline__ int v_slot(int key, int slot) { return slot ^ ((key & 3) | ((key >> 2) & 12)); }
 
-__device__ __forceinline__ v8h scale8(v8h x, _Float16 s) {
+// x s as an exact pair: hi = f16(x s), lo = x s - hi (x an integer code, s an f16 scale: the product
+// has at most 18 significant bits, so the remainder of its f16 rounding is an f16 number)
+__device__ __forceinline__ void scale8_pair(v8h x, _Float16 s, v8h& hi, v8h& lo) {
     const v8h sv = {s, s, s, s, s, s, s, s};
-    return x * sv;
+    hi = x * sv;
+    lo = __builtin_elementwise_fma(x, sv, -hi);
 }
 
 template <int G, int NW>
@@ -107,8 +116,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
 
     // ---- q rows: row r = 32 w + 16 n + lq is token r / G, head r % G; per-row power-of-two rescale
     v8h qop[kNQ][kNC];
-    float cr[kNQ], m_run[kNQ], l_run[kNQ];
-    v4f o[kNQ][kNCT];
+    float cr[kNQ], m_run[kNQ];
+    v4f o[kNQ][kNCT], ol[kNQ];   // ol: the denominators of the rows o holds (P against a column of ones)
 #pragma unroll
     for (int n = 0; n < kNQ; ++n) {
         const int r = 32 * w + 16 * n + lq;
@@ -140,9 +149,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
             for (int e = 0; e < 8; ++e) qop[n][c][e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[c][e], sh));
         cr[n] = __builtin_amdgcn_ldexpf(a.scale, -sh);
         m_run[n] = a.sinks ? a.sinks[h] * 1.44269504f : -__builtin_inff();
-        l_run[n] = (a.sinks && g == 0) ? 1.0f : 0.0f;
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct) o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        // a sink is one more term 2^(sink - m) = 1 of every row's denominator (its head is a.sinks' index of
+        // row 4 g + i, whose sink starts its running max)
+        const float l0 = a.sinks ? 1.0f : 0.0f;
+        ol[n] = v4f{l0, l0, l0, l0};
     }
 
     // ---- staging: thread tid takes 16 channels (part) of keys kappa_u = tid / 8 + 8 NW u of a tile;
@@ -173,16 +185,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
         for (int u = 0; u < U; ++u) {
             const int kappa = key0 + 8 * NW * u;
             const bool live = kbase + kappa < L;
-            const _Float16 ks = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(ksr[u])) : static_cast<_Float16>(0.0f);
+            const float ks = live ? f16_to_f32(static_cast<uint16_t>(ksr[u])) : 0.0f;
             const _Float16 vs = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsr[u])) : static_cast<_Float16>(0.0f);
             const v4u kr4 = kraw[u], vr4 = vraw[u];
-            const v8h k0 = scale8(i8x8_to_f16(kr4[0], kr4[1]), ks), k1 = scale8(i8x8_to_f16(kr4[2], kr4[3]), ks);
-            const v8h v0 = scale8(i8x8_to_f16(vr4[0], vr4[1]), vs), v1 = scale8(i8x8_to_f16(vr4[2], vr4[3]), vs);
+            const v8h k0 = i8x8_to_f16(kr4[0], kr4[1]), k1 = i8x8_to_f16(kr4[2], kr4[3]);
+            v8h vh0, vl0, vh1, vl1;
+            scale8_pair(i8x8_to_f16(vr4[0], vr4[1]), vs, vh0, vl0);
+            scale8_pair(i8x8_to_f16(vr4[2], vr4[3]), vs, vh1, vl1);
             const int kr = k_row(kappa);
             *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part) * 16) = k0;
             *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part + 1) * 16) = k1;
-            *reinterpret_cast<v8h*>(buf + kTileB + kappa * kRowB + v_slot(kappa, 2 * part) * 16) = v0;
-            *reinterpret_cast<v8h*>(buf + kTileB + kappa * kRowB + v_slot(kappa, 2 * part + 1) * 16) = v1;
+            // the scale of group part / 2 of key kappa (both threads of the group hold it; the even one stores)
+            if ((part & 1) == 0) reinterpret_cast<float*>(buf + kKs)[kappa * kNC + (part >> 1)] = ks;
+            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot(kappa, 2 * part) * 16) = vh0;
+            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot(kappa, 2 * part + 1) * 16) = vh1;
+            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot(kappa, 2 * part) * 16) = vl0;
+            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot(kappa, 2 * part + 1) * 16) = vl1;
         }
     };
 
@@ -195,15 +213,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
             // fresh lane offsets per n: the first tile's K reads are not kept in registers for the second
             asm volatile("" : "+v"(lane));
             const int klq = lane & 15, kg = lane >> 4;
+            const float4* ksc = reinterpret_cast<const float4*>(buf + kKs);   // [key] -> 4 group scales
             v4f s[kNT];
 #pragma unroll
             for (int t = 0; t < kNT; ++t) {
                 const int row = 16 * t + klq;
+                v4f dg[kNC];
 #pragma unroll
                 for (int c = 0; c < kNC; ++c) {
                     const v8h kop = *reinterpret_cast<const v8h*>(buf + row * kRowB + k_slot(row, 4 * c + kg) * 16);
-                    s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[n][c], c == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : s[t],
-                                                                  0, 0, 0);
+                    dg[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[n][c], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                }
+                // element i is key 16 kg + 4 t + i: its group dots meet its group scales in FP32
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 kq = ksc[16 * kg + 4 * t + i];
+                    float sv = dg[0][i] * kq.x;
+                    sv = __builtin_fmaf(dg[1][i], kq.y, sv);
+                    sv = __builtin_fmaf(dg[2][i], kq.z, sv);
+                    s[t][i] = __builtin_fmaf(dg[3][i], kq.w, sv);
                 }
             }
             if (masked) {
@@ -232,47 +260,54 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
                 const float mn = fmaxf(mo, ms);
                 const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
                 m_run[n] = mn;
-                l_run[n] *= alpha;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float ai = __shfl(alpha, 4 * g + i, kWave);
 #pragma unroll
                     for (int ct = 0; ct < kNCT; ++ct) o[n][ct][i] *= ai;
+                    ol[n][i] *= ai;
                 }
             }
             // every row sees key 0 in the first tile, so mref is finite from there on and a masked
             // score (-inf) gives p = 2^-inf = 0 exactly
             const float mref = m_run[n];
-            float lsum = 0.0f;
 #pragma unroll
             for (int t = 0; t < kNT; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], cr[n], -mref));
-                    lsum += p;
                     pf[n][t >> 1][4 * (t & 1) + i] = static_cast<_Float16>(p);
                 }
-            l_run[n] += lsum;
         }
         // acc += P V: B operand = keys 16 g + 8 u + 4 h + k (k = lq / 4) of channels 16 ct + 4 (lq % 4) ..
         // + 3, transposed so that lane lq receives channel 16 ct + lq of those 4 keys
-        const uint8_t* vt = buf + kTileB;
+        auto vop_of = [&](const uint8_t* vt, int ct, int u) {
+            v4h half[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int key = 16 * g + 8 * u + 4 * h + (lq >> 2), m = lq & 3;
+                const uint8_t* p = vt + key * kRowB + v_slot(key, 2 * ct + (m >> 1)) * 16 + 8 * (m & 1);
+                half[h] = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s_p)(p)));
+            }
+            return v8h{half[0][0], half[0][1], half[0][2], half[0][3], half[1][0], half[1][1], half[1][2], half[1][3]};
+        };
 #pragma unroll
         for (int ct = 0; ct < kNCT; ++ct)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                v4h half[2];
+                const v8h vhi = vop_of(buf + kVHi, ct, u), vlo = vop_of(buf + kVLo, ct, u);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int key = 16 * g + 8 * u + 4 * h + (lq >> 2), m = lq & 3;
-                    const uint8_t* p = vt + key * kRowB + v_slot(key, 2 * ct + (m >> 1)) * 16 + 8 * (m & 1);
-                    half[h] = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s_p)(p)));
+                for (int n = 0; n < kNQ; ++n) {
+                    o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], vhi, o[n][ct], 0, 0, 0);
+                    o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], vlo, o[n][ct], 0, 0, 0);
                 }
-                const v8h vop = {half[0][0], half[0][1], half[0][2], half[0][3], half[1][0], half[1][1], half[1][2], half[1][3]};
-#pragma unroll
-                for (int n = 0; n < kNQ; ++n)
-                    o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], vop, o[n][ct], 0, 0, 0);
             }
+        const _Float16 one = static_cast<_Float16>(1.0f);
+        const v8h ones = {one, one, one, one, one, one, one, one};
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int n = 0; n < kNQ; ++n) ol[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], ones, ol[n], 0, 0, 0);
     };
 
     // ---- key loop: tile j is processed from buffer j % 2 while tile j + 1's codes are in flight;
@@ -299,15 +334,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
         __syncthreads();
     }
 
-    // ---- epilogue: l over the 4 lane groups, out = acc / l
+    // ---- epilogue: out = acc / l (l of row 4 g + i is in every lane of group g)
 #pragma unroll
     for (int n = 0; n < kNQ; ++n) {
-        float lt = l_run[n];
-        lt = lt + shfl_xor(lt, 16);
-        lt = lt + shfl_xor(lt, 32);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float inv = 1.0f / __shfl(lt, 4 * g + i, kWave);
+            const float inv = 1.0f / ol[n][i];
             const int r = 32 * w + 16 * n + 4 * g + i;
             const int j = j0 + r / G;
             if (j >= qlen || qs0 + j < 0 || qs0 + j >= a.T) continue;

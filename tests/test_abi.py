@@ -268,6 +268,18 @@ def test_prefix_merge_binding_rejects_wrong_tensors():
         a.update(b)
         with pytest.raises(ValueError):
             sq.sq_attn_prefix_lse_merge(q, a["pf"], a["mu"], a["out"], a["lse"])
+    # an empty prefix (zero strides) passes the binding's checks and reaches the library, which needs a GPU stream:
+    # only the binding's own checks are exercised here
+    import numpy as np
+    e8 = torch.from_numpy(np.zeros((1, 0, Hk, D), np.int8))
+    e16 = torch.from_numpy(np.zeros((1, 0, Hk, D // 32), np.float16))
+    assert e8.stride() == (0, 0, 0, 0)
+    try:
+        sq.sq_attn_prefix_lse_merge(q, sq.Q8Prefix(e8, e16, e8, e16), None, out, lse)
+    except ValueError as e:
+        raise AssertionError("an empty prefix is valid: %s" % e)
+    except Exception:
+        pass   # past the binding: the CPU has no HIP stream
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -108,7 +108,7 @@ def test_paged_decode_and_prefill_bf16_out():
     np.testing.assert_array_equal(_bits(d16), _rne_bits(d32))
     pref = O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale)
     dref = O.paged_decode(q[last], kc, ks, vc, vs, bt, lens, scale)
-    for got, ref, tol, what in ((p16, pref, 6e-3, "prefill"), (d16, dref, 2e-3, "decode")):
+    for got, ref, tol, what in ((p16, pref, 2e-3, "prefill"), (d16, dref, 2e-3, "decode")):
         ref = ref.astype(np.float64)
         rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
         err = np.abs(_as_f32(got) - ref)

@@ -1,10 +1,12 @@
 """GPU parity of the paged causal prefill over a q8 cache (sq_paged_prefill) against the oracle's binary64
 [impl] _prefill_torch_from_cache.
 
-Tolerance (from the kernel's arithmetic: keys, values and P rounded once to f16, relative <= 2^-11 each, FP32
-softmax and accumulation): per (token, head) row, ||gpu - ref|| <= 2e-3 ||ref|| and every element within
-6e-3 rms(row). A model of those roundings on the CPU gives at most 6.4e-4 and 2.1e-3 on these inputs; a key
-lost or gained moves a row by about 1 / sqrt(keys) of its norm."""
+Tolerance: every element within 2e-3 rms(row) and ||gpu - ref|| <= 2e-3 ||ref|| per (token, head) row, the row
+being that query's own attention output (the rows of a batch attend 1 to thousands of keys, so their output RMS
+differs by orders of magnitude). The kernel's arithmetic: keys and values exact (codes widened to f16, key scales
+applied in FP32 per 32-channel dot, values as exact f16 pairs), P rounded once to f16 (relative <= 2^-11), its
+denominator summed from the same rounded P; a CPU emulation of that arithmetic gives at most 1.5e-3 per element
+on these inputs."""
 import math
 
 import numpy as np
@@ -18,7 +20,7 @@ from tests._util import dev, dev_bf16, host
 
 pytestmark = pytest.mark.gpu
 
-ROW_REL, ELEM_REL = 2e-3, 6e-3
+ROW_REL, ELEM_REL = 2e-3, 2e-3
 
 
 def check_rows(got, ref, what=""):
@@ -30,6 +32,8 @@ def check_rows(got, ref, what=""):
     bad = np.abs(err) > ELEM_REL * rms
     assert rel.max() <= ROW_REL, "%s: row relative error %.3g (row %s)" % (what, rel.max(), np.unravel_index(rel.argmax(), rel.shape))
     assert not bad.any(), "%s: %d elements beyond %.0e rms(row)" % (what, int(bad.sum()), ELEM_REL)
+    print("%s: row error %.3g, element error %.3g rms(row)" % (what, rel.max(), float((np.abs(err) / rms).max())),
+          flush=True)
     return float(rel.max())
 
 

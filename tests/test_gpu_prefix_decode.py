@@ -138,7 +138,7 @@ def test_cfg3_joint_with_q8_prefix_full_size():
 
 
 # ------------------------------------------------------------------------------------------------ paged decode
-def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3):
+def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3, v_sigma=1.0):
     g = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int32)
     pages = (lens + bs - 1) // bs
@@ -151,7 +151,7 @@ def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3):
         bt[n, :p] = perm[o:o + p]
         o += p
     kx = g.standard_normal(size=(NB, bs, Hk, D), dtype=np.float32)
-    vx = g.standard_normal(size=(NB, bs, Hk, D), dtype=np.float32)
+    vx = g.standard_normal(size=(NB, bs, Hk, D), dtype=np.float32) * np.float32(v_sigma)
     kc, ks = _q8(kx)
     vc, vs = _q8(vx)
     q = gen.normal_bf16((len(lens), 1, Hq, D), g).reshape(len(lens), Hq, D)
@@ -176,6 +176,19 @@ def test_paged_decode_parity(Hq, Hk):
     got = _gpu_decode(q, kc, ks, vc, vs, bt, lens, scale)
     check_float(got, ref, None, what="decode out")
     assert cosine(got, ref) >= 0.999999
+
+
+@pytest.mark.parametrize("v_sigma", [0.01, 0.003, 1e-4])
+def test_paged_decode_small_values(v_sigma):
+    """Values ~N(0, sigma^2): their FP16 scales are small, and the P.V weights p * vs would fall into f16's subnormal
+    range without the per-wave power-of-two rescale of the scales; held to the same bound."""
+    lens = [1, 17, 300, 1100, 4096]
+    print("decode small values sigma %g" % v_sigma, flush=True)
+    q, kc, ks, vc, vs, bt, lens = _decode_case(lens, 8, 2, 3100, v_sigma=v_sigma)
+    scale = 1.0 / np.sqrt(128.0)
+    ref = O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale)
+    got = _gpu_decode(q, kc, ks, vc, vs, bt, lens, scale)
+    check_float(got, ref, None, what="decode out sigma %g" % v_sigma)
 
 
 def test_paged_decode_block_permutation_is_bit_identical():
