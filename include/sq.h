@@ -22,7 +22,9 @@
  *  - Memory: every tensor pointer is a DEVICE pointer owned by the caller. The
  *    library never allocates, frees or keeps device memory; scratch memory is a
  *    caller-provided workspace whose size the matching *_workspace_bytes query
- *    returns (0 means no workspace is needed; the pointer may then be NULL).
+ *    returns (0 means no workspace is needed; the pointer may then be NULL). The one
+ *    exception is sq_paged_decode_noalloc, whose scratch is a fixed array of the
+ *    library's own on each GPU it runs on (SQ_DECODE_SCRATCH_BYTES).
  *  - Strides are in elements. The last (channel) dimension of every row view is
  *    contiguous. Row bases must be 16-byte aligned (SQ_ERR_ALIGN otherwise).
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call only
@@ -287,6 +289,25 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
                     int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
                     sq_dtype out_dtype, int64_t on, int64_t oh, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- D, without allocation. For callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Computes exactly what sq_paged_decode computes (the same kernels, the same
+ * arguments without ws / ws_bytes), with the segment partials in a file-scope device
+ * array of SQ_DECODE_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends. Nothing is allocated by the call. Its first call on a device looks the
+ * array's address up (hipGetSymbolAddress) with that device current. A call whose
+ * partials, sq_paged_decode_workspace_bytes(num_seqs, Hq, D, max_seq_len), exceed the
+ * array returns SQ_ERR_WORKSPACE before anything is enqueued (64 MiB holds e.g. 64
+ * sequences x 32 query heads up to 16,128 positions). All calls on one GPU share the
+ * array: calls whose work may overlap on that GPU (other streams, other threads) race and
+ * must be ordered by the caller. No part of the array needs to start at zero. */
+#define SQ_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+int sq_paged_decode_noalloc(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
+                            const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
+                            const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
+                            int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
+                            sq_dtype out_dtype, int64_t on, int64_t oh, void* stream);
 
 /* ---- D3. Paged causal prefill over a q8 cache [impl] _prefill_torch_from_cache,
  * _cache_seq, _sdpa_one (per sequence, mask k_pos <= key_offset + q_pos); [tq] unified

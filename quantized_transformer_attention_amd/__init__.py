@@ -73,7 +73,7 @@ ABI_VERSION = 3  # SQ_ABI_VERSION of the sq.h these argument lists follow
 EXPORTS = ["sq_scale_count", "sq_norm_stats", "sq_kmean_workspace_bytes", "sq_kmean", "sq_quant_qk_workspace_bytes",
            "sq_quant_qk", "sq_quant_v_fp8_workspace_bytes", "sq_quant_v_fp8", "sq_attn_workspace_bytes", "sq_attn",
            "sq_attn_prefix_lse_merge_workspace_bytes", "sq_attn_prefix_lse_merge", "sq_paged_decode_workspace_bytes",
-           "sq_paged_decode", "sq_paged_prefill", "sq_q8_cache_write", "sq_lse_merge", "sq_status_string", "sq_last_error", "sq_abi_version"]
+           "sq_paged_decode", "sq_paged_decode_noalloc", "sq_paged_prefill", "sq_q8_cache_write", "sq_lse_merge", "sq_status_string", "sq_last_error", "sq_abi_version"]
 
 
 def lib():
@@ -107,6 +107,8 @@ def lib():
         L.sq_paged_decode_workspace_bytes.restype = _sz
         L.sq_paged_decode.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
                                       _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp, _sz, _vp]
+        L.sq_paged_decode_noalloc.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
+                                              _int, _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp]
         L.sq_paged_prefill.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
                                        _vp, _int, _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp]
         L.sq_lse_merge.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
@@ -425,6 +427,29 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
                              out.stride(0), out.stride(1),
                              _ptr(ws), nb,
                              _stream(dev)))
+    return out
+
+
+DECODE_SCRATCH_BYTES = 64 << 20   # SQ_DECODE_SCRATCH_BYTES
+
+
+def sq_paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tensor, v_cache: torch.Tensor,
+                            v_scale: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                            softmax_scale: float, out: torch.Tensor, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sq_paged_decode without allocation (for callers that cannot allocate: graph capture, serving loops): the
+    segment partials live in the library's own scratch array on the GPU; out (N, Hq, D), FP32 or bf16, is given by
+    the caller and nothing is allocated here either. Calls that overlap on one GPU share that array and race."""
+    _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens)
+    N, Hq, D = q.shape
+    NB, bs, Hk, _ = k_cache.shape
+    if sinks is not None:
+        assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == Hq, "sinks: FP32 (Hq,)"
+    assert out.dim() == 3 and tuple(out.shape) == (N, Hq, D) and out.stride(2) == 1, "out: (N, Hq, D), channels contiguous"
+    L = lib()
+    _check(L.sq_paged_decode_noalloc(_ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                                     _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0),
+                                     _ptr(seq_lens), N, max_seq_len, Hq, D, softmax_scale, _ptr(sinks), _ptr(out),
+                                     _out_dtype(out), out.stride(0), out.stride(1), _stream(q.device)))
     return out
 
 

@@ -406,13 +406,15 @@ size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_
     return round_up(sizeof(float) * static_cast<size_t>(num_seqs) * Hq * segs * (D + 2));
 }
 
-int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
-                    const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
-                    const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
-                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
-                    sq_dtype out_dtype, int64_t on, int64_t oh, void* ws, size_t ws_bytes, void* stream) {
-    clear_error();
-    const char* what = "sq_paged_decode";
+namespace {
+// Validation of the paged decode's arguments (everything but the workspace) into its kernel arguments.
+// SQ_OK with *empty set when there is nothing to do; a failure sets the detail under the name what.
+int decode_args(const char* what, const void* q, int64_t qn, int64_t qh, const int8_t* k_cache,
+                const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
+                int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
+                int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
+                sq_dtype out_dtype, int64_t on, int64_t oh, DecodeArgs& a, bool* empty) {
+    *empty = false;
     if (num_seqs < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
         return fail(SQ_ERR_SHAPE, "%s: bad sizes (num_seqs %d, Hq %d, Hk %d)", what, num_seqs, Hq, Hk);
     if (D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", what, D);
@@ -421,7 +423,10 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     const int G = Hq / Hk;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(SQ_ERR_UNSUPPORTED, "%s: Hq / Hk = %d (1, 2, 4 or 8)", what, G);
-    if (num_seqs == 0) return SQ_OK;
+    if (num_seqs == 0) {
+        *empty = true;
+        return SQ_OK;
+    }
     if (max_seq_len < 1) return fail(SQ_ERR_SHAPE, "%s: max_seq_len must be >= 1", what);
     if (!q || !k_cache || !k_scale || !v_cache || !v_scale || !block_table || !seq_lens || !out)
         return fail(SQ_ERR_NULL, "%s: a required pointer is NULL", what);
@@ -441,11 +446,7 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
         const int st = check_out(out, out_dtype, what);
         if (st) return st;
     }
-    {
-        const int st = check_ws(ws, ws_bytes, sq_paged_decode_workspace_bytes(num_seqs, Hq, D, max_seq_len), what);
-        if (st) return st;
-    }
-    DecodeArgs a{};
+    a = DecodeArgs{};
     a.q = static_cast<const uint16_t*>(q); a.qn = qn; a.qh = qh;
     a.kc = k_cache; a.ks = k_scale; a.vc = v_cache; a.vs = v_scale;
     a.num_blocks = num_blocks; a.bs = block_size; a.Hk = Hk; a.Hq = Hq; a.D = D;
@@ -455,8 +456,61 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     a.sinks = sinks;
     a.out = static_cast<float*>(out); a.out_bf16 = out_dtype == SQ_BF16;
     a.on = on; a.oh = oh;
-    a.part = static_cast<float*>(ws);
     a.segs = (max_seq_len + kDecodeSeg - 1) / kDecodeSeg;
+    return SQ_OK;
+}
+}  // namespace
+
+int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
+                    const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
+                    const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
+                    int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
+                    sq_dtype out_dtype, int64_t on, int64_t oh, void* ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    const char* what = "sq_paged_decode";
+    DecodeArgs a;
+    bool empty = false;
+    {
+        const int st = decode_args(what, q, qn, qh, k_cache, k_scale, v_cache, v_scale, num_blocks, block_size, Hk,
+                                   block_table, bt_stride, seq_lens, num_seqs, max_seq_len, Hq, D, softmax_scale, sinks,
+                                   out, out_dtype, on, oh, a, &empty);
+        if (st || empty) return st;
+    }
+    {
+        const int st = check_ws(ws, ws_bytes, sq_paged_decode_workspace_bytes(num_seqs, Hq, D, max_seq_len), what);
+        if (st) return st;
+    }
+    a.part = static_cast<float*>(ws);
+    return launch_decode(a, stream);
+}
+
+int sq_paged_decode_noalloc(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
+                            const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
+                            const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
+                            int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
+                            sq_dtype out_dtype, int64_t on, int64_t oh, void* stream) {
+    clear_error();
+    const char* what = "sq_paged_decode_noalloc";
+    DecodeArgs a;
+    bool empty = false;
+    {
+        const int st = decode_args(what, q, qn, qh, k_cache, k_scale, v_cache, v_scale, num_blocks, block_size, Hk,
+                                   block_table, bt_stride, seq_lens, num_seqs, max_seq_len, Hq, D, softmax_scale, sinks,
+                                   out, out_dtype, on, oh, a, &empty);
+        if (st || empty) return st;
+    }
+    const size_t need = sq_paged_decode_workspace_bytes(num_seqs, Hq, D, max_seq_len);
+    if (need > SQ_DECODE_SCRATCH_BYTES)
+        return fail(SQ_ERR_WORKSPACE,
+                    "%s: %d sequences x %d heads up to %d positions need %zu bytes of segment partials, more than the "
+                    "library's scratch array (%zu); call sq_paged_decode with a workspace",
+                    what, num_seqs, Hq, max_seq_len, need, static_cast<size_t>(SQ_DECODE_SCRATCH_BYTES));
+    void* ws = nullptr;
+    {
+        const int st = decode_scratch(&ws);
+        if (st) return st;
+    }
+    a.part = static_cast<float*>(ws);
     return launch_decode(a, stream);
 }
 

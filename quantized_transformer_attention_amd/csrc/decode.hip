@@ -33,8 +33,15 @@
 // read from block 0 instead (never from the bad entry), their scores are -inf and their
 // value scales zero, so a bad table cannot fault the device; with no blocks at all nothing
 // is read and the output is 0.
+#include <atomic>
+
 #include "device.h"
 #include "sq_internal.h"
+
+// Segment partials of sq_paged_decode_noalloc: one array on every GPU the library runs on,
+// held until the process ends. In host code this name is a host-side stand-in, never a device
+// address: host code uses only the address decode_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[SQ_DECODE_SCRATCH_BYTES];
 
 namespace sq {
 namespace {
@@ -359,6 +366,30 @@ __global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
 inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of scratch per device id (null: not looked up)
+}  // namespace
+
+int decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_paged_decode_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SQ_ERR_UNSUPPORTED, "sq_paged_decode_noalloc: device %d (at most %d devices)", dev, kMaxDevices);
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // with this device current: each GPU holds its own copy of the array at its own address
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(SQ_ERR_HIP, "sq_paged_decode_noalloc: hipGetSymbolAddress of the scratch array failed: %s",
+                        hipGetErrorString(e));
+        g_scratch[dev].store(p, std::memory_order_release);   // racing first calls store the same address
+    }
+    *ptr = p;
+    return SQ_OK;
+}
 
 int launch_decode(const DecodeArgs& a, void* stream) {
     if (a.N == 0) return SQ_OK;

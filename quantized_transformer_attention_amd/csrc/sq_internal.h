@@ -217,6 +217,9 @@ int launch_prefix(const PrefixArgs& a, void* stream);
 int launch_lse_merge(const MergeArgs& a, void* stream);
 int launch_cache_write(const CacheWriteArgs& a, bool f32, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
+// The device address of the decode's own scratch array on the current device (looked up once per
+// device); SQ_OK or an SQ_ERR_* code with the detail set.
+int decode_scratch(void** ptr);
 int launch_prefill(const PrefillArgs& a, void* stream);
 constexpr int kPrefillWaves = 8;            // waves per prefill workgroup (32 rows each)
 

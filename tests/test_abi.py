@@ -206,6 +206,23 @@ def test_paged_decode_validation_errors():
     assert _call_decode(ws=None) == -6                     # the segment partials need a workspace
 
 
+def test_paged_decode_noalloc_rejects_oversize_before_any_device_call():
+    """The no-allocation decode refuses, on the host and before any HIP call, work whose segment partials exceed its
+    fixed scratch array (64 sequences x 32 heads x 16,384 positions needs 65 MiB)."""
+    L = sq.lib()
+    assert sq.DECODE_SCRATCH_BYTES == 64 << 20
+    need = L.sq_paged_decode_workspace_bytes(64, 32, 128, 16384)
+    assert need > sq.DECODE_SCRATCH_BYTES >= L.sq_paged_decode_workspace_bytes(64, 32, 128, 16128)
+    st = L.sq_paged_decode_noalloc(0x1000, 32 * 128, 128, 0x2000, 0x3000, 0x4000, 0x5000, 100, 16, 8, 0x6000, 1024,
+                                   0x7000, 64, 16384, 32, 128, 0.088, None, 0x8000, sq.SQ_F32, 32 * 128, 128, None)
+    assert st == -6
+    assert b"scratch" in L.sq_last_error()
+    # a bad argument inside the limit is rejected by the decode's own validation (still no device call)
+    st = L.sq_paged_decode_noalloc(0x1000, 32 * 128, 128, 0x2000, 0x3000, 0x4000, 0x5000, 100, 16, 8, 0x6000, 1024,
+                                   0x7000, 4, 1000, 32, 96, 0.088, None, 0x8000, sq.SQ_F32, 32 * 128, 128, None)
+    assert st == -5
+
+
 def test_paged_bindings_reject_wrong_dtypes():
     """The Python binding checks the paged entry points' tensors before any library call (CPU tensors suffice):
     int64 lengths or a float32 q would otherwise be read as int32 / bf16 by the kernels."""
