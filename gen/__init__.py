@@ -111,7 +111,7 @@ class AttnConfig:
 CFG1 = AttnConfig("tiny", 1, B=1, H=2, Hk=2, Sq=256, Sk=256, D=64, norm="head", q_layout="per_block", q_block=64,
                   k_layout="per_block", k_block=64, pv="bf16", kv_tile=64)
 CFG2 = AttnConfig("video", 2, B=1, H=40, Hk=40, Sq=32760, Sk=32760, D=128, norm="all_heads", q_layout="thread_q",
-                  q_block=32, k_layout="thread_k", k_block=64, pv="fp8", kv_tile=128, outliers=51)
+                  q_block=32, k_layout="thread_k", k_block=64, pv="fp8", kv_tile=64, outliers=51)
 CFG3 = AttnConfig("joint_prefix", 3, B=1, H=24, Hk=24, Sq=8704, Sk=8704, D=128, norm="head", q_layout="per_block",
                   q_block=128, k_layout="per_block", k_block=64, pv="bf16", kv_tile=64, weight_rows=[512, 8192],
                   prefix=4096)

@@ -219,8 +219,8 @@ int sq_quant_v_fp8(const sq_rows* v, uint8_t* codes, int64_t ob, int64_t oh, int
  * sum Pt Vt with Pt = bf16(p) (bf16 v) or e4m3(256 p) (FP8 v); out = acc / l (bf16 v)
  * or acc * vs / (256 l) (FP8 v); lse = m + log2 l (base 2, the scores' log2 units).
  * q rows carry the softmax scale (log2(e)/sqrt(D) through sm_scale). q layouts:
- * PER_BLOCK, THREAD_Q, WARP_Q; k layouts: PER_BLOCK, THREAD_K. kv_tile: 64 or 128
- * (FP8 P.V: 128). out (B, Sq, H, D) at out[b*ob + i*ot + h*oh + c] in elements of
+ * PER_BLOCK, THREAD_Q, WARP_Q; k layouts: PER_BLOCK, THREAD_K. kv_tile: 64 or 128.
+ * out (B, Sq, H, D) at out[b*ob + i*ot + h*oh + c] in elements of
  * out_dtype: SQ_F32, or SQ_BF16 (the FP32 result rounded to nearest even; an option for
  * callers that keep activations in bf16), aligned to its element size (SQ_ERR_ALIGN;
  * another dtype SQ_ERR_UNSUPPORTED); lse FP32 (B, H, Sq) at lse[b*lb + h*lh + i], or NULL.

@@ -247,7 +247,6 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
     if (v->dtype == SQ_BF16 && 2 * k->D * (padded_keys(k->S) + 256) >= kLim)
         return fail(SQ_ERR_UNSUPPORTED, "sq_attn: one kv head's values span more than 2 GiB");
     if (v->dtype == SQ_FP8E4M3) {
-        if (kv_tile != 128) return fail(SQ_ERR_UNSUPPORTED, "sq_attn: FP8 P.V needs kv_tile 128");
         if (v->st != 1) return fail(SQ_ERR_STRIDE, "sq_attn: FP8 values must be channel-major (st == 1)");
         if (!v->scale) return fail(SQ_ERR_NULL, "sq_attn: FP8 values need their per-channel scales");
         if (v->sd < (k->S + 15) / 16 * 16 || v->sd % 16 || v->sb < 0 || v->sh < 0 || v->vsb < 0 || v->vsh < 0)

@@ -6,21 +6,23 @@
 // triton_turboquant_unified_attention.py (kernel_tq_unified_attention_2d: m_j, P,
 // l_j, alpha, acc). [impl] _repeat_kv_for_heads fixes the GQA head mapping.
 //
-// Design (one workgroup = 4 waves = 128 queries of one (b, h); K and V^T tiles of
-// KT keys staged once in LDS and shared by the 4 waves):
-//  * S^T = K Q^T with v_mfma_i32_16x16x64_i8: the 16x16 result puts one query per
-//    lane column (lane % 16) and 4 keys per lane, so the row max and sum over keys
-//    are in-lane plus two cross-lane steps.
-//  * K rows are permuted into LDS so that lane group g (lane / 16) ends up holding
-//    the KT/4 consecutive keys [g KT/4, (g+1) KT/4): those registers are then
-//    already the A operand (P, queries x keys) of the P.V MFMA, and the B operand
-//    (V, keys x channels) is a contiguous run of keys of one channel -- which is why
-//    V is read channel-major (sq_quant_v_fp8 writes FP8 V that way; bf16 V is
-//    staged channel-major by k_v_transpose).
+// Design (one workgroup = 4 waves = 128 queries of one (b, h), 32 per wave; K and V^T
+// tiles of KT keys staged once in LDS by DMA and shared by the 4 waves):
+//  * S^T = K Q^T with v_mfma_i32_32x32x32_i8: the 32x32 result puts one query per lane
+//    (lane % 32) and 16 keys of each 32-key block per lane, the two halves of the wave
+//    (lane / 32) holding different keys, so a row max or sum is in-lane plus one step
+//    across the halves.
+//  * O^T = V^T P^T (channels x queries) with v_mfma_scale_f32_32x32x64_f8f6f4 (FP8) or
+//    v_mfma_f32_32x32x16_bf16: the B operand P^T is, per lane, a run of consecutive keys
+//    of that lane's query -- K rows are permuted into LDS so that the S^T registers of a
+//    lane are exactly those keys, in order, in runs of 8 consecutive keys -- and the A
+//    operand V^T is a run of keys of one channel, which is why V is read channel-major
+//    (sq_quant_v_fp8 writes FP8 V that way; bf16 V is staged channel-major by
+//    k_v_transpose). The output rows of a query stay in its own lane, so rescaling them
+//    needs no exchange, and it is skipped when no row max of the wave moved (alpha = 1).
 //  * The softmax max is taken on the int32 dots per k-scale group (c > 0 makes
 //    RN(a c) monotonic in a), and p = 2^fma(a, c, -m') uses the hardware exp2.
-//  * FP8 P.V: Pt = e4m3(256 p) by a scaled convert (2^-8 scale: exact), one
-//    v_mfma_f32_16x16x128_f8f6f4 per 16 channels per 128 keys.
+//  * FP8 P.V: Pt = e4m3(256 p) by a scaled convert (2^-8 scale: exact).
 #include "device.h"
 #include "sq_internal.h"
 
@@ -29,7 +31,9 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 
@@ -43,28 +47,44 @@ __device__ __forceinline__ int pack_fp8x4_256(float a, float b, float c, float d
 
 template <int D, int KT, bool FP8>
 struct Cfg {
-    static constexpr int NQ = 2;                     // 16-query tiles per wave
-    static constexpr int QPB = 4 * NQ * 16;          // queries per workgroup
-    static constexpr int NT = KT / 16;               // 16-key sub-tiles
-    static constexpr int NC = D / 64;                // 64-channel chunks of Q.K^T
-    static constexpr int NCT = D / 16;               // 16-channel tiles of P.V
-    static constexpr int KQ = KT / 4;                // keys per lane group
+    static constexpr int QPB = 4 * 32;               // queries per workgroup: 4 waves of 32
+    static constexpr int NB = KT / 32;               // 32-key blocks of S^T
+    static constexpr int NCS = D / 32;               // 32-channel steps of Q.K^T (and blocks of O^T)
+    static constexpr int NCH = KT / 64 > 0 ? KT / 64 : 1;   // 64-key chunks (THREAD_K scale blocks)
     static constexpr int VB = FP8 ? 1 : 2;           // bytes per V element
     static constexpr int RBV = KT * VB;              // bytes of one V^T row (one channel)
     static constexpr int KBYTES = KT * D, VBYTES = D * RBV;
     static constexpr int KNS = D / 16, VNS = RBV / 16;   // 16-byte slots per K row and per V^T row
+    // score groups sharing one c: FP8 (64-key chunk, k-scale group q); bf16 (32-key block, q)
+    static constexpr int NG = FP8 ? 4 * NCH : 4 * NB;
 };
 
-// Copies key tile [kbase, kbase + KT) of K (rows permuted: key kappa -> row 16 t + 4 G + i
-// with kappa = G KQ + 4 t + i) and of V^T straight from global memory into LDS with
-// buffer_load_dwordx4 ... lds: lane i of a wave fills bytes [16 i, 16 i + 16) of a 1 KB
-// piece. The buffer resources end at the last valid byte of the (b, kv head) slices, so
-// rows past the end read as zeros (their scores are masked) and can never fault.
+// Key (within the tile) held in K's LDS row rho. Row rho = 32 b + r of 32-key block b with r =
+// 8 j + 4 h + i is output register 4 j + i of the lanes of half h for block b; the keys are chosen
+// so that lane half h holds, in register order, the consecutive keys its P^T operand needs:
+//   FP8 (64 keys per product): block b = 2 s + t gives keys 64 s + 32 h + 16 t + 4 j + i;
+//   bf16 (16 keys per product): block b gives keys 32 b + 16 (j >> 1) + 8 h + 4 (j & 1) + i.
+// Either way 8 consecutive registers (fixed b and j >> 1) hold 8 consecutive keys from a multiple of 8.
+template <bool FP8>
+__host__ __device__ constexpr int kappa_of_row(int rho) {
+    const int b = rho >> 5, r = rho & 31, j = r >> 3, h = (r >> 2) & 1, i = r & 3;
+    return FP8 ? 64 * (b >> 1) + 32 * h + 16 * (b & 1) + 4 * j + i
+               : 32 * b + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
+}
+
+// The k-scale group of output register 4 j + i (any block): THREAD_K group (key mod 8) / 2.
+__host__ __device__ constexpr int kgroup(int j, int i) { return 2 * (j & 1) + (i >> 1); }
+
+// Copies key tile [kbase, kbase + KT) of K (rows permuted as kappa_of_row) and of V^T straight
+// from global memory into LDS with buffer_load_dwordx4 ... lds: lane i of a wave fills bytes
+// [16 i, 16 i + 16) of a 1 KB piece. The buffer resources end at the last valid byte of the
+// (b, kv head) slices, so rows past the end read as zeros (their scores are masked) and can
+// never fault.
 //
-// Wave w fills pieces 4 u + w. Piece 4 u + w starts 4096 u / D rows (K) and 4096 u / RBV
-// rows (V^T) after piece w, a whole number of swizzle periods, so a lane's slot is the same
-// in every piece and its source offset moves by a wave-uniform amount: the per-lane part
-// is computed once (dma_lane_offsets) and a tile costs one add per piece.
+// Wave w fills pieces 4 u + w. Piece 4 u + w starts 4096 u / D rows (K) and 4096 u / RBV rows
+// (V^T) after piece w, a whole number of swizzle periods and of 32-key blocks, so a lane's slot
+// is the same in every piece and its source key moves by kappa_of_row(4096 u / D), a constant:
+// the per-lane part is computed once (dma_lane_offsets) and a tile costs one add per piece.
 template <int D, int KT, bool FP8>
 struct DmaOffsets {
     int k, v;   // byte offsets of this lane's 16 bytes of piece w, relative to tile 0
@@ -73,14 +93,13 @@ struct DmaOffsets {
 template <int D, int KT, bool FP8>
 __device__ __forceinline__ DmaOffsets<D, KT, FP8> dma_lane_offsets(int kst, int vrow, int w, int lane) {
     using C = Cfg<D, KT, FP8>;
-    static_assert((4096 / D) % 16 == 0, "K pieces must advance by whole swizzle periods");
+    static_assert((4096 / D) % 32 == 0, "K pieces must advance by whole blocks and swizzle periods");
     static_assert((4096 / C::RBV) % 16 == 0, "V pieces must advance by whole swizzle periods");
     DmaOffsets<D, KT, FP8> r;
     {
         const int o = 1024 * w + 16 * lane;
         const int row = o / D, ls = swz<C::KNS>(row, (o % D) / 16);
-        const int key = ((row & 15) >> 2) * C::KQ + 4 * (row >> 4) + (row & 3);
-        r.k = key * kst + ls * 16;
+        r.k = kappa_of_row<FP8>(row) * kst + ls * 16;
     }
     {
         const int o = 1024 * w + 16 * lane;
@@ -99,12 +118,11 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buf
     // wave-uniform offsets recomputed per tile (scalar adds) rather than hoisted out of the
     // key loop, where they would crowd the scalar registers into spilling
     asm volatile("" : "+s"(w), "+s"(kst), "+s"(vrow));
-    // piece 4 u + w of K: keys advance by (4096 u / D rows) / 16 rows per 4 keys
     const int kb = kbase * kst;
 #pragma unroll
     for (int u = 0; u < KCH / 4; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lvoid_t*)(kl + 1024 * (4 * u + w)), 16,
-                                                 off.k + kb + (u * (4096 / D) / 4) * kst, 0, 0, 0);
+                                                 off.k + kb + kappa_of_row<FP8>(u * (4096 / D)) * kst, 0, 0, 0);
     const int vb = kbase * C::VB;
 #pragma unroll
     for (int u = 0; u < VCH / 4; ++u)
@@ -112,148 +130,172 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buf
                                                  off.v + vb + (u * (4096 / C::RBV)) * vrow, 0, 0, 0);
 }
 
+// The key scales a lane needs for one tile, raw (FP32): THREAD_K the 4 scales of each 64-key
+// chunk (key t in group (t >> 1) & 3); PER_BLOCK the scale of each 32-key block b at [b >> 1][b & 1]
+// (its keys never straddle a scale block for this lane half). Past the last scale the buffer
+// load gives 0.
+template <int D, int KT, bool FP8>
+struct KScales {
+    v4f c[Cfg<D, KT, FP8>::NCH];
+};
+
+template <int D, int KT, bool FP8>
+__device__ __forceinline__ KScales<D, KT, FP8> load_kscales(__amdgpu_buffer_rsrc_t r, int kbase, int h, int layout,
+                                                              int shift) {
+    using C = Cfg<D, KT, FP8>;
+    KScales<D, KT, FP8> k;
+    if (layout == SQ_LAYOUT_THREAD_K) {
+#pragma unroll
+        for (int ch = 0; ch < C::NCH; ++ch)
+            k.c[ch] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * ((kbase >> 6) + ch), 0, 0));
+    } else {
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
+            // the lowest key of this lane half in block b: its 32-key run lies in one scale block
+            const int kmin = kbase + (FP8 ? 64 * (b >> 1) + 32 * h + 16 * (b & 1) : 32 * b + 8 * h);
+            k.c[b >> 1][b & 1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (kmin >> shift), 0, 0));
+        }
+    }
+    return k;
+}
 
 template <int D, int KT, bool FP8>
 struct WaveState {
     using C = Cfg<D, KT, FP8>;
-    v4i qop[C::NQ][C::NC];
-    float qsc[C::NQ];
-    float m_run[C::NQ], l_run[C::NQ];
-    v4f o[C::NQ][C::NCT];
+    v4i qop[C::NCS];          // B operand of S^T: this lane's query, channels 32 c + 16 h .. + 15
+    float qsc;
+    float m_run, l_run;
+    v16f o[C::NCS];           // O^T: this lane's query, channels 32 cb + 8 j + 4 h + i
 };
 
-typedef float v4f_t __attribute__((ext_vector_type(4)));
-
-// Key scales of the KQ keys [kg0, kg0 + KQ) of one lane group, by k-scale group q: THREAD_K
-// keeps 4 scales per 64 keys, key t in group (t >> 1) & 3; PER_BLOCK one per 32, 64 or 128
-// keys (KQ <= 32 keys never straddle a block). Past the last scale the buffer load gives 0.
-__device__ __forceinline__ v4f_t load_kscales(__amdgpu_buffer_rsrc_t r, int kg0, int layout, int shift) {
-    if (layout == SQ_LAYOUT_THREAD_K) {
-        return __builtin_bit_cast(v4f_t, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (kg0 >> 6), 0, 0));
-    } else {
-        const float s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (kg0 >> shift), 0, 0));
-        return v4f_t{s, s, s, s};
-    }
-}
-
-// One key tile: S^T = K Q^T on INT8 MFMA, online softmax in base 2, acc += P V.
-// ks: this lane group's key scales for the tile (load_kscales).
-// TAIL: keys are masked per query, key kappa of query qi kept iff kappa < min(Sk, qend0 + qi - q0)
-// with qend0 the key end of the wave's first query (Sk when not causal).
-template <int D, int KT, bool FP8, bool TAIL>
-__device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
-                                          const uint8_t* v_lds, int kbase, v4f_t ks, int lq, int g, int qend0) {
-    using C = Cfg<D, KT, FP8>;
-    // c = RN(qs ks) per k-scale group of this lane group's keys (times score_scale: exact for 1)
-    const int kg0 = kbase + C::KQ * g;
-    float cg[C::NQ][4];
+// One key tile: S^T = K Q^T on INT8 MFMA, online softmax in base 2, O^T += V^T P^T.
+// tail (wave-uniform): keys are masked per query, key kappa of query ql (lane % 32) kept iff kappa <
+// min(Sk, qend0 + ql) - kbase with qend0 the key end of the wave's first query (Sk when not causal).
+// Only the masking and the exponentials branch on it: the products and the accumulator take one path.
+template <bool FP8, int NB>
+__device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, float mn, bool tail, float& lsum,
+                                         v8i* pf8, v8bf* pbf) {
 #pragma unroll
-    for (int n = 0; n < C::NQ; ++n)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) cg[n][q] = (st.qsc[n] * ks[q]) * a.score_scale;
-
-    // per 16-query tile n: S^T = K Q^T (int32), then the online softmax and its P operand.
-    // Only one tile's scores are live; K is read from LDS again for the second tile.
-    v8i pf8[C::NQ];
-    v8bf pbf[C::NQ][KT / 32];
-    float alpha[C::NQ];
-    int lane = 16 * g + lq;
-#pragma unroll
-    for (int n = 0; n < C::NQ; ++n) {
-        // fresh lane offsets per tile n: without them the first tile's K operand reads would
-        // be kept in registers for the second
-        asm volatile("" : "+v"(lane));
-        const int klq = lane & 15, kg = lane >> 4;
-        v4i s[C::NT];
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t) {
-#pragma unroll
-            for (int ch = 0; ch < C::NC; ++ch) {
-                const int row = 16 * t + klq;
-                const v4i kop = *reinterpret_cast<const v4i*>(k_lds + row * D + swz<C::KNS>(row, 4 * ch + kg) * 16);
-                s[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop, st.qop[n][ch], ch == 0 ? v4i{0, 0, 0, 0} : s[t], 0, 0, 0);
-            }
-        }
-        // keys of this lane group in the tile that this lane's query sees (all KQ but in the last
-        // tile and, causal, the diagonal ones); opaque so that the masks are not computed once
-        // before the key loop and kept (64 scalar registers of lane masks)
-        int nval = min(static_cast<int>(a.Sk), qend0 + 16 * n + lq) - kg0;
-        if (TAIL) asm volatile("" : "+v"(nval));
-        int amx[4] = {INT32_MIN, INT32_MIN, INT32_MIN, INT32_MIN};
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (TAIL && 4 * t + i >= nval) s[t][i] = INT32_MIN;
-                const int q = 2 * (t & 1) + (i >> 1);
-                amx[q] = max(amx[q], s[t][i]);
-            }
-        float mt = -__builtin_inff();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float mq = static_cast<float>(amx[q]) * cg[n][q];
-            if (!TAIL || amx[q] != INT32_MIN) mt = fmaxf(mt, mq);
-        }
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        const float mo = st.m_run[n];
-        const float mn = fmaxf(mo, mt);
-        alpha[n] = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-        st.m_run[n] = mn;
-        float lsum = 0.0f;
-#pragma unroll
-        for (int t = 0; t < C::NT; ++t) {
+        for (int j = 0; j < 4; ++j) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int q = 2 * (t & 1) + (i >> 1);
-                const int av = s[t][i];
-                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(static_cast<float>(av), cg[n][q], -mn));
-                if (TAIL && av == INT32_MIN) pv = 0.0f;
+                const int gi = FP8 ? 4 * (b >> 1) + kgroup(j, i) : 4 * b + kgroup(j, i);
+                const int av = s[b][4 * j + i];
+                float x = __builtin_fmaf(static_cast<float>(av), cg[gi], -mn);
+                if (tail && av == INT32_MIN) x = -__builtin_inff();   // a masked key: p = 0 exactly
+                const float pv = __builtin_amdgcn_exp2f(x);
                 p[i] = pv;
                 lsum += pv;
             }
             if constexpr (FP8) {
-                pf8[n][t] = pack_fp8x4_256(p[0], p[1], p[2], p[3]);
+                // keys 64 (b >> 1) + 32 h + 16 (b & 1) + 4 j + i: dword 4 (b & 1) + j of chunk b >> 1
+                pf8[b >> 1][4 * (b & 1) + j] = pack_fp8x4_256(p[0], p[1], p[2], p[3]);
             } else {
+                // keys 32 b + 16 (j >> 1) + 8 h + 4 (j & 1) + i: elements 4 (j & 1) + i of step 2 b + (j >> 1)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pbf[n][t >> 1][4 * (t & 1) + i] = static_cast<__bf16>(p[i]);
+                for (int i = 0; i < 4; ++i) pbf[2 * b + (j >> 1)][4 * (j & 1) + i] = static_cast<__bf16>(p[i]);
             }
         }
-        st.l_run[n] = st.l_run[n] * alpha[n] + lsum;
+}
+
+template <int D, int KT, bool FP8>
+__device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
+                                          const uint8_t* v_lds, int kbase, const KScales<D, KT, FP8>& ks, int ql,
+                                          int h, int qend0, int layout, bool tail) {
+    using C = Cfg<D, KT, FP8>;
+    // c = RN(qs ks) per score group (times score_scale: exact for 1)
+    float cg[C::NG];
+#pragma unroll
+    for (int gi = 0; gi < C::NG; ++gi) {
+        const int q = gi & 3, blk = gi >> 2;                  // FP8: blk = 64-key chunk; bf16: 32-key block
+        const int ch = FP8 ? blk : blk >> 1;
+        const float tk = ks.c[ch][q];
+        const float pb = FP8 ? ks.c[ch][0] : ks.c[ch][blk & 1];
+        cg[gi] = (st.qsc * (layout == SQ_LAYOUT_THREAD_K ? tk : pb)) * a.score_scale;
     }
 
-    // Rescale the accumulator rows (query 4 g + i of tile n) by alpha. Unconditional: alpha is
-    // exactly 1 where no max moved, and a branch around the product makes the compiler keep a
-    // second copy of the accumulator (register moves every tile, spills).
+    // S^T of the tile: s[b][4 j + i] = dot of this lane's query with key kappa_of_row(32 b + 8 j + 4 h + i)
+    v16i s[C::NB];
 #pragma unroll
-    for (int n = 0; n < C::NQ; ++n)
+    for (int b = 0; b < C::NB; ++b) {
+        const int row = 32 * b + ql;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ai = __shfl(alpha[n], 4 * g + i, kWave);
-#pragma unroll
-            for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct][i] *= ai;
+        for (int c = 0; c < C::NCS; ++c) {
+            const v4i kop = *reinterpret_cast<const v4i*>(k_lds + row * D + swz<C::KNS>(row, 2 * c + h) * 16);
+            s[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, st.qop[c], c == 0 ? v16i{} : s[b], 0, 0, 0);
         }
+    }
+    if (tail) {
+        // keys this lane's query sees: local key < nval (a lane of half h holds the half-0 keys plus 32 h
+        // (FP8 permutation) or 8 h (bf16)); opaque so that it is not computed once before the key loop
+        int nval = min(static_cast<int>(a.Sk), qend0 + ql) - kbase - (FP8 ? 32 : 8) * h;
+        asm volatile("" : "+v"(nval));
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (kappa_of_row<FP8>(32 * b + 8 * (r >> 2) + (r & 3)) >= nval) s[b][r] = INT32_MIN;
+    }
+    // maxima per score group (int32), then scaled; a group with every key masked is left out
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int gi = 0; gi < C::NG; ++gi) {
+        const int q = gi & 3, blk = gi >> 2;
+        int amx = INT32_MIN;
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = r >> 2, i = r & 3;
+                if (kgroup(j, i) == q && (FP8 ? (b >> 1) == blk : b == blk)) amx = max(amx, s[b][r]);
+            }
+        const float mq = static_cast<float>(amx) * cg[gi];
+        mt = fmaxf(mt, amx != INT32_MIN ? mq : -__builtin_inff());
+    }
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const float mo = st.m_run;
+    const float mn = fmaxf(mo, mt);
+    const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+    st.m_run = mn;
 
-    // acc += Pt Vt
+    // p = 2^(a c - m'), l += p, P^T operands
+    float lsum = 0.0f;
+    v8i pf8[C::NCH];
+    v8bf pbf[KT / 16];
+    if (tail) exp_pack<FP8, C::NB>(s, cg, mn, true, lsum, pf8, pbf);
+    else exp_pack<FP8, C::NB>(s, cg, mn, false, lsum, pf8, pbf);
+    st.l_run = st.l_run * alpha + lsum;
+
+    // Rescale the accumulator of this lane's query by alpha, unless no query of the wave moved its max
+    // (alpha is then exactly 1 everywhere and the products would change nothing). The products are
+    // written in place (a read-write operand), so both paths leave the accumulator in the same registers.
+    if (__builtin_amdgcn_ballot_w64(mn != mo) != 0) {
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct) {
-        const int row = ct * 16 + lq;
+        for (int cb = 0; cb < C::NCS; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) asm volatile("v_mul_f32 %0, %1, %0" : "+v"(st.o[cb][e]) : "v"(alpha));
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int cb = 0; cb < C::NCS; ++cb) {
+        const int row = 32 * cb + ql;
         if constexpr (FP8) {
-            const v4i lo = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VNS>(row, 2 * g) * 16);
-            const v4i hi = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VNS>(row, 2 * g + 1) * 16);
-            const v8i vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-            for (int n = 0; n < C::NQ; ++n)
-                st.o[n][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pf8[n], vop, st.o[n][ct], 0, 0, 0, 0, 0, 0);
+            for (int ch = 0; ch < C::NCH; ++ch) {
+                const v4i lo = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VNS>(row, 4 * ch + 2 * h) * 16);
+                const v4i hi = *reinterpret_cast<const v4i*>(v_lds + row * C::RBV + swz<C::VNS>(row, 4 * ch + 2 * h + 1) * 16);
+                const v8i vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                st.o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pf8[ch], st.o[cb], 0, 0, 0, 0, 0, 0);
+            }
         } else {
 #pragma unroll
-            for (int u = 0; u < KT / 32; ++u) {
-                const int ls = (C::KQ * g + 8 * u) / 8;       // 16-byte slot of keys KQ g + 8 u .. + 7
-                const v8bf vop = *reinterpret_cast<const v8bf*>(v_lds + row * C::RBV + swz<C::VNS>(row, ls) * 16);
-#pragma unroll
-                for (int n = 0; n < C::NQ; ++n)
-                    st.o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pbf[n][u], vop, st.o[n][ct], 0, 0, 0);
+            for (int u = 0; u < KT / 16; ++u) {
+                const v8bf vop = *reinterpret_cast<const v8bf*>(v_lds + row * C::RBV + swz<C::VNS>(row, 2 * u + h) * 16);
+                st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pbf[u], st.o[cb], 0, 0, 0);
             }
         }
     }
@@ -263,44 +305,42 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
 template <int D, int KT, bool FP8>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     using C = Cfg<D, KT, FP8>;
+    static_assert(!FP8 || KT % 64 == 0, "FP8 P.V takes 64 keys per product");
     __shared__ __attribute__((aligned(1024))) uint8_t buf0[C::KBYTES + C::VBYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t buf1[C::KBYTES + C::VBYTES];
-    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lq = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, ql = l & 31, h = l >> 5;
     const int64_t nqb = (a.Sq + C::QPB - 1) / C::QPB;
     const int64_t items = nqb * a.H * a.B;
     const int64_t item = xcd_item(blockIdx.x, (items + 7) / 8);
     if (item >= items) return;  // uniform over the workgroup
     // causal: the last query blocks see the most keys and are dealt first
-    const int64_t qb = a.causal ? nqb - 1 - item % nqb : item % nqb, h = (item / nqb) % a.H, b = item / (nqb * a.H);
-    const int64_t hk = h / (a.H / a.Hk);
-    const int64_t q0 = qb * C::QPB + w * (C::NQ * 16);
+    const int64_t qb = a.causal ? nqb - 1 - item % nqb : item % nqb, hh = (item / nqb) % a.H, b = item / (nqb * a.H);
+    const int64_t hk = hh / (a.H / a.Hk);
+    const int64_t q0 = qb * C::QPB + w * 32;
 
-    // a sink starts the running max at its logit (base 2) and the sum at 1, counted once: in lane
-    // group 0, whose sum the epilogue adds to the other three
-    const float m0 = a.sinks ? a.sinks[h] * 1.44269504f : -__builtin_inff();
-    const float l0 = (a.sinks && g == 0) ? 1.0f : 0.0f;
     WaveState<D, KT, FP8> st;
-#pragma unroll
-    for (int n = 0; n < C::NQ; ++n) {
-        const int64_t qi = q0 + n * 16 + lq;
+    {
+        const int64_t qi = q0 + ql;
         const bool ok = qi < a.Sq;
 #pragma unroll
-        for (int ch = 0; ch < C::NC; ++ch) {
-            v4i z = {0, 0, 0, 0};
-            st.qop[n][ch] = ok ? *reinterpret_cast<const v4i*>(a.q + b * a.qsb + qi * a.qst + h * a.qsh + ch * 64 + 16 * g) : z;
+        for (int c = 0; c < C::NCS; ++c) {
+            const v4i z = {0, 0, 0, 0};
+            st.qop[c] = ok ? *reinterpret_cast<const v4i*>(a.q + b * a.qsb + qi * a.qst + hh * a.qsh + 32 * c + 16 * h) : z;
         }
-        st.qsc[n] = ok ? a.qs[b * a.qssb + h * a.qssh + scale_idx(qi, a.q_layout, a.q_block)] : 0.0f;
-        st.m_run[n] = m0;
-        st.l_run[n] = l0;
+        st.qsc = ok ? a.qs[b * a.qssb + hh * a.qssh + scale_idx(qi, a.q_layout, a.q_block)] : 0.0f;
+        // a sink starts the running max at its logit (base 2) and the sum at 1, counted once: in
+        // lane half 0, whose sum the epilogue adds to the other half's
+        st.m_run = a.sinks ? a.sinks[hh] * 1.44269504f : -__builtin_inff();
+        st.l_run = (a.sinks && h == 0) ? 1.0f : 0.0f;
 #pragma unroll
-        for (int ct = 0; ct < C::NCT; ++ct) st.o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < C::NCS; ++c) st.o[c] = v16f{};
     }
 
     // what the epilogue needs, folded to a few values before the key loop (fewer live scalars)
-    const int64_t obase = b * a.ob + h * a.oh;   // element offset of (b, h) in out
+    const int64_t obase = b * a.ob + hh * a.oh;   // element offset of (b, h) in out
     const bool obf = a.out_bf16 != 0;
     const int64_t ot = a.ot;
-    float* const lbase = a.lse ? a.lse + b * a.lb + h * a.lh : nullptr;
+    float* const lbase = a.lse ? a.lse + b * a.lb + hh * a.lh : nullptr;
     const float* const vsbase = FP8 ? a.vscale + b * a.vssb + hk * a.vssh : nullptr;
     const int q0i = static_cast<int>(q0), Sq = static_cast<int>(a.Sq);
 
@@ -316,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const int kv_end = a.causal ? min(Sk, static_cast<int>(min(a.Sq, qb * C::QPB + C::QPB)) + off) : Sk;
     const int ntiles = (kv_end + KT - 1) / KT;
     const int qend0 = a.causal ? q0i + off + 1 : Sk;
-    const int lo_end = min(Sk, qend0), hi_end = a.causal ? min(Sk, q0i + C::NQ * 16 + off) : Sk;
+    const int lo_end = min(Sk, qend0), hi_end = a.causal ? min(Sk, q0i + 32 + off) : Sk;
     const int kst = static_cast<int>(a.kst), vrow = static_cast<int>(a.vsd) * C::VB;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(kb), 0, static_cast<int>((a.Sk - 1) * a.kst + D), 0x00020000);
@@ -327,60 +367,51 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, doff); };
     // the key scales of tile j + 1 are fetched (before its K/V copy) while tile j is
     // processed, so no wait on them ever waits for a copy in flight
-    auto kscales = [&](int j) { return load_kscales(ksr, j * KT + C::KQ * g, kl_layout, kl_shift); };
-    auto step = [&](int j, const uint8_t* buf, v4f_t ks) {
+    auto kscales = [&](int j) { return load_kscales<D, KT, FP8>(ksr, j * KT, h, kl_layout, kl_shift); };
+    auto step = [&](int j, const uint8_t* buf, const KScales<D, KT, FP8>& ks) {
         const int kbase = j * KT;
         if (kbase >= hi_end) return;  // no query of the wave sees the tile: its state is unchanged
-        if (kbase + KT > lo_end) tile_step<D, KT, FP8, true>(a, st, buf, buf + C::KBYTES, kbase, ks, lq, g, qend0);
-        else tile_step<D, KT, FP8, false>(a, st, buf, buf + C::KBYTES, kbase, ks, lq, g, qend0);
+        tile_step<D, KT, FP8>(a, st, buf, buf + C::KBYTES, kbase, ks, ql, h, qend0, kl_layout, kbase + KT > lo_end);
     };
-    v4f_t ks_next = kscales(0);
+    KScales<D, KT, FP8> ks_next = kscales(0);
     copy(0, buf0);
     wait_vm();
     __syncthreads();
-    for (int j = 0; j < ntiles; j += 2) {
-        v4f_t ks_cur = ks_next;
+    // one tile per iteration, its buffer chosen at run time (wave-uniform): a loop body unrolled
+    // per buffer would hold the accumulator in two register ranges and copy it between them
+    for (int j = 0; j < ntiles; ++j) {
+        const bool odd = (j & 1) != 0;
+        uint8_t* cur = odd ? buf1 : buf0;
+        uint8_t* nxt = odd ? buf0 : buf1;
+        const KScales<D, KT, FP8> ks_cur = ks_next;
         if (j + 1 < ntiles) {
             ks_next = kscales(j + 1);
-            copy(j + 1, buf1);
+            copy(j + 1, nxt);
         }
-        step(j, buf0, ks_cur);
-        wait_vm();
-        __syncthreads();
-        if (j + 1 >= ntiles) break;
-        ks_cur = ks_next;
-        if (j + 2 < ntiles) {
-            ks_next = kscales(j + 2);
-            copy(j + 2, buf0);
-        }
-        step(j + 1, buf1, ks_cur);
+        step(j, cur, ks_cur);
         wait_vm();
         __syncthreads();
     }
 
-    // epilogue: l over the 4 lane groups, lse, out = acc / l (x vs / 256)
+    // epilogue: l over the two lane halves, lse, out = acc / l (x vs / 256)
+    float lt = st.l_run;
+    lt = lt + shfl_xor(lt, 32);
+    const int qi = q0i + ql;
+    if (lbase && h == 0 && qi < Sq) lbase[qi] = st.m_run + log2f(lt);
+    if (qi < Sq) {
+        const float inv = 1.0f / lt;
+        const int64_t orow = obase + qi * ot;
 #pragma unroll
-    for (int n = 0; n < C::NQ; ++n) {
-        float lt = st.l_run[n];
-        lt = lt + shfl_xor(lt, 16);
-        lt = lt + shfl_xor(lt, 32);
-        const int qi = q0i + n * 16 + lq;
-        if (lbase && g == 0 && qi < Sq) lbase[qi] = st.m_run[n] + log2f(lt);
+        for (int cb = 0; cb < C::NCS; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float li = __shfl(lt, 4 * g + i, kWave);
-            const float inv = 1.0f / li;
-            const int qr = q0i + n * 16 + 4 * g + i;
-            if (qr >= Sq) continue;
-            const int64_t orow = obase + qr * ot;
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int ct = 0; ct < C::NCT; ++ct) {
-                const int c = ct * 16 + lq;
-                float val = st.o[n][ct][i] * inv;
-                if constexpr (FP8) val = val * (vsbase[c] * 0.00390625f);
-                store_out(a.out, orow + c, val, obf);
-            }
-        }
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 32 * cb + 8 * j + 4 * h + i;
+                    float val = st.o[cb][4 * j + i] * inv;
+                    if constexpr (FP8) val = val * (vsbase[c] * 0.00390625f);
+                    store_out(a.out, orow + c, val, obf);
+                }
     }
 }
 
@@ -430,8 +461,13 @@ int launch_attn(const AttnArgs& a, void* stream) {
     dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
     hipStream_t s = S(stream);
     if (a.v_fp8) {
-        if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 128, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_attn<64, 128, true>), grid, dim3(256), 0, s, a);
+        if (a.kv_tile == 128) {
+            if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 128, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_attn<64, 128, true>), grid, dim3(256), 0, s, a);
+        } else {
+            if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 64, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_attn<64, 64, true>), grid, dim3(256), 0, s, a);
+        }
     } else if (a.kv_tile == 128) {
         if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 128, false>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((k_attn<64, 128, false>), grid, dim3(256), 0, s, a);

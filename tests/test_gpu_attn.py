@@ -49,6 +49,10 @@ CASES = [
     (64, 6, 3, 100, 200, (0, 128), (2, 64), "bf16", 64),
     (64, 2, 2, 1, 1, (0, 64), (0, 64), "bf16", 64),
     (128, 2, 2, 5, 1, (0, 64), (0, 64), "fp8", 128),
+    (128, 4, 2, 200, 333, (1, 32), (2, 64), "fp8", 64),
+    (64, 4, 4, 130, 300, (0, 32), (0, 32), "fp8", 64),
+    (128, 2, 1, 129, 65, (3, 128), (0, 128), "fp8", 64),
+    (128, 2, 2, 3, 1, (0, 64), (2, 64), "fp8", 64),
 ]
 
 

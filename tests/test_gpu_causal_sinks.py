@@ -57,6 +57,9 @@ CASES = [
     (64, 2, 2, 100, 77, (0, 64), (0, 64), "bf16", 64, False, True),
     (128, 2, 2, 1, 1, (0, 64), (0, 64), "fp8", 128, True, True),          # one query, one key
     (64, 2, 1, 1, 190, (0, 64), (0, 64), "bf16", 64, True, False),        # one query after 189 keys
+    (128, 4, 2, 300, 300, (1, 32), (2, 64), "fp8", 64, True, True),       # FP8 P.V over 64-key tiles
+    (128, 2, 2, 200, 457, (3, 128), (0, 32), "fp8", 64, True, False),
+    (64, 2, 2, 33, 97, (0, 64), (2, 64), "fp8", 64, True, True),
 ]
 
 
@@ -80,7 +83,7 @@ def test_causal_sinks_parity(case):
     np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
 
 
-@pytest.mark.parametrize("pv,kvt", [("fp8", 128), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("pv,kvt", [("fp8", 128), ("fp8", 64), ("bf16", 64), ("bf16", 128)])
 def test_last_causal_row_is_the_full_row(pv, kvt):
     """With Sq == Sk the last query sees every key: its causal row equals the non-causal row bit for bit (masked
     keys add exact zeros), and so does its lse."""
@@ -110,9 +113,9 @@ def test_causal_at_size_sampled_rows():
     sinks = np.array([0.5, -1.0, 2.0, 1.0], np.float32)
     g = np.random.default_rng(80)
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, S - 1], g.choice(S, 40, replace=False)])).astype(np.int64)
-    ref, rlse, allow, run = O.attn(O.QK(qc, qs, 1, 32), O.QK(kc, ks, 2, 64), v, True, vs, kv_tile=128, rows=rows,
+    ref, rlse, allow, run = O.attn(O.QK(qc, qs, 1, 32), O.QK(kc, ks, 2, 64), v, True, vs, kv_tile=64, rows=rows,
                                    causal=True, sinks=sinks, want_run_allow=True)
-    out, lse = _gpu(qc, qs, 1, 32, kc, ks, 2, 64, v, vs, 128, True, sinks)
+    out, lse = _gpu(qc, qs, 1, 32, kc, ks, 2, 64, v, vs, 64, True, sinks)
     check_float(out[:, rows], ref, allow, what="out", run=run)
     np.testing.assert_allclose(lse[:, :, rows], rlse, rtol=0, atol=1e-4)
 
