@@ -28,7 +28,10 @@ LAYOUT_PER_BLOCK, LAYOUT_THREAD_Q, LAYOUT_THREAD_K, LAYOUT_WARP_Q = 0, 1, 2, 3
 
 
 def build(force: bool = False) -> str:
-    """Compile oracle.c with gcc (plain IEEE arithmetic, OpenMP over rows)."""
+    """Compile oracle.c with gcc (plain IEEE arithmetic, OpenMP over rows). SQ_ORACLE_LIBRARY names another build
+    of it to load instead (e.g. an instrumented one in tests)."""
+    if os.environ.get("SQ_ORACLE_LIBRARY"):
+        return os.environ["SQ_ORACLE_LIBRARY"]
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",

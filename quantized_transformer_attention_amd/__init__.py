@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsq.so")
+# SQ_LIBRARY: load another build of the same library (e.g. an instrumented host build in tests)
+LIB_PATH = os.environ.get("SQ_LIBRARY") or os.path.join(_HERE, "libsq.so")
 
 SQ_OK = 0
 SQ_BF16, SQ_F16, SQ_F32, SQ_I8, SQ_FP8E4M3 = range(5)

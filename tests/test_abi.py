@@ -106,7 +106,7 @@ def test_attn_validation_errors():
     v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 16, None, 0, 0)
     assert call(_qk(), _qk(), vv=v8, tile=128) == -1       # FP8 needs its scales
     v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 16, 0x5000, 0, 0)
-    assert call(_qk(), _qk(), vv=v8, tile=64) == -5        # FP8 P.V runs 128-key tiles
+    assert call(_qk(), _qk(), vv=v8, tile=96) == -5        # kv_tile 64 or 128
     v8 = sq.sq_values(0x3000, sq.SQ_FP8E4M3, 0, 1, 0, 8, 0x5000, 0, 0)
     assert call(_qk(), _qk(), vv=v8, tile=128) == -3       # channel stride below the key count
     assert call(_qk(S=0), _qk()) == 0                      # no queries: no-op
