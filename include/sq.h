@@ -48,8 +48,9 @@ extern "C" {
 
 /* Raised whenever an argument list changes: 2 added causal masking and sinks (sq_attn,
  * sq_paged_decode) and sq_paged_prefill; 3 added out_dtype (FP32 or bf16 outputs) to
- * sq_attn, sq_paged_decode and sq_paged_prefill. sq_abi_version() returns it. */
-#define SQ_ABI_VERSION 3
+ * sq_attn, sq_paged_decode and sq_paged_prefill; 4 added q_dtype (bf16 or f16 queries) to
+ * sq_paged_decode, sq_paged_decode_noalloc and sq_paged_prefill. sq_abi_version() returns it. */
+#define SQ_ABI_VERSION 4
 
 enum {
     SQ_OK = 0,
@@ -108,8 +109,7 @@ typedef struct {
  * (FP32). SPLIT_HALF pairs channel p with p + pairs; INTERLEAVED pairs 2p with
  * 2p + 1; channels >= 2*pairs pass through. rb = 0 serves every batch item.
  * A (..., pairs, 2) table has rp = 2, rc = 1; 2x2 matrices [[cos,-sin],[sin,cos]]
- * (..., pairs, 2, 2) have rp = 4, rc = 2. SPLIT_HALF rotates all D/2 pairs (pairs == D/2);
- * INTERLEAVED takes any pairs <= D/2. */
+ * (..., pairs, 2, 2) have rp = 4, rc = 2. Both modes take any pairs in [1, D/2]. */
 typedef struct {
     sq_rope_mode mode;
     const float* table;
@@ -267,16 +267,16 @@ int sq_lse_merge(float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int
 
 /* ---- D. Paged GQA decode over a q8 cache [impl] _cache_seq, _sdpa_one,
  * _decode_torch; [tq] block-table addressing and split-KV segments. Sequence n of
- * length L = seq_lens[n] (1 <= L <= max_seq_len) has one query (bf16 (N, Hq, D) at
- * q[n*qn + h*qh + c]) at position L - 1, which attends positions 0..L-1. Position
+ * length L = seq_lens[n] (1 <= L <= max_seq_len) has one query ((N, Hq, D) of q_dtype,
+ * SQ_BF16 or SQ_F16, at q[n*qn + h*qh + c]) at position L - 1, which attends positions 0..L-1. Position
  * pos lives in physical block block_table[n*bt_stride + pos / block_size], slot
  * pos % block_size. Caches [num_blocks, block_size, Hk, D] int8 (contiguous), FP16
  * scales [num_blocks, block_size, Hk, D/32]; keys and values are code * scale.
  * Softmax of (q . k) * softmax_scale; out (N, Hq, D) at out[n*on + h*oh + c] in elements
  * of out_dtype (SQ_F32, or SQ_BF16 rounded to nearest even, as sq_attn).
  * max_seq_len is a host bound for the workspace and the grid (no device read).
- * block_size 16; D 128; Hq / Hk in {1, 2, 4, 8}. q 16-byte aligned rows, caches
- * 16-byte aligned, scale tensors 8-byte aligned (one row of 4 FP16 per slot and head).
+ * block_size 16; D 64 or 128; Hq / Hk in {1, 2, 4, 8}. q 16-byte aligned rows, caches
+ * 16-byte aligned, scale tensors aligned to one row of D/32 FP16 (D/16 bytes).
  * Both products run on f16 matrix units with FP32 accumulation: q is carried as f16
  * after an exact power-of-two rescale per head, and the weight of a value row is
  * f16(p * value scale) (relative rounding <= 2^-11 per weight).
@@ -284,8 +284,8 @@ int sq_lse_merge(float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int
  * [tq] USE_SINKS (the split kernel's first segment carries it): exp(sink) joins the
  * softmax denominator once per (sequence, head) and adds no value row. */
 size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_len);
-int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
-                    const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
+int sq_paged_decode(const void* q, sq_dtype q_dtype, int64_t qn, int64_t qh, const int8_t* k_cache,
+                    const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
                     int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
                     sq_dtype out_dtype, int64_t on, int64_t oh, void* ws, size_t ws_bytes, void* stream);
@@ -303,8 +303,8 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
  * array: calls whose work may overlap on that GPU (other streams, other threads) race and
  * must be ordered by the caller. No part of the array needs to start at zero. */
 #define SQ_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
-int sq_paged_decode_noalloc(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
-                            const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
+int sq_paged_decode_noalloc(const void* q, sq_dtype q_dtype, int64_t qn, int64_t qh, const int8_t* k_cache,
+                            const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                             const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
                             int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
                             sq_dtype out_dtype, int64_t on, int64_t oh, void* stream);
@@ -313,21 +313,24 @@ int sq_paged_decode_noalloc(const void* q, int64_t qn, int64_t qh, const int8_t*
  * _cache_seq, _sdpa_one (per sequence, mask k_pos <= key_offset + q_pos); [tq] unified
  * 2D kernel (varlen q blocks by query_start_len, context_len = seq_len - query_len,
  * USE_SINKS). Sequence n owns the packed query tokens [query_start[n], query_start[n+1])
- * of q (bf16 (num_tokens, Hq, D) at q[t*qt + h*qh + c]; query_start int32 (num_seqs + 1,),
+ * of q ((num_tokens, Hq, D) of q_dtype, SQ_BF16 or SQ_F16, at q[t*qt + h*qh + c]; query_start
+ * int32 (num_seqs + 1,),
  * nondecreasing, query_start[0] = 0, query_start[num_seqs] = num_tokens) and the keys at
  * positions 0 .. L-1 of its paged cache, L = seq_lens[n] (the context plus its own
  * queries, whose keys and values must already be in the cache, e.g. by
  * sq_q8_cache_write; q_len <= L <= max_seq_len). Its query j sits at position L - q_len + j
  * and attends positions 0 .. L - q_len + j. Caches, scales, block table and softmax_scale
- * as sq_paged_decode (block_size 16, D 128, Hq / Hk in {1, 2, 4, 8}); sinks NULL or FP32
- * (Hq,). out (num_tokens, Hq, D) at out[t*ot + h*oh + c] in elements of out_dtype (SQ_F32,
- * or SQ_BF16 rounded to nearest even, as sq_attn). Both products run on f16
- * matrix units with FP32 accumulation: q as f16 after an exact power-of-two rescale per
- * (token, head), keys and values dequantized to f16 (code * scale rounded once), P as f16
- * (relative rounding <= 2^-11 each); cached keys and values must stay below 65504 in
- * magnitude (the f16 range). A block-table entry outside [0, num_blocks) is read as block 0
- * (no fault; that sequence's rows are then undefined). No workspace; only enqueues. */
-int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, const int8_t* k_cache,
+ * as sq_paged_decode (block_size 16, D 64 or 128, Hq / Hk in {1, 2, 4, 8}; scales 2-byte
+ * aligned); sinks NULL or FP32 (Hq,). out (num_tokens, Hq, D) at out[t*ot + h*oh + c] in
+ * elements of out_dtype (SQ_F32, or SQ_BF16 rounded to nearest even, as sq_attn). Both
+ * products run on f16 matrix units with FP32 accumulation: q as f16 after an exact
+ * power-of-two rescale per (token, head); key codes widened exactly to f16, each 32-channel
+ * dot meeting its FP16 key scale in FP32; each value code * scale held exactly as a pair of
+ * f16 (cached values must stay below 65504 in magnitude); P as f16 (relative rounding
+ * <= 2^-11), the denominator summed from the same f16 P. A block-table entry outside
+ * [0, num_blocks) is read as block 0 (no fault; that sequence's rows are then undefined).
+ * No workspace; only enqueues. */
+int sq_paged_prefill(const void* q, sq_dtype q_dtype, int64_t qt, int64_t qh, int64_t num_tokens, const int8_t* k_cache,
                      const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
                      int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                      const int32_t* query_start, int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale,

@@ -91,10 +91,10 @@ def _declare(L):
     L.orc_prefix_merge.argtypes = [P(_QK), P(_Prefix), _vp, _f32, _int, _f64, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                    _vp, _vp]
     L.orc_q8_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp]
-    L.orc_paged_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _f64, _vp,
+    L.orc_paged_decode.argtypes = [_vp, _int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _f64, _vp,
                                    _vp]
     L.orc_attn_exact.argtypes = [P(_Rows), P(_Rows), _vp, P(_Prefix), _vp, _i64, _vp]
-    L.orc_paged_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
+    L.orc_paged_prefill.argtypes = [_vp, _int, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
                                     _f64, _vp, _vp, _i64, _vp]
 
 
@@ -360,15 +360,17 @@ def q8_cache_write(k, v, slot_mapping, k_cache, k_scale, v_cache, v_scale):
 
 
 def paged_decode(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, scale, sinks=None):
-    """Binary64 paged decode over a q8 cache: out (N, Hq, D). sinks: FP32 (Hq,) per-head sink logits or None."""
-    q = _c(q, np.uint16)
+    """Binary64 paged decode over a q8 cache: out (N, Hq, D). q: bf16 bits (uint16) or float16 values.
+    sinks: FP32 (Hq,) per-head sink logits or None."""
+    q_f16 = int(np.asarray(q).dtype == np.float16)
+    q = _c(np.asarray(q).view(np.uint16), np.uint16)
     kc, ks, vc, vsc = _c(k_cache, np.int8), _c(k_scale, np.uint16), _c(v_cache, np.int8), _c(v_scale, np.uint16)
     bt, sl = _c(block_table, np.int32), _c(seq_lens, np.int32)
     N, Hq, D = q.shape
     bs, Hk = kc.shape[1], kc.shape[2]
     out = np.empty((N, Hq, D), np.float64)
     sk_ = _c(sinks, np.float32) if sinks is not None else None
-    lib().orc_paged_decode(_p(q), _p(kc), _p(ks), _p(vc), _p(vsc), bs, Hk, _p(bt), bt.shape[1], _p(sl), N, Hq, D,
+    lib().orc_paged_decode(_p(q), q_f16, _p(kc), _p(ks), _p(vc), _p(vsc), bs, Hk, _p(bt), bt.shape[1], _p(sl), N, Hq, D,
                            float(scale), _p(sk_), _p(out))
     return out
 
@@ -376,8 +378,10 @@ def paged_decode(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, s
 def paged_prefill(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, query_start, scale, sinks=None,
                   rows=None):
     """Binary64 paged causal prefill over a q8 cache ([impl] _prefill_torch_from_cache): q bf16 (T, Hq, D) packed
-    by query_start (N + 1,); seq_lens (N,) keys per sequence (context + its queries). out (len(rows) or T, Hq, D)."""
-    q = _c(q, np.uint16)
+    by query_start (N + 1,); seq_lens (N,) keys per sequence (context + its queries). out (len(rows) or T, Hq, D).
+    q: bf16 bits (uint16) or float16 values."""
+    q_f16 = int(np.asarray(q).dtype == np.float16)
+    q = _c(np.asarray(q).view(np.uint16), np.uint16)
     kc, ks, vc, vsc = _c(k_cache, np.int8), _c(k_scale, np.uint16), _c(v_cache, np.int8), _c(v_scale, np.uint16)
     bt, sl, qsl = _c(block_table, np.int32), _c(seq_lens, np.int32), _c(query_start, np.int32)
     T, Hq, D = q.shape
@@ -386,7 +390,7 @@ def paged_prefill(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, 
     n = rows_.size if rows_ is not None else T
     out = np.empty((n, Hq, D), np.float64)
     sk_ = _c(sinks, np.float32) if sinks is not None else None
-    lib().orc_paged_prefill(_p(q), _p(kc), _p(ks), _p(vc), _p(vsc), bs, Hk, _p(bt), bt.shape[1], _p(sl), _p(qsl),
+    lib().orc_paged_prefill(_p(q), q_f16, _p(kc), _p(ks), _p(vc), _p(vsc), bs, Hk, _p(bt), bt.shape[1], _p(sl), _p(qsl),
                             sl.size, Hq, D, float(scale), _p(sk_), _p(rows_), n, _p(out))
     return out
 

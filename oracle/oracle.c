@@ -699,9 +699,14 @@ void orc_q8_quantize(const float* x, int64_t rows, int64_t D, int8_t* codes, uin
  * keeps them all). Position pos lives in physical block block_table[n][pos / bs],
  * slot pos % bs. Keys and values are the exact q8 values code * fp16 scale;
  * binary64 softmax of (q . k) * scale. Caches [NB, bs, Hk, D], scales
- * [NB, bs, Hk, D/32]; q (N, Hq, D) bf16; out (N, Hq, D).
+ * [NB, bs, Hk, D/32]; q (N, Hq, D) bf16, or binary16 when q_f16; out (N, Hq, D).
  * ---------------------------------------------------------------------------- */
-void orc_paged_decode(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
+/* A query element: bf16, or IEEE binary16 when q_f16 (both exact in binary64). */
+static double q_value(const uint16_t* q, int64_t i, int q_f16) {
+    return q_f16 ? f16_value(q[i]) : (double)bf16_f32(q[i]);
+}
+
+void orc_paged_decode(const uint16_t* q, int q_f16, const int8_t* kc, const uint16_t* ks,
                       const int8_t* vc, const uint16_t* vsc, int64_t bs, int64_t Hk,
                       const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                       int64_t N, int64_t Hq, int64_t D, double scale,
@@ -719,7 +724,7 @@ void orc_paged_decode(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
                 int64_t base = (phys * bs + slot) * Hk + hk;
                 double dot = 0.0;
                 for (int64_t d = 0; d < D; ++d)
-                    dot += (double)bf16_f32(q[(n * Hq + h) * D + d]) * ((double)kc[base * D + d] * f16_value(ks[base * NG + d / 32]));
+                    dot += q_value(q, (n * Hq + h) * D + d, q_f16) * ((double)kc[base * D + d] * f16_value(ks[base * NG + d / 32]));
                 s[pos] = dot * scale;
                 m = fmax(m, s[pos]);
             }
@@ -748,9 +753,9 @@ void orc_paged_decode(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
  * 0..key_offset + j (the mask k_pos <= key_offset + q_pos). Keys and values are the exact
  * q8 values code * fp16 scale; binary64 softmax of (q . k) * scale; a sink adds exp(sink)
  * to the denominator only. rows: the query tokens to compute (NULL: all T of them);
- * out (nrows, Hq, D). q (T, Hq, D) bf16 contiguous.
+ * out (nrows, Hq, D). q (T, Hq, D) bf16 (binary16 when q_f16) contiguous.
  * ---------------------------------------------------------------------------- */
-void orc_paged_prefill(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
+void orc_paged_prefill(const uint16_t* q, int q_f16, const int8_t* kc, const uint16_t* ks,
                        const int8_t* vc, const uint16_t* vsc, int64_t bs, int64_t Hk,
                        const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                        const int32_t* query_start, int64_t N, int64_t Hq, int64_t D, double scale,
@@ -776,7 +781,7 @@ void orc_paged_prefill(const uint16_t* q, const int8_t* kc, const uint16_t* ks,
                 int64_t base = (phys * bs + slot) * Hk + hk;
                 double dot = 0.0;
                 for (int64_t d = 0; d < D; ++d)
-                    dot += (double)bf16_f32(q[(t * Hq + h) * D + d]) * ((double)kc[base * D + d] * f16_value(ks[base * NG + d / 32]));
+                    dot += q_value(q, (t * Hq + h) * D + d, q_f16) * ((double)kc[base * D + d] * f16_value(ks[base * NG + d / 32]));
                 s[pos] = dot * scale;
                 m = fmax(m, s[pos]);
             }

@@ -69,7 +69,7 @@ class sq_q8prefix(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 3  # SQ_ABI_VERSION of the sq.h these argument lists follow
+ABI_VERSION = 4  # SQ_ABI_VERSION of the sq.h these argument lists follow
 
 EXPORTS = ["sq_scale_count", "sq_norm_stats", "sq_kmean_workspace_bytes", "sq_kmean", "sq_quant_qk_workspace_bytes",
            "sq_quant_qk", "sq_quant_v_fp8_workspace_bytes", "sq_quant_v_fp8", "sq_attn_workspace_bytes", "sq_attn",
@@ -106,11 +106,11 @@ def lib():
                                                _i64, _vp, _i64, _i64, _vp, _sz, _vp]
         L.sq_paged_decode_workspace_bytes.argtypes = [_int, _int, _int, _int]
         L.sq_paged_decode_workspace_bytes.restype = _sz
-        L.sq_paged_decode.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
+        L.sq_paged_decode.argtypes = [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp, _int,
                                       _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp, _sz, _vp]
-        L.sq_paged_decode_noalloc.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
+        L.sq_paged_decode_noalloc.argtypes = [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
                                               _int, _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp]
-        L.sq_paged_prefill.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
+        L.sq_paged_prefill.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _vp, _i64, _vp,
                                        _vp, _int, _int, _int, _int, _f32, _vp, _vp, _int, _i64, _i64, _vp]
         L.sq_lse_merge.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
                                    _i64, _i64, _i64, _vp]
@@ -385,9 +385,14 @@ def sq_attn_prefix_lse_merge(q: QK, prefix: Q8Prefix, k_mean: Optional[torch.Ten
 
 
 
+def _q_dtype(q: torch.Tensor) -> int:
+    return SQ_F16 if q.dtype == torch.float16 else SQ_BF16
+
+
 def _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens, query_start=None):
     """Host-side dtype and layout checks of the paged entry points' tensors (the C ABI takes raw pointers)."""
-    assert q.dtype == torch.bfloat16 and q.dim() == 3 and q.stride(2) == 1, "q: bf16 (tokens, Hq, D), channels contiguous"
+    assert q.dtype in (torch.bfloat16, torch.float16) and q.dim() == 3 and q.stride(2) == 1, \
+        "q: bf16 or f16 (tokens, Hq, D), channels contiguous"
     for c in (k_cache, v_cache):
         assert c.dtype == torch.int8 and c.dim() == 4 and c.is_contiguous(), "caches: contiguous int8 [NB, bs, Hk, D]"
     for sc in (k_scale, v_scale):
@@ -407,7 +412,7 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
                     softmax_scale: float, out: Optional[torch.Tensor] = None,
                     workspace: Optional[Workspace] = None, sinks: Optional[torch.Tensor] = None,
                     out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """Paged GQA decode over a q8 cache. q bf16 (N, Hq, D); caches int8 [NB, bs, Hk, D] with FP16 scales
+    """Paged GQA decode over a q8 cache. q bf16 or f16 (N, Hq, D), D 64 or 128; caches int8 [NB, bs, Hk, D] with FP16 scales
     [NB, bs, Hk, D/32]; block_table int32 (N, max_blocks); seq_lens int32 (N,); sinks FP32 (Hq,) per-head sink
     logits (natural log) or None. Returns (N, Hq, D) in out_dtype (FP32 or bf16)."""
     _check_paged(q, k_cache, k_scale, v_cache, v_scale, block_table, seq_lens)
@@ -422,7 +427,7 @@ def sq_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tenso
     L = lib()
     need = L.sq_paged_decode_workspace_bytes(N, Hq, D, max_seq_len)
     ws, nb = workspace.get(need) if workspace is not None else _ws(need, dev)
-    _check(L.sq_paged_decode(_ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+    _check(L.sq_paged_decode(_ptr(q), _q_dtype(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                              _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0), _ptr(seq_lens), N,
                              max_seq_len, Hq, D, softmax_scale, _ptr(sinks), _ptr(out), _out_dtype(out),
                              out.stride(0), out.stride(1),
@@ -447,7 +452,7 @@ def sq_paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, k_scale: tor
         assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == Hq, "sinks: FP32 (Hq,)"
     assert out.dim() == 3 and tuple(out.shape) == (N, Hq, D) and out.stride(2) == 1, "out: (N, Hq, D), channels contiguous"
     L = lib()
-    _check(L.sq_paged_decode_noalloc(_ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+    _check(L.sq_paged_decode_noalloc(_ptr(q), _q_dtype(q), q.stride(0), q.stride(1), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                                      _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0),
                                      _ptr(seq_lens), N, max_seq_len, Hq, D, softmax_scale, _ptr(sinks), _ptr(out),
                                      _out_dtype(out), out.stride(0), out.stride(1), _stream(q.device)))
@@ -459,7 +464,7 @@ def sq_paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tens
                      query_start: torch.Tensor, max_seq_len: int, softmax_scale: float,
                      out: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None,
                      out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """Paged causal (chunked) prefill over a q8 cache. q bf16 (num_tokens, Hq, D), packed by query_start int32
+    """Paged causal (chunked) prefill over a q8 cache. q bf16 or f16 (num_tokens, Hq, D), D 64 or 128, packed by query_start int32
     (N + 1,); seq_lens int32 (N,) keys per sequence (context + its queries, already in the cache); caches and
     block_table as sq_paged_decode; sinks FP32 (Hq,) or None. Returns (num_tokens, Hq, D) in out_dtype (FP32 or
     bf16)."""
@@ -472,7 +477,7 @@ def sq_paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, k_scale: torch.Tens
     if sinks is not None:
         assert sinks.dtype == torch.float32 and sinks.is_contiguous() and sinks.numel() == Hq, "sinks: FP32 (Hq,)"
     L = lib()
-    _check(L.sq_paged_prefill(_ptr(q), q.stride(0), q.stride(1), T, _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+    _check(L.sq_paged_prefill(_ptr(q), _q_dtype(q), q.stride(0), q.stride(1), T, _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
                               _ptr(v_scale), NB, bs, Hk, _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
                               _ptr(query_start), seq_lens.numel(), max_seq_len, Hq, D, softmax_scale, _ptr(sinks),
                               _ptr(out), _out_dtype(out), out.stride(0), out.stride(1), _stream(dev)))

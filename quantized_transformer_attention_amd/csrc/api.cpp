@@ -408,7 +408,7 @@ size_t sq_paged_decode_workspace_bytes(int num_seqs, int Hq, int D, int max_seq_
 namespace {
 // Validation of the paged decode's arguments (everything but the workspace) into its kernel arguments.
 // SQ_OK with *empty set when there is nothing to do; a failure sets the detail under the name what.
-int decode_args(const char* what, const void* q, int64_t qn, int64_t qh, const int8_t* k_cache,
+int decode_args(const char* what, const void* q, sq_dtype q_dtype, int64_t qn, int64_t qh, const int8_t* k_cache,
                 const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
                 int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                 int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
@@ -416,7 +416,9 @@ int decode_args(const char* what, const void* q, int64_t qn, int64_t qh, const i
     *empty = false;
     if (num_seqs < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
         return fail(SQ_ERR_SHAPE, "%s: bad sizes (num_seqs %d, Hq %d, Hk %d)", what, num_seqs, Hq, Hk);
-    if (D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", what, D);
+    if (D != 64 && D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d (64 or 128)", what, D);
+    if (q_dtype != SQ_BF16 && q_dtype != SQ_F16)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: q dtype %d (bf16 or f16)", what, (int)q_dtype);
     if (block_size != 16) return fail(SQ_ERR_UNSUPPORTED, "%s: block_size %d (only 16)", what, block_size);
     if (Hq % Hk) return fail(SQ_ERR_SHAPE, "%s: Hq %d not a multiple of Hk %d", what, Hq, Hk);
     const int G = Hq / Hk;
@@ -436,8 +438,8 @@ int decode_args(const char* what, const void* q, int64_t qn, int64_t qh, const i
         return fail(SQ_ERR_ALIGN, "%s: q rows must start on 16-byte boundaries", what);
     if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15))
         return fail(SQ_ERR_ALIGN, "%s: caches must be 16-byte aligned", what);
-    if ((reinterpret_cast<uintptr_t>(k_scale) & 7) || (reinterpret_cast<uintptr_t>(v_scale) & 7))
-        return fail(SQ_ERR_ALIGN, "%s: FP16 scale rows must be 8-byte aligned", what);
+    if (((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & (D / 16 - 1)) != 0)
+        return fail(SQ_ERR_ALIGN, "%s: FP16 scale rows must be aligned to their size (%d bytes)", what, D / 16);
     if (on < 0 || oh < 0) return fail(SQ_ERR_STRIDE, "%s: negative output stride", what);
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
         return fail(SQ_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", what);
@@ -446,7 +448,7 @@ int decode_args(const char* what, const void* q, int64_t qn, int64_t qh, const i
         if (st) return st;
     }
     a = DecodeArgs{};
-    a.q = static_cast<const uint16_t*>(q); a.qn = qn; a.qh = qh;
+    a.q = static_cast<const uint16_t*>(q); a.q_f16 = q_dtype == SQ_F16; a.qn = qn; a.qh = qh;
     a.kc = k_cache; a.ks = k_scale; a.vc = v_cache; a.vs = v_scale;
     a.num_blocks = num_blocks; a.bs = block_size; a.Hk = Hk; a.Hq = Hq; a.D = D;
     a.bt = block_table; a.bt_stride = bt_stride; a.lens = seq_lens;
@@ -460,7 +462,7 @@ int decode_args(const char* what, const void* q, int64_t qn, int64_t qh, const i
 }
 }  // namespace
 
-int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
+int sq_paged_decode(const void* q, sq_dtype q_dtype, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
                     const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                     const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
                     int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
@@ -470,7 +472,7 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     DecodeArgs a;
     bool empty = false;
     {
-        const int st = decode_args(what, q, qn, qh, k_cache, k_scale, v_cache, v_scale, num_blocks, block_size, Hk,
+        const int st = decode_args(what, q, q_dtype, qn, qh, k_cache, k_scale, v_cache, v_scale, num_blocks, block_size, Hk,
                                    block_table, bt_stride, seq_lens, num_seqs, max_seq_len, Hq, D, softmax_scale, sinks,
                                    out, out_dtype, on, oh, a, &empty);
         if (st || empty) return st;
@@ -483,7 +485,8 @@ int sq_paged_decode(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache
     return launch_decode(a, stream);
 }
 
-int sq_paged_decode_noalloc(const void* q, int64_t qn, int64_t qh, const int8_t* k_cache, const uint16_t* k_scale,
+int sq_paged_decode_noalloc(const void* q, sq_dtype q_dtype, int64_t qn, int64_t qh, const int8_t* k_cache,
+                            const uint16_t* k_scale,
                             const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks, int block_size, int Hk,
                             const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens, int num_seqs,
                             int max_seq_len, int Hq, int D, float softmax_scale, const float* sinks, void* out,
@@ -493,7 +496,7 @@ int sq_paged_decode_noalloc(const void* q, int64_t qn, int64_t qh, const int8_t*
     DecodeArgs a;
     bool empty = false;
     {
-        const int st = decode_args(what, q, qn, qh, k_cache, k_scale, v_cache, v_scale, num_blocks, block_size, Hk,
+        const int st = decode_args(what, q, q_dtype, qn, qh, k_cache, k_scale, v_cache, v_scale, num_blocks, block_size, Hk,
                                    block_table, bt_stride, seq_lens, num_seqs, max_seq_len, Hq, D, softmax_scale, sinks,
                                    out, out_dtype, on, oh, a, &empty);
         if (st || empty) return st;
@@ -515,7 +518,7 @@ int sq_paged_decode_noalloc(const void* q, int64_t qn, int64_t qh, const int8_t*
 
 
 // ---------------------------------------------------------------------------- D3. paged causal prefill
-int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, const int8_t* k_cache,
+int sq_paged_prefill(const void* q, sq_dtype q_dtype, int64_t qt, int64_t qh, int64_t num_tokens, const int8_t* k_cache,
                      const uint16_t* k_scale, const int8_t* v_cache, const uint16_t* v_scale, int64_t num_blocks,
                      int block_size, int Hk, const int32_t* block_table, int64_t bt_stride, const int32_t* seq_lens,
                      const int32_t* query_start, int num_seqs, int max_seq_len, int Hq, int D, float softmax_scale,
@@ -525,7 +528,9 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
     if (num_seqs < 0 || num_tokens < 0 || Hq < 1 || Hk < 1 || num_blocks < 0)
         return fail(SQ_ERR_SHAPE, "%s: bad sizes (num_seqs %d, num_tokens %lld, Hq %d, Hk %d)", what, num_seqs,
                     (long long)num_tokens, Hq, Hk);
-    if (D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", what, D);
+    if (D != 64 && D != 128) return fail(SQ_ERR_UNSUPPORTED, "%s: head dim %d (64 or 128)", what, D);
+    if (q_dtype != SQ_BF16 && q_dtype != SQ_F16)
+        return fail(SQ_ERR_UNSUPPORTED, "%s: q dtype %d (bf16 or f16)", what, (int)q_dtype);
     if (block_size != 16) return fail(SQ_ERR_UNSUPPORTED, "%s: block_size %d (only 16)", what, block_size);
     if (Hq % Hk) return fail(SQ_ERR_SHAPE, "%s: Hq %d not a multiple of Hk %d", what, Hq, Hk);
     const int G = Hq / Hk;
@@ -545,8 +550,8 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
         return fail(SQ_ERR_ALIGN, "%s: q rows must start on 16-byte boundaries", what);
     if ((reinterpret_cast<uintptr_t>(k_cache) & 15) || (reinterpret_cast<uintptr_t>(v_cache) & 15))
         return fail(SQ_ERR_ALIGN, "%s: caches must be 16-byte aligned", what);
-    if ((reinterpret_cast<uintptr_t>(k_scale) & 7) || (reinterpret_cast<uintptr_t>(v_scale) & 7))
-        return fail(SQ_ERR_ALIGN, "%s: FP16 scale rows must be 8-byte aligned", what);
+    if (((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 1) != 0)
+        return fail(SQ_ERR_ALIGN, "%s: FP16 scales must be 2-byte aligned", what);
     if (ot < 0 || oh < 0) return fail(SQ_ERR_STRIDE, "%s: negative output stride", what);
     if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
         return fail(SQ_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", what);
@@ -555,9 +560,9 @@ int sq_paged_prefill(const void* q, int64_t qt, int64_t qh, int64_t num_tokens, 
         if (st) return st;
     }
     PrefillArgs a{};
-    a.q = static_cast<const uint16_t*>(q); a.qt = qt; a.qh = qh;
+    a.q = static_cast<const uint16_t*>(q); a.q_f16 = q_dtype == SQ_F16; a.qt = qt; a.qh = qh;
     a.kc = k_cache; a.ks = k_scale; a.vc = v_cache; a.vs = v_scale;
-    a.num_blocks = num_blocks; a.Hk = Hk; a.Hq = Hq;
+    a.num_blocks = num_blocks; a.Hk = Hk; a.Hq = Hq; a.D = D;
     a.bt = block_table; a.bt_stride = bt_stride;
     a.lens = seq_lens; a.qstart = query_start;
     a.N = num_seqs; a.max_len = max_seq_len;

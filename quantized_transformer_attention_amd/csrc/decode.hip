@@ -8,14 +8,14 @@
 // segments' max and exp-sum); [kit] WanGP shared/attention_kit.py (q8: int8 per
 // token, head and 32 channels with one FP16 scale).
 //
-// The path is bound by HBM: per cached token and kv head 2 x 128 code bytes + 2 x 8
-// scale bytes. One workgroup (4 waves) owns one segment of kDecodeSeg positions of
+// The path is bound by HBM: per cached token and kv head 2 x D code bytes + 2 x D/16
+// scale bytes (D = 64 or 128). One workgroup (4 waves) owns one segment of kDecodeSeg positions of
 // one (sequence, kv head) and serves all Hq / Hk query heads from a single read of
 // the segment's K and V; each wave takes 64 positions (4 pages). Both contractions run
 // on the f16 matrix cores (f32 accumulation), the query heads padded to 16 rows:
 //  * Q.K: K codes are loaded straight into the B operand layout (8 channels of one
 //    position per lane) and widened exactly to f16 (byte permute + packed f16 subtract);
-//    q is f16 after an exact power-of-two
+//    q (bf16 or f16) is f16 after an exact power-of-two
 //    rescale per head (the head's largest |q| lands in [2^14, 2^15), so no bf16 value
 //    overflows); one MFMA per 32-channel q8 group, whose dot then meets its FP16 key scale
 //    in FP32. Scores (log2 units) go to LDS.
@@ -46,7 +46,6 @@ static __device__ __align__(256) unsigned char scratch[SQ_DECODE_SCRATCH_BYTES];
 namespace sq {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kSeg = kDecodeSeg;
 constexpr int kTpw = kSeg / 4;  // positions per wave
 static_assert(kTpw == 64, "a wave takes 4 pages");
@@ -56,11 +55,22 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
-template <int G>
+// The NG = D / 32 FP16 group scales of one cache row (8 or 4 bytes).
+template <int D>
+__device__ __forceinline__ uint2 load_scale_row(const uint16_t* p) {
+    if constexpr (D == 128) return *reinterpret_cast<const uint2*>(p);
+    else return make_uint2(*reinterpret_cast<const uint32_t*>(p), 0u);
+}
+
+template <int G, int D>
 __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
+    constexpr int NG = D / 32;        // q8 channel groups (and MFMAs per score)
+    constexpr int NCT = D / 16;       // 16-channel output tiles of P.V
+    constexpr int NV = D / 16;        // 16-byte V loads per lane (64 rows of D bytes per wave)
+    constexpr int RPL = 1024 / D;     // V rows per load
     __shared__ __attribute__((aligned(16))) float sc[G][kSeg];             // scores [head][position]
-    __shared__ __attribute__((aligned(1024))) uint8_t vst[4][kTpw * kD];   // each wave's V rows; then its partial acc
-    __shared__ __attribute__((aligned(16))) float4 vsf[4][kTpw];           // their scales as FP32 (4 per row)
+    __shared__ __attribute__((aligned(1024))) uint8_t vst[4][kTpw * D];    // each wave's V rows; then its partial acc
+    __shared__ __attribute__((aligned(16))) float4 vsf[4][kTpw];           // their scales as FP32 (NG per row)
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, j = l >> 4, lc = l & 15;
     // The Hk workgroups of one (sequence, segment) run back to back on one XCD (workgroup i
     // goes to XCD i % 8), so each cache slot's rows and scale rows (all heads side by side in
@@ -99,48 +109,49 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     // makes it wait for the one before): a page outside the table reads block 0's rows instead,
     // positions past the end read their page's unused slots; all of them get score -inf and
     // value scale 0.
-    uint4 qraw[4];
+    uint4 qraw[NG];
     {
         const uint16_t* qp = a.q + static_cast<int64_t>(n) * a.qn + static_cast<int64_t>(hk * G + min(lc, G - 1)) * a.qh;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) qraw[g] = *reinterpret_cast<const uint4*>(qp + 32 * g + 8 * j);
+        for (int g = 0; g < NG; ++g) qraw[g] = *reinterpret_cast<const uint4*>(qp + 32 * g + 8 * j);
     }
     // K of page t: lane (j, lc) takes position 16 t + lc, channels 32 g + 8 j .. + 7 of each group g
-    uint2 kr[4][4];
+    uint2 kr[4][NG];
     uint2 ksr[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int64_t row = (rowbase[t] >= 0 ? rowbase[t] : hk) + static_cast<int64_t>(lc) * a.Hk;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) kr[t][g] = *reinterpret_cast<const uint2*>(a.kc + row * kD + 32 * g + 8 * j);
-        ksr[t] = *reinterpret_cast<const uint2*>(a.ks + row * (kD / 32));
+        for (int g = 0; g < NG; ++g) kr[t][g] = *reinterpret_cast<const uint2*>(a.kc + row * D + 32 * g + 8 * j);
+        ksr[t] = load_scale_row<D>(a.ks + row * NG);
     }
 
-    // V rows: load r holds rows 8 r .. 8 r + 7 (lane l: row 8 r + l / 8, bytes 16 (l % 8)); V scales:
-    // lane l takes row l's 4 FP16. Both go to LDS once the scores are done.
-    uint4 vraw[8];
+    // V rows: load r holds rows RPL r .. RPL r + RPL - 1 (lane l: row RPL r + l / NV, bytes 16 (l % NV));
+    // V scales: lane l takes row l's NG FP16. Both go to LDS once the scores are done.
+    uint4 vraw[NV];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int64_t rb = rowbase[r >> 1] >= 0 ? rowbase[r >> 1] : hk;
-        const int slot = 8 * (r & 1) + (l >> 3);
-        vraw[r] = *reinterpret_cast<const uint4*>(a.vc + (rb + static_cast<int64_t>(slot) * a.Hk) * kD + 16 * (l & 7));
+    for (int r = 0; r < NV; ++r) {
+        const int row = RPL * r + l / NV;           // wave-local row: page row / 16, slot row % 16
+        const int64_t rb = rowbase[row >> 4] >= 0 ? rowbase[row >> 4] : hk;
+        vraw[r] = *reinterpret_cast<const uint4*>(a.vc + (rb + static_cast<int64_t>(row & 15) * a.Hk) * D + 16 * (l % NV));
     }
     uint2 vsr;
     {
         const int64_t rb0 = rowbase[l >> 4];
         const int64_t rb = rb0 >= 0 ? rb0 : hk;
-        vsr = *reinterpret_cast<const uint2*>(a.vs + (rb + static_cast<int64_t>(l & 15) * a.Hk) * (kD / 32));
+        vsr = load_scale_row<D>(a.vs + (rb + static_cast<int64_t>(l & 15) * a.Hk) * NG);
     }
     // ---- q of head m = lc (zero rows for m >= G): channels 32 g + 8 j .. + 7 as f16, times
     // 2^sh with sh per head putting its largest |q| in [2^14, 2^15)
-    v8h qa[4];
+    v8h qa[NG];
     int sh = 0;
     {
-        float f[4][8];
+        float f[NG][8];
         float mx = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            unpack_bf16x8(qraw[g], f[g]);
+        for (int g = 0; g < NG; ++g) {
+            if (a.q_f16) unpack_f16x8(qraw[g], f[g]);
+            else unpack_bf16x8(qraw[g], f[g]);
 #pragma unroll
             for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(f[g][k]));
         }
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
         mx = fmaxf(mx, shfl_xor(mx, 32));
         sh = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) + 1 : 0;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 qa[g][k] = lc < G ? static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[g][k], sh)) : static_cast<_Float16>(0.0f);
@@ -161,23 +172,22 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) scl[i] = __builtin_amdgcn_ldexpf(a.scale, -__shfl(sh, min(4 * j + i, 15), kWave));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        v4f dg[4];
+        v4f dg[NG];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < NG; ++g)
             dg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[g], i8x8_to_f16(kr[t][g].x, kr[t][g].y),
                                                           v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
         // lane (j, lc) now holds heads 4 j + i of position 16 t + lc
         const int pos = wp0 + 16 * t + lc;
         const bool ok = rowbase[t] >= 0 && pos < s1;
-        const float k0 = f16_to_f32(ksr[t].x & 0xffff), k1 = f16_to_f32(ksr[t].x >> 16);
-        const float k2 = f16_to_f32(ksr[t].y & 0xffff), k3 = f16_to_f32(ksr[t].y >> 16);
+        const float ks[4] = {f16_to_f32(ksr[t].x & 0xffff), f16_to_f32(ksr[t].x >> 16), f16_to_f32(ksr[t].y & 0xffff),
+                             f16_to_f32(ksr[t].y >> 16)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = 4 * j + i;
-            float sv = dg[0][i] * k0;
-            sv = __builtin_fmaf(dg[1][i], k1, sv);
-            sv = __builtin_fmaf(dg[2][i], k2, sv);
-            sv = __builtin_fmaf(dg[3][i], k3, sv);
+            float sv = dg[0][i] * ks[0];
+#pragma unroll
+            for (int g = 1; g < NG; ++g) sv = __builtin_fmaf(dg[g][i], ks[g], sv);
             sv = sv * scl[i];
             if (h < G) sc[h][w * kTpw + 16 * t + lc] = ok ? sv : -__builtin_inff();
         }
@@ -185,13 +195,14 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     // this wave's V rows and value scales to LDS (scales zero on rows past the end of the
     // sequence or on an unread page)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(vst[w] + 1024 * r + 16 * l) = vraw[r];
+    for (int r = 0; r < NV; ++r) *reinterpret_cast<uint4*>(vst[w] + 1024 * r + 16 * l) = vraw[r];
     // value scales times 2^esh: the wave's largest |scale| lands in [2^14, 2^15), so the f16 weights
     // p vs 2^esh <= 2^15 stay normal for the keys that matter; o is multiplied by 2^-esh after the loop
     int esh = 0;
     {
         const bool okv = rowbase[l >> 4] >= 0 && wp0 + l < s1;
         const h2 s01 = __builtin_bit_cast(h2, vsr.x), s23 = __builtin_bit_cast(h2, vsr.y);
+        // (D = 64: two scales; the other two lanes of the float4 are 0 and never read)
         float4 sf = okv ? make_float4(static_cast<float>(s01[0]), static_cast<float>(s01[1]), static_cast<float>(s23[0]),
                                       static_cast<float>(s23[1]))
                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -223,9 +234,9 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     for (int h = 0; h < G; ++h)
         if (lc == h) Mm = M[h];
     const bool live = lc < G && Mm > -__builtin_inff();
-    v4f o[8];
+    v4f o[NCT];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) o[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ct = 0; ct < NCT; ++ct) o[ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     float lsum = 0.0f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -244,22 +255,24 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) lsum += p[k];
         // weights per group: P'_g[k] = f16(p[k] * vs[k][g])
-        v8h pw[4];
+        v8h pw[NG];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float4 sf = vsf[w][r0 + k];
             pw[0][k] = static_cast<_Float16>(p[k] * sf.x);
             pw[1][k] = static_cast<_Float16>(p[k] * sf.y);
-            pw[2][k] = static_cast<_Float16>(p[k] * sf.z);
-            pw[3][k] = static_cast<_Float16>(p[k] * sf.w);
+            if constexpr (NG == 4) {
+                pw[NG - 2][k] = static_cast<_Float16>(p[k] * sf.z);
+                pw[NG - 1][k] = static_cast<_Float16>(p[k] * sf.w);
+            }
         }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
             // lanes 2 k and 2 k + 1 of the group give row r0 + k's channels 16 ct .. + 7 and + 8 .. + 15;
             // lane lc receives channel 16 ct + lc of the 8 rows
             typedef __attribute__((address_space(3))) v2i* lv2p;
             const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lv2p)(vst[w] + (r0 + (lc >> 1)) * kD + 16 * ct + 8 * (lc & 1)));
+                (lv2p)(vst[w] + (r0 + (lc >> 1)) * D + 16 * ct + 8 * (lc & 1)));
             o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[ct >> 1], i8x8_to_f16(raw[0], raw[1]), o[ct], 0, 0, 0);
         }
     }
@@ -267,32 +280,32 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     lsum += shfl_xor(lsum, 32);
     // undo the value-scale factor (exact: a power of two on FP32)
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[ct][i] = __builtin_amdgcn_ldexpf(o[ct][i], -esh);
 
     // ---- the 4 waves' partials (same max) summed; lane (j, lc) of o[ct] holds heads 4 j + i, channel 16 ct + lc
     float* red = reinterpret_cast<float*>(vst[w]);   // this wave's own rows: read by nobody else
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (4 * j + i < G) red[(4 * j + i) * kD + 16 * ct + lc] = o[ct][i];
+            if (4 * j + i < G) red[(4 * j + i) * D + 16 * ct + lc] = o[ct][i];
     // this wave's exp-sums in its own (now unused) scale rows
     float* lred = reinterpret_cast<float*>(vsf[w]);
     if (j == 0 && lc < G) lred[lc] = lsum;
     __syncthreads();
     const int nseg = a.segs;
-    for (int idx = tid; idx < G * (kD + 2); idx += 256) {
-        const int h = idx / (kD + 2), c = idx % (kD + 2);
+    for (int idx = tid; idx < G * (D + 2); idx += 256) {
+        const int h = idx / (D + 2), c = idx % (D + 2);
         float v;
-        if (c < kD) {
+        if (c < D) {
             const float* r0 = reinterpret_cast<const float*>(vst[0]);
             const float* r1 = reinterpret_cast<const float*>(vst[1]);
             const float* r2 = reinterpret_cast<const float*>(vst[2]);
             const float* r3 = reinterpret_cast<const float*>(vst[3]);
-            v = (r0[h * kD + c] + r1[h * kD + c]) + (r2[h * kD + c] + r3[h * kD + c]);
-        } else if (c == kD) {
+            v = (r0[h * D + c] + r1[h * D + c]) + (r2[h * D + c] + r3[h * D + c]);
+        } else if (c == D) {
             float mh = -__builtin_inff();
 #pragma unroll
             for (int q = 0; q < G; ++q)
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
             const float* l3 = reinterpret_cast<const float*>(vsf[3]);
             v = (l0[h] + l1[h]) + (l2[h] + l3[h]);
         }
-        a.part[((static_cast<int64_t>(n) * a.Hq + hk * G + h) * nseg + seg) * (kD + 2) + c] = v;
+        a.part[((static_cast<int64_t>(n) * a.Hq + hk * G + h) * nseg + seg) * (D + 2) + c] = v;
     }
 }
 
@@ -313,23 +326,24 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
 // owns channel c; the segments' maxima and weights are computed 128 at a time, one
 // segment per thread, and shared through LDS; each channel's weighted sum then reads
 // its partials 8 loads at a time.
-__global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
-    constexpr int SB = kD, NL = 8;
+template <int D>
+__global__ __launch_bounds__(D) void k_decode_reduce(DecodeArgs a) {
+    constexpr int SB = D, NL = 8;
     __shared__ float wl[2][SB];  // per segment of the pass: weight, exp-sum
-    __shared__ float red[kD / 64];
+    __shared__ float red[D / 64];
     const int c = threadIdx.x, hq = blockIdx.x, n = blockIdx.y;
     const int L = a.num_blocks > 0 ? min(a.lens[n], a.max_len) : 0;
     const int nseg = L > 0 ? (L + kSeg - 1) / kSeg : 0;
-    const float* p = a.part + (static_cast<int64_t>(n) * a.Hq + hq) * a.segs * (kD + 2);
+    const float* p = a.part + (static_cast<int64_t>(n) * a.Hq + hq) * a.segs * (D + 2);
     float mg = -__builtin_inff();
-    for (int s = c; s < nseg; s += SB) mg = fmaxf(mg, p[s * (kD + 2) + kD]);
+    for (int s = c; s < nseg; s += SB) mg = fmaxf(mg, p[s * (D + 2) + D]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, shfl_xor(mg, off));
     if ((c & 63) == 0) red[c >> 6] = mg;
     __syncthreads();
     // a sink joins as one more term of the denominator, at its logit in base 2
     const float sk = a.sinks ? a.sinks[hq] * 1.44269504f : -__builtin_inff();
-    mg = fmaxf(fmaxf(red[0], red[1]), sk);
+    mg = fmaxf(fmaxf(red[0], red[D / 64 - 1]), sk);
     float tot = 0.0f, o = 0.0f;
     if (mg > -__builtin_inff()) {  // uniform over the workgroup
         if (sk > -__builtin_inff()) tot = __builtin_amdgcn_exp2f(sk - mg);
@@ -337,9 +351,9 @@ __global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
             const int s = s0 + c;
             float wgt = 0.0f, ls = 0.0f;
             if (s < nseg) {
-                const float ms = p[s * (kD + 2) + kD];
+                const float ms = p[s * (D + 2) + D];
                 wgt = ms > -__builtin_inff() ? __builtin_amdgcn_exp2f(ms - mg) : 0.0f;
-                ls = p[s * (kD + 2) + kD + 1];
+                ls = p[s * (D + 2) + D + 1];
             }
             __syncthreads();  // the previous pass has finished reading wl
             wl[0][c] = wgt;
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(kD) void k_decode_reduce(DecodeArgs a) {
             for (int j0 = 0; j0 < ns; j0 += NL) {
                 float v[NL];
 #pragma unroll
-                for (int j = 0; j < NL; ++j) v[j] = p[(s0 + min(j0 + j, ns - 1)) * (kD + 2) + c];
+                for (int j = 0; j < NL; ++j) v[j] = p[(s0 + min(j0 + j, ns - 1)) * (D + 2) + c];
 #pragma unroll
                 for (int j = 0; j < NL; ++j)
                     if (j0 + j < ns) {
@@ -391,19 +405,26 @@ int decode_scratch(void** ptr) {
     return SQ_OK;
 }
 
-int launch_decode(const DecodeArgs& a, void* stream) {
-    if (a.N == 0) return SQ_OK;
-    const int G = a.Hq / a.Hk;
+namespace {
+template <int D>
+void launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     const int64_t chunks = static_cast<int64_t>(a.segs) * a.N;      // (sequence, segment) pairs
     dim3 g1(static_cast<unsigned>((chunks + 7) / 8 * 8 * a.Hk));
-    switch (G) {
-    case 1: hipLaunchKernelGGL(k_decode_split<1>, g1, dim3(256), 0, S(stream), a); break;
-    case 2: hipLaunchKernelGGL(k_decode_split<2>, g1, dim3(256), 0, S(stream), a); break;
-    case 4: hipLaunchKernelGGL(k_decode_split<4>, g1, dim3(256), 0, S(stream), a); break;
-    default: hipLaunchKernelGGL(k_decode_split<8>, g1, dim3(256), 0, S(stream), a); break;
+    switch (a.Hq / a.Hk) {
+    case 1: hipLaunchKernelGGL((k_decode_split<1, D>), g1, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_decode_split<2, D>), g1, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_decode_split<4, D>), g1, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_decode_split<8, D>), g1, dim3(256), 0, s, a); break;
     }
-    hipLaunchKernelGGL(k_decode_reduce, dim3(static_cast<unsigned>(a.Hq), static_cast<unsigned>(a.N)), dim3(kD), 0,
-                       S(stream), a);
+    hipLaunchKernelGGL(k_decode_reduce<D>, dim3(static_cast<unsigned>(a.Hq), static_cast<unsigned>(a.N)), dim3(D), 0, s,
+                       a);
+}
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, void* stream) {
+    if (a.N == 0) return SQ_OK;
+    if (a.D == 128) launch_decode_d<128>(a, S(stream));
+    else launch_decode_d<64>(a, S(stream));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_paged_decode: kernel launch failed: %s", hipGetErrorString(e));
     return SQ_OK;

@@ -21,6 +21,18 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
     f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
 }
 
+// 8 f16 (one 16-byte load) -> 8 floats (exact).
+__device__ __forceinline__ void unpack_f16x8(const uint4& u, float* f) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h2_t h = __builtin_bit_cast(h2_t, w[i]);
+        f[2 * i] = static_cast<float>(h[0]);
+        f[2 * i + 1] = static_cast<float>(h[1]);
+    }
+}
+
 // Stores element idx of an output tensor: FP32, or bfloat16 rounded to nearest even when bf16
 // (idx counts elements of the stored type).
 __device__ __forceinline__ void store_out(float* out, int64_t idx, float v, bool bf16) {

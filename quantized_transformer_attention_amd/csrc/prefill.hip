@@ -10,15 +10,15 @@
 // seq_len - query_len, online softmax, sinks (USE_SINKS: M = sink logit, L = 1).
 //
 // Design (one workgroup = NW waves = 32 NW rows = 32 NW / G tokens x G heads of one kv head;
-// 64-key tiles = 4 pages):
-//  * K and V tiles are staged once per workgroup, key-major in LDS (256 bytes per key, 16-byte
+// 64-key tiles = 4 pages; head dim D = 64 or 128):
+//  * K and V tiles are staged once per workgroup, key-major in LDS (2 D bytes per key, 16-byte
 //    slots XOR-swizzled): K as its int8 codes widened exactly to f16, with its FP16 group
 //    scales as FP32 beside them; V as an exact pair of f16 values per element, hi = f16(code
 //    vs) and lo = code vs - hi (one fused multiply-add: the remainder fits in f16), so that
 //    neither K nor V is rounded. The next tile's codes and scales are loaded into registers
 //    while the current tile is processed; the block-table entries of the tile after it are
 //    read (scalar) one step earlier still.
-//  * q is carried as f16 after an exact power-of-two rescale per row (its largest |q| in
+//  * q (bf16 or f16) is carried as f16 after an exact power-of-two rescale per row (its largest |q| in
 //    [2^14, 2^15)), undone exactly in the row's score scale.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16, one product per 32-channel q8 group (exact
 //    f16 products, FP32 sums) meeting its key scale in FP32: s = sum_g dot_g ks_g. K rows are
@@ -43,13 +43,21 @@
 namespace sq {
 namespace {
 
-constexpr int kD = 128, kBS = 16, kKT = 64;
+constexpr int kBS = 16, kKT = 64;
 constexpr float kLag = 8.0f;                // how far a row's reference max may trail its max
-constexpr int kNQ = 2, kNT = kKT / 16, kNC = kD / 32, kNCT = kD / 16;
-constexpr int kRowB = 2 * kD;               // one f16 key row in LDS
-constexpr int kTileB = kKT * kRowB;         // 16 KB per tile and f16 tensor
-constexpr int kVHi = kTileB, kVLo = 2 * kTileB, kKs = 3 * kTileB;   // buffer: K codes, V hi, V lo, K scales
-constexpr int kBufB = 3 * kTileB + kKT * kNC * 4;
+constexpr int kNQ = 2, kNT = kKT / 16;
+
+// LDS tile geometry of head dim D: per key one f16 row of D channels (NS 16-byte slots) in each of
+// K, V hi and V lo, then the keys' FP32 group scales.
+template <int D>
+struct PfTile {
+    static constexpr int kNC = D / 32, kNCT = D / 16, NS = D / 8;
+    static constexpr int kRowB = 2 * D;
+    static constexpr int kTileB = kKT * kRowB;                                  // 16 KB at D = 128
+    static constexpr int kVHi = kTileB, kVLo = 2 * kTileB, kKs = 3 * kTileB;   // K codes, V hi, V lo, K scales
+    static constexpr int kBufB = 3 * kTileB + kKT * kNC * 4;
+    static constexpr int KPW = kWave * 16 / D;                                  // keys a wave stages per pass
+};
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -58,12 +66,14 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lv4s_p;
 
-// LDS row of key kappa in the K tile, and the 16-byte slot swizzles: K is read as 16 rows x one
-// slot per lane group (row & 15 spreads the 16 rows over all banks); V as 16 keys 16 g + 8 u +
-// 4 h + k (k, g = 0..3) x two slots, spread by k | g << 2.
+// LDS row of key kappa in the K tile, and the 16-byte slot swizzles (NS slots per row): K is read as
+// 16 rows x one slot per lane group (row mod NS spreads the rows over the banks); V as 16 keys
+// 16 g + 8 u + 4 h + k (k, g = 0..3) x two slots, spread by k | g << 2 (D = 128) or k | (g & 1) << 2.
 __device__ __forceinline__ int k_row(int kappa) { return 16 * ((kappa >> 2) & 3) + 4 * (kappa >> 4) + (kappa & 3); }
-__device__ __forceinline__ int k_slot(int row, int slot) { return slot ^ (row & 15); }
-__device__ __forceinline__ int v_slot(int key, int slot) { return slot ^ ((key & 3) | ((key >> 2) & 12)); }
+template <int D>
+__device__ __forceinline__ int k_slot(int row, int slot) { return slot ^ (row & (D / 8 - 1)); }
+template <int D>
+__device__ __forceinline__ int v_slot(int key, int slot) { return slot ^ ((key & 3) | ((key >> 2) & (D / 8 - 4))); }
 
 // x s as an exact pair: hi = f16(x s), lo = x s - hi (x an integer code, s an f16 scale: the product
 // has at most 18 significant bits, so the remainder of its f16 rounding is an f16 number)
@@ -73,11 +83,17 @@ __device__ __forceinline__ void scale8_pair(v8h x, _Float16 s, v8h& hi, v8h& lo)
     lo = __builtin_elementwise_fma(x, sv, -hi);
 }
 
-template <int G, int NW>
+template <int G, int NW, int D>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a) {
+    using C = PfTile<D>;
+    constexpr int kNC = C::kNC, kNCT = C::kNCT, kRowB = C::kRowB, kBufB = C::kBufB;
+    constexpr int kVHi = C::kVHi, kVLo = C::kVLo, kKs = C::kKs;
     constexpr int kRows = 32 * NW;                      // rows per workgroup
     constexpr int BQ = kRows / G;                       // query tokens per workgroup
-    constexpr int U = 8 / NW;                           // 16-byte K (and V) chunks per thread and tile
+    // 16-byte K (and V) chunks per thread and tile; with more stagers than chunks the waves past
+    // the tile's keys stage nothing
+    constexpr int U = kKT / (NW * C::KPW) > 0 ? kKT / (NW * C::KPW) : 1;
+    static_assert(U * NW * C::KPW >= kKT, "every key of a tile has a stager");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufB];
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lq = l & 15, g = l >> 4;
 
@@ -132,11 +148,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
         float mx = 0.0f;
 #pragma unroll
         for (int c = 0; c < kNC; ++c) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[c][2 * e] = bf16_lo(raw[c][e]);
-                f[c][2 * e + 1] = bf16_hi(raw[c][e]);
-            }
+            const uint4 rc = make_uint4(raw[c][0], raw[c][1], raw[c][2], raw[c][3]);
+            if (a.q_f16) unpack_f16x8(rc, f[c]);
+            else unpack_bf16x8(rc, f[c]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[c][e]));
         }
@@ -157,33 +171,38 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
         ol[n] = v4f{l0, l0, l0, l0};
     }
 
-    // ---- staging: thread tid takes 16 channels (part) of keys kappa_u = tid / 8 + 8 NW u of a tile;
-    // the pages of those keys are wave-uniform: tile page w / 2 + NW u / 2
-    const int part = tid & 7, key0 = tid >> 3;
+    // ---- staging: thread tid takes 16 channels (part) of keys kappa_u = tid / (D / 16) + NW KPW u of a
+    // tile; the pages of those keys are wave-uniform: tile page (KPW w + NW KPW u) / 16
+    constexpr int PARTS = D / 16;
+    const int part = tid % PARTS, key0 = tid / PARTS;
+    const bool stager = C::KPW * w < kKT;               // wave-uniform
     const int64_t rowstride = a.Hk;                     // cache rows per slot
     auto page_block = [&](int tile, int u) {
-        const int page = __builtin_amdgcn_readfirstlane(min(tile * (kKT / kBS) + (NW / 2) * u + (w >> 1), last_page));
+        const int tp = stager ? (C::KPW * w + NW * C::KPW * u) / kBS : 0;
+        const int page = __builtin_amdgcn_readfirstlane(min(tile * (kKT / kBS) + tp, last_page));
         const int b = bt[page];
         return (b >= 0 && b < a.num_blocks) ? b : 0;    // a bad entry reads block 0 (no fault)
     };
     v4u kraw[U], vraw[U];
     uint32_t ksr[U], vsr[U];
     auto load_tile = [&](const int* blk) {
+        if (!stager) return;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t row = (static_cast<int64_t>(blk[u]) * kBS + ((key0 + 8 * NW * u) & 15)) * rowstride + hk;
-            kraw[u] = *reinterpret_cast<const v4u*>(a.kc + row * kD + 16 * part);
-            vraw[u] = *reinterpret_cast<const v4u*>(a.vc + row * kD + 16 * part);
-            ksr[u] = a.ks[row * (kD / 32) + (part >> 1)];
-            vsr[u] = a.vs[row * (kD / 32) + (part >> 1)];
+            const int64_t row = (static_cast<int64_t>(blk[u]) * kBS + ((key0 + NW * C::KPW * u) & 15)) * rowstride + hk;
+            kraw[u] = *reinterpret_cast<const v4u*>(a.kc + row * D + 16 * part);
+            vraw[u] = *reinterpret_cast<const v4u*>(a.vc + row * D + 16 * part);
+            ksr[u] = a.ks[row * kNC + (part >> 1)];
+            vsr[u] = a.vs[row * kNC + (part >> 1)];
         }
     };
     // keys at or past L (unused slots, clamped pages) get zero scales: their scores are masked and their
     // values must not carry a NaN or inf of memory nobody wrote into the P.V sums
     auto store_tile = [&](uint8_t* buf, int kbase) {
+        if (!stager) return;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int kappa = key0 + 8 * NW * u;
+            const int kappa = key0 + NW * C::KPW * u;
             const bool live = kbase + kappa < L;
             const float ks = live ? f16_to_f32(static_cast<uint16_t>(ksr[u])) : 0.0f;
             const _Float16 vs = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsr[u])) : static_cast<_Float16>(0.0f);
@@ -193,14 +212,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
             scale8_pair(i8x8_to_f16(vr4[0], vr4[1]), vs, vh0, vl0);
             scale8_pair(i8x8_to_f16(vr4[2], vr4[3]), vs, vh1, vl1);
             const int kr = k_row(kappa);
-            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part) * 16) = k0;
-            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot(kr, 2 * part + 1) * 16) = k1;
+            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot<D>(kr, 2 * part) * 16) = k0;
+            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot<D>(kr, 2 * part + 1) * 16) = k1;
             // the scale of group part / 2 of key kappa (both threads of the group hold it; the even one stores)
             if ((part & 1) == 0) reinterpret_cast<float*>(buf + kKs)[kappa * kNC + (part >> 1)] = ks;
-            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot(kappa, 2 * part) * 16) = vh0;
-            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot(kappa, 2 * part + 1) * 16) = vh1;
-            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot(kappa, 2 * part) * 16) = vl0;
-            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot(kappa, 2 * part + 1) * 16) = vl1;
+            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot<D>(kappa, 2 * part) * 16) = vh0;
+            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot<D>(kappa, 2 * part + 1) * 16) = vh1;
+            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot<D>(kappa, 2 * part) * 16) = vl0;
+            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot<D>(kappa, 2 * part + 1) * 16) = vl1;
         }
     };
 
@@ -213,7 +232,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
             // fresh lane offsets per n: the first tile's K reads are not kept in registers for the second
             asm volatile("" : "+v"(lane));
             const int klq = lane & 15, kg = lane >> 4;
-            const float4* ksc = reinterpret_cast<const float4*>(buf + kKs);   // [key] -> 4 group scales
+            const float* ksc = reinterpret_cast<const float*>(buf + kKs);   // [key][kNC] group scales
             v4f s[kNT];
 #pragma unroll
             for (int t = 0; t < kNT; ++t) {
@@ -221,17 +240,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
                 v4f dg[kNC];
 #pragma unroll
                 for (int c = 0; c < kNC; ++c) {
-                    const v8h kop = *reinterpret_cast<const v8h*>(buf + row * kRowB + k_slot(row, 4 * c + kg) * 16);
+                    const v8h kop = *reinterpret_cast<const v8h*>(buf + row * kRowB + k_slot<D>(row, 4 * c + kg) * 16);
                     dg[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[n][c], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                 }
                 // element i is key 16 kg + 4 t + i: its group dots meet its group scales in FP32
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float4 kq = ksc[16 * kg + 4 * t + i];
-                    float sv = dg[0][i] * kq.x;
-                    sv = __builtin_fmaf(dg[1][i], kq.y, sv);
-                    sv = __builtin_fmaf(dg[2][i], kq.z, sv);
-                    s[t][i] = __builtin_fmaf(dg[3][i], kq.w, sv);
+                    const float* kq = ksc + (16 * kg + 4 * t + i) * kNC;
+                    float kv[kNC];
+                    if constexpr (kNC == 4) {
+                        const float4 k4 = *reinterpret_cast<const float4*>(kq);
+                        kv[0] = k4.x; kv[1] = k4.y; kv[kNC - 2] = k4.z; kv[kNC - 1] = k4.w;
+                    } else {
+                        const float2 k2 = *reinterpret_cast<const float2*>(kq);
+                        kv[0] = k2.x; kv[1] = k2.y;
+                    }
+                    float sv = dg[0][i] * kv[0];
+#pragma unroll
+                    for (int c = 1; c < kNC; ++c) sv = __builtin_fmaf(dg[c][i], kv[c], sv);
+                    s[t][i] = sv;
                 }
             }
             if (masked) {
@@ -286,7 +313,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int key = 16 * g + 8 * u + 4 * h + (lq >> 2), m = lq & 3;
-                const uint8_t* p = vt + key * kRowB + v_slot(key, 2 * ct + (m >> 1)) * 16 + 8 * (m & 1);
+                const uint8_t* p = vt + key * kRowB + v_slot<D>(key, 2 * ct + (m >> 1)) * 16 + 8 * (m & 1);
                 half[h] = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s_p)(p)));
             }
             return v8h{half[0][0], half[0][1], half[0][2], half[0][3], half[1][0], half[1][1], half[1][2], half[1][3]};
@@ -352,18 +379,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
 
 }  // namespace
 
+namespace {
+template <int D>
+void launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+    const dim3 block(64 * kPrefillWaves);
+    switch (a.Hq / a.Hk) {
+        case 1: hipLaunchKernelGGL((k_paged_prefill<1, kPrefillWaves, D>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_paged_prefill<2, kPrefillWaves, D>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_paged_prefill<4, kPrefillWaves, D>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_paged_prefill<8, kPrefillWaves, D>), grid, block, 0, s, a); break;
+    }
+}
+}  // namespace
+
 int launch_prefill(const PrefillArgs& a, void* stream) {
     const int64_t items = a.nqb * a.Hk;
     if (items == 0) return SQ_OK;
     dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
-    const dim3 block(64 * kPrefillWaves);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (a.Hq / a.Hk) {
-        case 1: hipLaunchKernelGGL((k_paged_prefill<1, kPrefillWaves>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_paged_prefill<2, kPrefillWaves>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_paged_prefill<4, kPrefillWaves>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_paged_prefill<8, kPrefillWaves>), grid, block, 0, s, a); break;
-    }
+    if (a.D == 128) launch_prefill_d<128>(a, grid, s);
+    else launch_prefill_d<64>(a, grid, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_paged_prefill: kernel launch failed: %s", hipGetErrorString(e));
     return SQ_OK;

@@ -56,15 +56,28 @@ __device__ __forceinline__ float row_sumsq(const float* x) {
 // in flight before it computes any of them: row_fetch issues the loads (unconditionally,
 // so a caller passes a row index clamped into [0, T) and masks the result of a row past
 // the end), rows4 computes four steps of rows. Every lane of a row takes part in rows4
-// (the norm's butterfly and the shared root). ROPE_SPLIT_HALF here rotates all D/2 pairs (the entry point checks
-// pairs == D/2). PERTOK: a weight row per token (RowArgs::wrows), else one shared row.
+// (the norm's butterfly and the shared root). SQ_ROPE_SPLIT_HALF rotates all D/2 pairs,
+// lane-locally; kRopeSplitPart (split half over pairs < D/2, channel p with p + pairs) takes
+// each partner from the row's lanes through the wave's LDS exchange row.
+// PERTOK: a weight row per token (RowArgs::wrows), else one shared row.
 template <int NORM, int ROPE, bool PERTOK>
 struct RowRaw {
     uint2 xu, xv;     // bf16 channels 4 lc .. 4 lc + 3 and D/2 + 4 lc .. D/2 + 4 lc + 3
     float ms;         // all-heads mean square of the token
     uint2 wu, wv;     // per-token weight row, same channels as x
-    float tc[8];      // rotation table: cos 0..3 in tc[0..3], sin 0..3 in tc[4..7]
+    // rotation table: cos in tc[0..NT), sin in tc[NT..2 NT); NT = 4 pairs of the lane, or
+    // with kRopeSplitPart the pair of each of its 8 channels
+    static constexpr int NT = ROPE == kRopeSplitPart ? 8 : 4;
+    float tc[2 * NT];
 };
+
+// Pair of channel slot k (0..7) of lane lc under kRopeSplitPart, or -1 where the channel
+// passes through (c >= 2 pairs).
+template <int D>
+__device__ __forceinline__ int64_t part_pair(int lc, int k, int64_t pairs) {
+    const int64_t c = k < 4 ? 4 * lc + k : D / 2 + 4 * lc + (k - 4);
+    return c < pairs ? c : (c < 2 * pairs ? c - pairs : -1);
+}
 
 // Where the rows of a token range start (the range's first token t0 at (b, h)): a row
 // t0 + rr of a tensor sits rr times its token stride in bytes past the base; the entry
@@ -108,6 +121,14 @@ __device__ __forceinline__ void row_fetch(const RowArgs& a, const RowBase& rb, u
             const float4 v = *reinterpret_cast<const float4*>(tb + 8 * lc + 4);
             r.tc[0] = u.x; r.tc[4] = u.y; r.tc[1] = u.z; r.tc[5] = u.w;
             r.tc[2] = v.x; r.tc[6] = v.y; r.tc[3] = v.z; r.tc[7] = v.w;
+        } else if constexpr (ROPE == kRopeSplitPart) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                int64_t pair = part_pair<D>(lc, k, a.pairs);
+                if (pair < 0) pair = 0;  // not applied
+                r.tc[k] = tb[a.rp * pair];
+                r.tc[8 + k] = tb[a.rp * pair + a.rc];
+            }
         } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -146,10 +167,11 @@ __device__ __forceinline__ void inv_rms4(const float* v, int lc, float* inv) {
     inv[3] = row_lane<LPR, 3>(r);
 }
 
-// Second half: z = rotate(bf16(x * inv * w)).
+// Second half: z = rotate(bf16(x * inv * w)). xch: this row's D floats of the wave's
+// exchange rows in LDS (kRopeSplitPart only).
 template <int D, int NORM, int ROPE, bool PERTOK>
 __device__ __forceinline__ void row_apply(const RowArgs& a, const RowRaw<NORM, ROPE, PERTOK>& r, const float* x,
-                                          float inv, const float* wsh, int lc, float* z) {
+                                          float inv, const float* wsh, int lc, float* xch, float* z) {
     float y[8];
     if constexpr (NORM == SQ_NORM_NONE) {
 #pragma unroll
@@ -179,6 +201,28 @@ __device__ __forceinline__ void row_apply(const RowArgs& a, const RowRaw<NORM, R
             z[k] = __builtin_fmaf(cs, y[k], (-sn) * y[4 + k]);
             z[4 + k] = __builtin_fmaf(sn, y[k], cs * y[4 + k]);
         }
+    } else if constexpr (ROPE == kRopeSplitPart) {
+        // the row goes to LDS, each rotated channel reads its partner back: leading c < pairs
+        // with c + pairs, trailing c in [pairs, 2 pairs) with c - pairs. The fences order the
+        // wave's LDS accesses for the compiler (a wave executes its LDS operations in order).
+        *reinterpret_cast<float4*>(xch + 4 * lc) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4*>(xch + D / 2 + 4 * lc) = make_float4(y[4], y[5], y[6], y[7]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t P = a.pairs;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t c = k < 4 ? 4 * lc + k : D / 2 + 4 * lc + (k - 4);
+            const float cs = r.tc[k], sn = r.tc[8 + k];
+            if (c < P) z[k] = __builtin_fmaf(cs, y[k], (-sn) * xch[c + P]);
+            else if (c < 2 * P) z[k] = __builtin_fmaf(sn, xch[c - P], cs * y[k]);
+            else z[k] = y[k];
+        }
+        // the next row's stores wait for these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     } else {  // interleaved: channel 2p with 2p + 1
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -197,13 +241,13 @@ __device__ __forceinline__ void row_apply(const RowArgs& a, const RowRaw<NORM, R
 // Steps s0 .. s0 + 3 of a lane's fetched rows through both halves into z.
 template <int D, int NORM, int ROPE, bool PERTOK>
 __device__ __forceinline__ void rows4(const RowArgs& a, const RowRaw<NORM, ROPE, PERTOK>* raw, const float* wsh,
-                                      int lc, float (*z)[8]) {
+                                      int lc, float* xch, float (*z)[8]) {
     float x[4][8], v[4], inv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = row_stats<D, NORM, ROPE, PERTOK>(a, raw[j], x[j]);
     if constexpr (NORM != SQ_NORM_NONE) inv_rms4<D / 8>(v, lc, inv);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) row_apply<D, NORM, ROPE, PERTOK>(a, raw[j], x[j], inv[j], wsh, lc, z[j]);
+    for (int j = 0; j < 4; ++j) row_apply<D, NORM, ROPE, PERTOK>(a, raw[j], x[j], inv[j], wsh, lc, xch, z[j]);
 }
 
 // The shared weight row of a head (PERTOK == false); unused without a norm.
@@ -292,7 +336,8 @@ __global__ __launch_bounds__(256) void k_norm_stats(NormStatsArgs a) {
 // arithmetic of the step ahead of it, so two steps of loads are in flight at the start
 // and one while a step computes.
 template <int D, int NORM, int ROPE, bool CONTIG, bool PERTOK>
-__device__ __forceinline__ void kmean_block(const KmeanArgs& a, int64_t b, int64_t h, int64_t blk, int lc, int r) {
+__device__ __forceinline__ void kmean_block(const KmeanArgs& a, int64_t b, int64_t h, int64_t blk, int lc, int r,
+                                            float* xch) {
     constexpr int LPR = D / 8;
     const bool active = r < 4;
     float wsh[8];
@@ -312,7 +357,7 @@ __device__ __forceinline__ void kmean_block(const KmeanArgs& a, int64_t b, int64
     for (int j0 = 0; j0 < 16; j0 += 4) {
         __builtin_amdgcn_sched_barrier(0);  // the step's loads stay ahead of the arithmetic below
         float z[4][8];
-        rows4<D, NORM, ROPE, PERTOK>(a.r, raw + j0, wsh, lc, z);
+        rows4<D, NORM, ROPE, PERTOK>(a.r, raw + j0, wsh, lc, xch, z);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bool valid = active && blk * 64 + 4 * (j0 + j) + r < a.r.T;
@@ -348,7 +393,10 @@ __global__ __launch_bounds__(256) void k_kmean_partial(KmeanArgs a) {
     if (item >= items) return;  // uniform over the workgroup
     const int64_t h = item % a.r.H, b = (item / a.r.H) % a.r.B, blk = (item / (a.r.H * a.r.B)) * 4 + w;
     if (blk >= a.nblk) return;  // wave-uniform
-    kmean_block<D, NORM, ROPE, CONTIG, PERTOK>(a, b, h, blk, lc, r);
+    // kRopeSplitPart: each wave's exchange rows, one per row it holds at a step (512 / D rows of D)
+    __shared__ __attribute__((aligned(16))) float xch_s[ROPE == kRopeSplitPart ? 4 * 512 : 4];
+    float* xch = ROPE == kRopeSplitPart ? xch_s + w * 512 + r * D : xch_s;
+    kmean_block<D, NORM, ROPE, CONTIG, PERTOK>(a, b, h, blk, lc, r, xch);
 }
 
 // Block sums are added in chunks of 16 consecutive blocks (ascending within a chunk),
@@ -400,7 +448,7 @@ __global__ __launch_bounds__(256) void k_kmean_final(KmeanArgs a) {
 // row |v| maxima join their groups' maxima in LDS.
 template <int D, int NORM, int ROPE, bool CONTIG, bool PERTOK>
 __device__ __forceinline__ void quant_rows(const QuantArgs& a, int64_t b, int64_t h, int64_t tile, int w, int lc,
-                                           int lr, uint32_t* amax_s, float (*v)[8]) {
+                                           int lr, uint32_t* amax_s, float* xch, float (*v)[8]) {
     constexpr int LPR = D / 8, RPI = kWave / LPR, IT = 32 / RPI;
     float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0}, wsh[8];
     if (a.mean) load_row_f32<D>(a.mean + b * a.mb + h * a.mh, lc, mu);
@@ -421,7 +469,7 @@ __device__ __forceinline__ void quant_rows(const QuantArgs& a, int64_t b, int64_
     float m[IT];
 #pragma unroll
     for (int i0 = 0; i0 < IT; i0 += 4) {
-        rows4<D, NORM, ROPE, PERTOK>(a.r, raw + i0, wsh, lc, v + i0);
+        rows4<D, NORM, ROPE, PERTOK>(a.r, raw + i0, wsh, lc, xch, v + i0);
 #pragma unroll
         for (int i = i0; i < i0 + 4; ++i) {
             m[i] = 0.0f;
@@ -456,7 +504,9 @@ __global__ __launch_bounds__(256) void k_quant_qk(QuantArgs a) {
     __syncthreads();
     float v[IT][8];
     const int layout = a.layout, block = a.block;
-    quant_rows<D, NORM, ROPE, CONTIG, PERTOK>(a, b, h, tile, w, lc, lr, amax_s, v);
+    __shared__ __attribute__((aligned(16))) float xch_s[ROPE == kRopeSplitPart ? 4 * 512 : 4];  // as in k_kmean_partial
+    float* xch = ROPE == kRopeSplitPart ? xch_s + w * 512 + lr * D : xch_s;
+    quant_rows<D, NORM, ROPE, CONTIG, PERTOK>(a, b, h, tile, w, lc, lr, amax_s, xch, v);
     __syncthreads();
     const int ng = groups_per_tile(layout, block);
     const GroupMap gmap(layout, block);
@@ -631,6 +681,7 @@ void launch_quant_rope(const QuantArgs& a, dim3 grid, hipStream_t s) {
     switch (a.r.rope) {
     case SQ_ROPE_NONE: launch_quant_c<D, NORM, SQ_ROPE_NONE>(a, grid, s); break;
     case SQ_ROPE_SPLIT_HALF: launch_quant_c<D, NORM, SQ_ROPE_SPLIT_HALF>(a, grid, s); break;
+    case kRopeSplitPart: launch_quant_c<D, NORM, kRopeSplitPart>(a, grid, s); break;
     default: launch_quant_c<D, NORM, SQ_ROPE_INTERLEAVED>(a, grid, s); break;
     }
 }
@@ -661,6 +712,7 @@ void launch_kmean_rope(const KmeanArgs& a, dim3 grid, hipStream_t s) {
     switch (a.r.rope) {
     case SQ_ROPE_NONE: launch_kmean_c<D, NORM, SQ_ROPE_NONE>(a, grid, s); break;
     case SQ_ROPE_SPLIT_HALF: launch_kmean_c<D, NORM, SQ_ROPE_SPLIT_HALF>(a, grid, s); break;
+    case kRopeSplitPart: launch_kmean_c<D, NORM, kRopeSplitPart>(a, grid, s); break;
     default: launch_kmean_c<D, NORM, SQ_ROPE_INTERLEAVED>(a, grid, s); break;
     }
 }

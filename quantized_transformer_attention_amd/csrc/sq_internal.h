@@ -14,6 +14,10 @@ int fail(int status, const char* fmt, ...);
 void clear_error();
 
 // ---------------------------------------------------------------- row prologue
+// Split-half rotation over pairs < D/2 (channel p with p + pairs): an internal mode next to
+// sq_rope_mode's values, since its partner exchange needs LDS.
+constexpr int kRopeSplitPart = 3;
+
 struct RowArgs {
     const uint16_t* x;          // bf16 rows
     int64_t B, T, H, D, sb, st, sh;
@@ -24,7 +28,7 @@ struct RowArgs {
     const float* ms;            // all-heads mean squares (b, t) or nullptr
     int64_t msb, mst;
     float eps;
-    int rope;                   // sq_rope_mode
+    int rope;                   // sq_rope_mode, or kRopeSplitPart
     const float* table;
     int64_t pairs, rb, rs, rp, rc;
     bool rope_contig;           // rp == 2, rc == 1 and 16-byte aligned rows
@@ -162,7 +166,8 @@ struct CacheWriteArgs {
 };
 
 struct DecodeArgs {
-    const uint16_t* q;
+    const uint16_t* q;          // bf16 or f16 (q_f16) (N, Hq, D) at q[n*qn + h*qh + c]
+    int q_f16;
     int64_t qn, qh;
     const int8_t* kc;
     const uint16_t* ks;
@@ -184,14 +189,15 @@ struct DecodeArgs {
 };
 
 struct PrefillArgs {
-    const uint16_t* q;          // bf16 (T, Hq, D) at q[t*qt + h*qh + c]
+    const uint16_t* q;          // bf16 or f16 (q_f16) (T, Hq, D) at q[t*qt + h*qh + c]
+    int q_f16;
     int64_t qt, qh;
     const int8_t* kc;
     const uint16_t* ks;
     const int8_t* vc;
     const uint16_t* vs;
     int64_t num_blocks;
-    int Hk, Hq;
+    int Hk, Hq, D;
     const int32_t* bt;
     int64_t bt_stride;
     const int32_t* lens;        // keys per sequence (context + its queries)

@@ -74,9 +74,6 @@ int check_rope(const sq_rope* r, const sq_rows* x, const char* what) {
     if (!r->table) return fail(SQ_ERR_NULL, "%s: rope table is NULL", what);
     if (r->pairs < 1 || r->pairs > x->D / 2)
         return fail(SQ_ERR_SHAPE, "%s: rope pairs %lld outside [1, D/2]", what, (long long)r->pairs);
-    if (r->mode == SQ_ROPE_SPLIT_HALF && r->pairs != x->D / 2)
-        return fail(SQ_ERR_UNSUPPORTED, "%s: split-half rope rotates all D/2 pairs (pairs %lld, D %lld)", what,
-                    (long long)r->pairs, (long long)x->D);
     if (r->rb < 0 || r->rs < 0 || r->rp < 0) return fail(SQ_ERR_STRIDE, "%s: negative rope stride", what);
     if ((reinterpret_cast<uintptr_t>(r->table) & 3) != 0) return fail(SQ_ERR_ALIGN, "%s: rope table misaligned", what);
     return SQ_OK;
@@ -116,6 +113,11 @@ RowArgs row_args(const sq_rows* x, const sq_norm* n, const sq_rope* r) {
         a.pairs = r->pairs; a.rb = r->rb; a.rs = r->rs; a.rp = r->rp; a.rc = r->rc;
         a.rope_contig = r->rp == 2 && r->rc == 1 && (reinterpret_cast<uintptr_t>(r->table) & 15) == 0 &&
                         r->rb % 4 == 0 && r->rs % 4 == 0;
+        // split half over fewer than D/2 pairs puts a channel's partner outside the lane that holds it
+        if (a.rope == SQ_ROPE_SPLIT_HALF && r->pairs != x->D / 2) {
+            a.rope = kRopeSplitPart;
+            a.rope_contig = false;
+        }
     }
     return a;
 }

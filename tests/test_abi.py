@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(L, name), name
     assert set(names) == set(sq.EXPORTS)
-    assert L.sq_abi_version() == sq.ABI_VERSION == 3
+    assert L.sq_abi_version() == sq.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -67,7 +67,9 @@ def test_quant_validation_errors():
     assert _call_quant(_rows(), eps=-1.0) == -2
     bad_norm = sq.sq_norm(sq.NORM_HEAD, 0, None, None, 0, 0, 1e-6)
     assert _call_quant(_rows(), norm=bad_norm) == -1
-    rope = sq.sq_rope(sq.ROPE_SPLIT_HALF, 0x4000, 12, 0, 128, 2, 1)  # pairs % 8 != 0
+    rope = sq.sq_rope(sq.ROPE_SPLIT_HALF, 0x4000, 0, 0, 128, 2, 1)   # no pairs
+    assert _call_quant(_rows(), rope=rope) == -2
+    rope = sq.sq_rope(3, 0x4000, 12, 0, 128, 2, 1)                   # no such mode
     assert _call_quant(_rows(), rope=rope) == -5
     rope = sq.sq_rope(sq.ROPE_SPLIT_HALF, 0x4000, 80, 0, 128, 2, 1)  # pairs > D / 2
     assert _call_quant(_rows(), rope=rope) == -2
@@ -156,14 +158,15 @@ def test_lse_merge_validation_errors():
 
 def _call_prefill(T=10, NB=4, bs=16, Hk=2, Hq=8, D=128, q=0x1000, qt=1024, qh=128, kc=0x2000, ks=0x3000, vc=0x4000,
                   vs=0x5000, bt=0x6000, bts=4, lens=0x7000, qs=0x8000, N=2, max_len=64, scale=0.125, out=0x9000,
-                  odt=sq.SQ_F32):
+                  odt=sq.SQ_F32, qdt=sq.SQ_BF16):
     L = sq.lib()
-    return L.sq_paged_prefill(q, qt, qh, T, kc, ks, vc, vs, NB, bs, Hk, bt, bts, lens, qs, N, max_len, Hq, D, scale,
+    return L.sq_paged_prefill(q, qdt, qt, qh, T, kc, ks, vc, vs, NB, bs, Hk, bt, bts, lens, qs, N, max_len, Hq, D, scale,
                               None, out, odt, Hq * D, D, None)
 
 
 def test_paged_prefill_validation_errors():
-    assert _call_prefill(D=64) == -5                       # head dim 128 only
+    assert _call_prefill(D=96) == -5                       # head dim 64 or 128
+    assert _call_prefill(qdt=sq.SQ_F32) == -5              # q bf16 or f16
     assert _call_prefill(bs=32) == -5                      # block size 16 only
     assert _call_prefill(Hq=6, Hk=4) == -2                 # heads not a multiple
     assert _call_prefill(Hq=32, Hk=2) == -5                # Hq / Hk = 16
@@ -175,7 +178,7 @@ def test_paged_prefill_validation_errors():
     assert _call_prefill(bts=3) == -3                      # table rows shorter than max_len needs
     assert _call_prefill(q=0x1008) == -4
     assert _call_prefill(qh=132) == -4
-    assert _call_prefill(ks=0x3002) == -4
+    assert _call_prefill(ks=0x3001) == -4                  # FP16 scales
     assert _call_prefill(scale=0.0) == -2
     assert _call_prefill(odt=sq.SQ_I8) == -5               # out FP32 or bf16
     assert _call_prefill(out=0x9002) == -4
@@ -183,14 +186,15 @@ def test_paged_prefill_validation_errors():
 
 def _call_decode(N=2, NB=4, bs=16, Hk=2, Hq=8, D=128, q=0x1000, qn=1024, qh=128, kc=0x2000, ks=0x3000, vc=0x4000,
                  vs=0x5000, bt=0x6000, bts=4, lens=0x7000, max_len=64, scale=0.125, out=0x9000, odt=sq.SQ_F32,
-                 ws=0x10000, wsb=1 << 20):
+                 ws=0x10000, wsb=1 << 20, qdt=sq.SQ_BF16):
     L = sq.lib()
-    return L.sq_paged_decode(q, qn, qh, kc, ks, vc, vs, NB, bs, Hk, bt, bts, lens, N, max_len, Hq, D, scale, None,
+    return L.sq_paged_decode(q, qdt, qn, qh, kc, ks, vc, vs, NB, bs, Hk, bt, bts, lens, N, max_len, Hq, D, scale, None,
                              out, odt, Hq * D, D, ws, wsb, None)
 
 
 def test_paged_decode_validation_errors():
-    assert _call_decode(D=64) == -5                        # head dim 128 only
+    assert _call_decode(D=96) == -5                        # head dim 64 or 128
+    assert _call_decode(qdt=sq.SQ_I8) == -5                # q bf16 or f16
     assert _call_decode(bs=32) == -5                       # block size 16 only
     assert _call_decode(Hq=6, Hk=4) == -2
     assert _call_decode(Hq=32, Hk=2) == -5                 # Hq / Hk = 16
@@ -199,7 +203,8 @@ def test_paged_decode_validation_errors():
     assert _call_decode(lens=None) == -1
     assert _call_decode(bts=3) == -3                       # table rows shorter than max_len needs
     assert _call_decode(q=0x1008) == -4
-    assert _call_decode(vs=0x5004) == -4
+    assert _call_decode(vs=0x5004) == -4                   # a row of 4 FP16 scales (D 128): 8-byte aligned
+    assert _call_decode(D=64, qh=64, vs=0x5002) == -4       # 2 scales (D 64): 4-byte aligned
     assert _call_decode(scale=float("inf")) == -2
     assert _call_decode(odt=sq.SQ_FP8E4M3) == -5           # out FP32 or bf16
     assert _call_decode(out=0x9001, odt=sq.SQ_BF16) == -4
@@ -213,13 +218,13 @@ def test_paged_decode_noalloc_rejects_oversize_before_any_device_call():
     assert sq.DECODE_SCRATCH_BYTES == 64 << 20
     need = L.sq_paged_decode_workspace_bytes(64, 32, 128, 16384)
     assert need > sq.DECODE_SCRATCH_BYTES >= L.sq_paged_decode_workspace_bytes(64, 32, 128, 16128)
-    st = L.sq_paged_decode_noalloc(0x1000, 32 * 128, 128, 0x2000, 0x3000, 0x4000, 0x5000, 100, 16, 8, 0x6000, 1024,
-                                   0x7000, 64, 16384, 32, 128, 0.088, None, 0x8000, sq.SQ_F32, 32 * 128, 128, None)
+    st = L.sq_paged_decode_noalloc(0x1000, sq.SQ_BF16, 32 * 128, 128, 0x2000, 0x3000, 0x4000, 0x5000, 100, 16, 8,
+                                   0x6000, 1024, 0x7000, 64, 16384, 32, 128, 0.088, None, 0x8000, sq.SQ_F32, 32 * 128, 128, None)
     assert st == -6
     assert b"scratch" in L.sq_last_error()
     # a bad argument inside the limit is rejected by the decode's own validation (still no device call)
-    st = L.sq_paged_decode_noalloc(0x1000, 32 * 128, 128, 0x2000, 0x3000, 0x4000, 0x5000, 100, 16, 8, 0x6000, 1024,
-                                   0x7000, 4, 1000, 32, 96, 0.088, None, 0x8000, sq.SQ_F32, 32 * 128, 128, None)
+    st = L.sq_paged_decode_noalloc(0x1000, sq.SQ_BF16, 32 * 128, 128, 0x2000, 0x3000, 0x4000, 0x5000, 100, 16, 8,
+                                   0x6000, 1024, 0x7000, 4, 1000, 32, 96, 0.088, None, 0x8000, sq.SQ_F32, 32 * 128, 128, None)
     assert st == -5
 
 

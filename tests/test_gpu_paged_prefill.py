@@ -37,7 +37,7 @@ def check_rows(got, ref, what=""):
     return float(rel.max())
 
 
-def _case(seed, ctx, qlen, Hq, Hk, D=128, bs=16, extra=3):
+def _case(seed, ctx, qlen, Hq, Hk, D=128, bs=16, extra=3, q_f16=False):
     """Varlen batch over a paged q8 cache: sequence n has ctx[n] cached keys before its qlen[n] queries (their
     keys in the cache as well), pages dealt from a seeded permutation, table rows padded with -1."""
     g = np.random.default_rng(seed)
@@ -53,13 +53,16 @@ def _case(seed, ctx, qlen, Hq, Hk, D=128, bs=16, extra=3):
         bt[n, :p] = perm[o:o + p]
         o += p
     qs = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
-    q = gen.normal_bf16((int(qs[-1]), 1, Hq, D), g).reshape(-1, Hq, D)
+    if q_f16:   # binary16 queries
+        q = (g.standard_normal(size=(int(qs[-1]), Hq, D)) * 4).astype(np.float16)
+    else:
+        q = gen.normal_bf16((int(qs[-1]), 1, Hq, D), g).reshape(-1, Hq, D)
     return q, kc, ks, vc, vs, bt, lens, qs
 
 
 def _gpu(q, kc, ks, vc, vs, bt, lens, qs, scale, sinks=None, max_len=None):
     f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
-    out = sq.sq_paged_prefill(dev_bf16(q), dev(kc), f16(ks), dev(vc), f16(vs), dev(bt), dev(lens), dev(qs),
+    out = sq.sq_paged_prefill(dev(q) if q.dtype == np.float16 else dev_bf16(q), dev(kc), f16(ks), dev(vc), f16(vs), dev(bt), dev(lens), dev(qs),
                               int(lens.max()) if max_len is None else max_len, scale,
                               sinks=dev(sinks) if sinks is not None else None)
     torch.cuda.synchronize()
@@ -86,6 +89,18 @@ def test_paged_prefill_parity(case):
     got = _gpu(q, kc, ks, vc, vs, bt, lens, qs, scale)
     rel = check_rows(got, ref, "prefill")
     print("max row rel %.3g" % rel)
+
+
+@pytest.mark.parametrize("D,q_f16", [(64, False), (64, True), (128, True)])
+def test_paged_prefill_head_dims_and_q_dtypes(D, q_f16):
+    """Head dim 64 and binary16 queries, ragged varlen batch with G = 1, 2 and 8 launches."""
+    for ctx, qlen, Hq, Hk in (((0, 100, 300), (90, 33, 1), 8, 4), ((0, 7), (200, 150), 4, 4), ((64,), (129,), 16, 2)):
+        print("prefill D %d q_f16 %d" % (D, q_f16), ctx, qlen, Hq, Hk, flush=True)
+        q, kc, ks, vc, vs, bt, lens, qs = _case(6200 + D + sum(ctx) + Hq, ctx, qlen, Hq, Hk, D=D, q_f16=q_f16)
+        scale = 1 / math.sqrt(D)
+        ref = O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale)
+        got = _gpu(q, kc, ks, vc, vs, bt, lens, qs, scale)
+        check_rows(got, ref, "prefill D %d" % D)
 
 
 def test_paged_prefill_sinks_and_max_len_bound():

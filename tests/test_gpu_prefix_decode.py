@@ -138,7 +138,7 @@ def test_cfg3_joint_with_q8_prefix_full_size():
 
 
 # ------------------------------------------------------------------------------------------------ paged decode
-def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3, v_sigma=1.0):
+def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3, v_sigma=1.0, q_f16=False):
     g = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int32)
     pages = (lens + bs - 1) // bs
@@ -154,13 +154,20 @@ def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3, v_sigma=1.0):
     vx = g.standard_normal(size=(NB, bs, Hk, D), dtype=np.float32) * np.float32(v_sigma)
     kc, ks = _q8(kx)
     vc, vs = _q8(vx)
-    q = gen.normal_bf16((len(lens), 1, Hq, D), g).reshape(len(lens), Hq, D)
+    if q_f16:   # binary16 queries, spread over f16's range
+        q = (g.standard_normal(size=(len(lens), Hq, D)) * 4).astype(np.float16)
+    else:
+        q = gen.normal_bf16((len(lens), 1, Hq, D), g).reshape(len(lens), Hq, D)
     return q, kc, ks, vc, vs, bt, lens
+
+
+def _dev_q(q):
+    return dev(q) if q.dtype == np.float16 else dev_bf16(q)
 
 
 def _gpu_decode(q, kc, ks, vc, vs, bt, lens, scale, max_len=None):
     f16 = lambda a: dev(a.view(np.int16)).view(torch.float16)
-    out = sq.sq_paged_decode(dev_bf16(q), dev(kc), f16(ks), dev(vc), f16(vs), dev(bt), dev(lens),
+    out = sq.sq_paged_decode(_dev_q(q), dev(kc), f16(ks), dev(vc), f16(vs), dev(bt), dev(lens),
                              int(lens.max()) if max_len is None else max_len, scale)
     torch.cuda.synchronize()
     return host(out)
@@ -175,6 +182,19 @@ def test_paged_decode_parity(Hq, Hk):
     ref = O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale)
     got = _gpu_decode(q, kc, ks, vc, vs, bt, lens, scale)
     check_float(got, ref, None, what="decode out")
+    assert cosine(got, ref) >= 0.999999
+
+
+@pytest.mark.parametrize("D,q_f16,Hq,Hk", [(64, False, 8, 2), (64, True, 16, 2), (128, True, 8, 2), (64, False, 4, 4)])
+def test_paged_decode_head_dims_and_q_dtypes(D, q_f16, Hq, Hk):
+    """Head dim 64 (two q8 groups per row) and binary16 queries, against the oracle's binary64 decode."""
+    lens = [1, 17, 255, 256, 257, 700]
+    print("decode D %d q_f16 %d Hq %d Hk %d" % (D, q_f16, Hq, Hk), flush=True)
+    q, kc, ks, vc, vs, bt, lens = _decode_case(lens, Hq, Hk, 3100 + D + Hq + q_f16, D=D, q_f16=q_f16)
+    scale = 1.0 / np.sqrt(float(D))
+    ref = O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale)
+    got = _gpu_decode(q, kc, ks, vc, vs, bt, lens, scale)
+    check_float(got, ref, None, what="decode D %d out" % D)
     assert cosine(got, ref) >= 0.999999
 
 

@@ -31,17 +31,25 @@ def _case(B, T, H, D, seed, outliers=0):
 LAYOUTS = [(0, 32), (0, 64), (0, 128), (1, 32), (2, 64), (3, 128)]
 
 
+# (mode, pairs): all D/2 pairs, fewer (split half over a pair count that is no multiple of
+# a lane's 4 channels, so partners sit in other lanes; interleaved over D/2 - 3)
+ROPES = {"none": (O.ROPE_NONE, 0), "split": (O.ROPE_SPLIT_HALF, None), "interleaved_part": (O.ROPE_INTERLEAVED, -3),
+         "split_part": (O.ROPE_SPLIT_HALF, 5)}
+
+
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("norm", [O.NORM_NONE, O.NORM_HEAD, O.NORM_ALL_HEADS])
-@pytest.mark.parametrize("rope", [O.ROPE_NONE, O.ROPE_SPLIT_HALF, O.ROPE_INTERLEAVED])
-def test_quant_bit_exact_ragged(D, norm, rope):
+@pytest.mark.parametrize("rope_name", list(ROPES))
+def test_quant_bit_exact_ragged(D, norm, rope_name):
     B, T, H = 2, 333, 3
-    print("quant D=%d norm=%d rope=%d" % (D, norm, rope), flush=True)
-    x = _case(B, T, H, D, 100 + D + 10 * norm + rope)
+    rope, pp = ROPES[rope_name]
+    pairs = D // 2 if pp is None else (D // 2 + pp if pp < 0 else D // 4 + pp)
+    print("quant D=%d norm=%d rope=%s pairs=%d" % (D, norm, rope_name, pairs), flush=True)
+    x = _case(B, T, H, D, 100 + D + 10 * norm + list(ROPES).index(rope_name))
     wd = H * D if norm == O.NORM_ALL_HEADS else D
     w = gen.uniform_bf16((2, wd), gen.rng(7, 1))
     wrows = (np.arange(T) >= 100).astype(np.int32)
-    table = gen.rope_table(T, D // 2 if rope == O.ROPE_SPLIT_HALF else D // 2 - 3, start=5)
+    table = gen.rope_table(T, pairs, start=5)
     pro = _pro(norm, rope, w, table, wrows)
     mu = O.kmean(x, pro)
     n, r = _gpu_specs(norm, rope, w, table, wrows)

@@ -228,6 +228,15 @@ def test_rope_is_complex_rotation():
     np.testing.assert_array_equal(zid, f32(x))
     zp = O.prologue_rows(x, O.Prologue(rope=O.ROPE_SPLIT_HALF, table=np.ascontiguousarray(tb[:, :, :, :16])))
     np.testing.assert_array_equal(zp[..., 32:], f32(x)[..., 32:])
+    # split half over Pp < D/2 pairs rotates the leading 2 Pp channels as a row of its own: channel p
+    # with p + Pp (not p + D/2), pair p of the table
+    Pp = 21
+    tp = gen.rope_table(T, Pp, start=7)
+    zq = O.prologue_rows(x, O.Prologue(rope=O.ROPE_SPLIT_HALF, table=tp)).astype(np.float64)
+    cq = (xv[..., :Pp] + 1j * xv[..., Pp:2 * Pp]) * (tp[0, :, 0, :, 0] + 1j * tp[0, :, 0, :, 1])[None, :, None, :]
+    np.testing.assert_allclose(zq[..., :Pp], cq.real, atol=1e-5)
+    np.testing.assert_allclose(zq[..., Pp:2 * Pp], cq.imag, atol=1e-5)
+    np.testing.assert_array_equal(zq[..., 2 * Pp:], xv[..., 2 * Pp:])
     # rotation keeps pair norms
     n0 = xv[..., :P] ** 2 + xv[..., P:] ** 2
     n1 = z[..., :P] ** 2 + z[..., P:] ** 2
@@ -674,6 +683,30 @@ def test_paged_decode_equals_contiguous_attention():
     # one key (L = 1): out = v
     np.testing.assert_allclose(out[0], np.repeat(vc[bt[0, 0], 0].astype(np.float64) * 2.0 ** -4, 4, axis=0),
                                rtol=1e-15)
+
+
+def test_paged_q_in_binary16_by_brute_force():
+    """q given as IEEE binary16 (the f16 query dtype) is read as binary16, not as bf16 bits: the decode equals a
+    numpy softmax over the gathered exact q8 keys and values, and the prefill's last rows equal that decode."""
+    g = np.random.default_rng(56)
+    q, kc, ks, vc, vs, bt, lens = _paged_case(g, D=128)
+    q16 = (g.standard_normal(q.shape) * 3).astype(np.float16)
+    scale = 0.0884
+    out = O.paged_decode(q16, kc, ks, vc, vs, bt, lens, scale)
+    kf = kc.astype(np.float64) * np.repeat(ks.view(np.float16).astype(np.float64), 32, axis=-1)
+    vf = vc.astype(np.float64) * np.repeat(vs.view(np.float16).astype(np.float64), 32, axis=-1)
+    for n, L in enumerate(lens):
+        pages = bt[n, :(L + 15) // 16]
+        kseq = kf[pages].reshape(-1, 2, 128)[:L]
+        vseq = vf[pages].reshape(-1, 2, 128)[:L]
+        for h in range(8):
+            s_ = kseq[:, h // 4] @ q16[n, h].astype(np.float64) * scale
+            p_ = np.exp(s_ - s_.max())
+            ref = (p_ / p_.sum()) @ vseq[:, h // 4]
+            np.testing.assert_allclose(out[n, h], ref, rtol=1e-12, atol=1e-12)
+    # one query per sequence as a prefill: each row is that sequence's decode
+    qs = np.arange(len(lens) + 1, dtype=np.int32)
+    np.testing.assert_array_equal(O.paged_prefill(q16, kc, ks, vc, vs, bt, lens, qs, scale), out)
 
 
 def test_paged_decode_block_permutation_invariance_and_dominant_key():
