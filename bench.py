@@ -19,7 +19,12 @@ attention workloads; GB/s of algorithmic bytes for the quantizer and decode).
 Prints ONE JSON line. roofline: the dominant kernel's algorithmic rate, from HIP events
 around its launches on the stream it runs on, against MI355X's published peak; traffic
 from the committed rocprofv3 counter summary when it was taken on the current kernel
-source. cpu_baseline: the CPU oracle timed on this host on a bounded sample.
+source. cpu_baseline (video, quantizer and decode workloads): the CPU oracle timed on this
+host on the same seeded inputs, in full where it finishes in seconds, else on sampled
+query rows with the full-size time extrapolated (the sample is named in the line).
+
+`python bench.py traffic ...` (see traffic_main) turns rocprofv3 FETCH_SIZE / WRITE_SIZE
+counter runs into the HBM bytes per launch stored in profiles/traffic.json.
 """
 from __future__ import annotations
 
@@ -148,12 +153,12 @@ def video_like(args, torch, sq, gen, c, timer, causal=False, sinks=None):
         "norm_stats_q": elems * 2 + c.B * c.Sq * 4, "norm_stats_k": elems * 2 + c.B * c.Sk * 4,
         "kmean": elems * 2, "quant_q": elems * 3, "quant_k": elems * 3, "quant_v": elems * 5,
     }
-    return step, bytes_
+    return step, bytes_, inp
 
 
 def run_video(args, torch, sq, gen, timer):
     c = gen.CFG2
-    step, bytes_ = video_like(args, torch, sq, gen, c, timer)
+    step, bytes_, inp = video_like(args, torch, sq, gen, c, timer)
     flops = c.flops()
     res = time_steps(args, torch, step, timer)
     attn_ms = timer.avg_ms("attn")
@@ -173,6 +178,9 @@ def run_video(args, torch, sq, gen, timer):
         "stages_gbs": {n: b / (timer.avg_ms(n) * 1e-3) / 1e9 for n, b in bytes_.items()},
         "core_pct_of_int8_peak": 100.0 * achieved / PEAK_TFLOPS_INT8,
     }
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_video(args, c, inp)
     return res, line
 
 
@@ -183,7 +191,7 @@ def run_causal(args, torch, sq, gen, timer):
 
     c = gen.CFG2
     sinks = torch.from_numpy(gen.rng(c.seed, gen.S_EXTRA).uniform(-1.0, 2.0, size=c.H).astype(np.float32)).cuda()
-    step, bytes_ = video_like(args, torch, sq, gen, c, timer, causal=True, sinks=sinks)
+    step, bytes_, _ = video_like(args, torch, sq, gen, c, timer, causal=True, sinks=sinks)
     flops = 4.0 * c.B * c.H * c.D * c.Sq * (c.Sq + 1) / 2
     res = time_steps(args, torch, step, timer)
     attn_ms = timer.avg_ms("attn")
@@ -208,7 +216,7 @@ def run_joint(args, torch, sq, gen, timer):
     import numpy as np
 
     c = gen.CFG3
-    step_proj, bytes_ = video_like(args, torch, sq, gen, c, timer)
+    step_proj, bytes_, _ = video_like(args, torch, sq, gen, c, timer)
     dev = torch.device("cuda:0")
     g = gen.rng(c.seed, gen.S_EXTRA)
     kc, ks = gen.q8_like((1, c.prefix, c.Hk, c.D), g)
@@ -246,7 +254,6 @@ def run_quantizer(args, torch, sq, gen, timer):
     dev = torch.device("cuda:0")
     x, w, table = gen.quant_inputs(c)
     xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-    del x
     norm = sq.Norm(sq.NORM_HEAD, torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev), None, None, c.eps)
     rope = sq.Rope(sq.ROPE_SPLIT_HALF, torch.from_numpy(table).to(dev))
     smq = gen.sm_scale_q(c.D)
@@ -284,6 +291,9 @@ def run_quantizer(args, torch, sq, gen, timer):
         "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
         "stages_gbs": {n: b / (timer.avg_ms(n) * 1e-3) / 1e9 for n, b in bytes_.items()},
     }
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_quantizer(args, c, x, w, table, runs, total)
     return res, line
 
 
@@ -297,8 +307,8 @@ def run_decode(args, torch, sq, gen, timer):
     vc, vs = gen.q8_like((NB, c.bs, c.Hk, c.D), g)
     f16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.float16).to(dev)
     kd, ksd, vd, vsd = torch.from_numpy(kc).to(dev), f16(ks), torch.from_numpy(vc).to(dev), f16(vs)
-    del kc, vc
-    q = torch.from_numpy(gen.decode_query(c).view(np.int16)).view(torch.bfloat16).to(dev)
+    qh = gen.decode_query(c)
+    q = torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(dev)
     btd, ld = torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev)
     ws = sq.Workspace(dev)
     out = torch.empty((c.N, c.Hq, c.D), dtype=torch.float32, device=dev)
@@ -323,6 +333,9 @@ def run_decode(args, torch, sq, gen, timer):
                                             float(nbytes)),
                      "avg_launch_ms": d_ms, "bytes_per_launch": nbytes},
     }
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_decode(args, c, qh, kc, ks, vc, vs, bt, lens, nbytes)
     return res, line
 
 
@@ -465,49 +478,136 @@ def time_steps(args, torch, step, timer):
 
 
 # ---------------------------------------------------------------------------------------------- CPU baseline
-def cpu_baseline_video(args):
-    """The oracle's quantized attention core on sampled query rows (all 40 heads, all 32760 keys) of the video
-    workload's shapes: seeded INT8 codes and scales in THREAD_Q / THREAD_K layouts and FP8 values."""
+def _timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def cpu_baseline_video(args, c, inp):
+    """The oracle on the benchmark's own seeded video inputs: the prologue stages (all-heads mean squares, k mean,
+    fused q and k quantization, V to FP8) in full, then the quantized attention core on sampled query rows (every
+    head, every key), as many as fit in --cpu-seconds. Its full-size step time is the prologue's plus the core's per
+    row times Sq (the core's work is linear in the rows); value is the workload's TFLOPS at that step time."""
     import numpy as np
 
     import gen
     import oracle as O
-    c = gen.CFG2
-    g = np.random.default_rng(c.seed)
-    qc = g.integers(-127, 128, size=(1, c.Sq, c.H, c.D), dtype=np.int8)
-    kc = g.integers(-127, 128, size=(1, c.Sk, c.H, c.D), dtype=np.int8)
-    qs = g.uniform(1e-3, 4e-3, size=(1, c.H, O.scale_count(c.Sq, 1, 32))).astype(np.float32)
-    ks = g.uniform(1e-3, 4e-3, size=(1, c.H, O.scale_count(c.Sk, 2, 64))).astype(np.float32)
-    v8 = g.integers(0, 0x7f, size=(1, c.Sk, c.H, c.D), dtype=np.uint8) | (g.integers(0, 2, size=(1, c.Sk, c.H, c.D),
-                                                                                       dtype=np.uint8) << 7)
-    vs = np.full((1, c.H, c.D), 0.01, np.float32)
-    q, k = O.QK(qc, qs, 1, 32), O.QK(kc, ks, 2, 64)
+    pq = O.Prologue(norm=O.NORM_ALL_HEADS, weight=inp.wq, weight_rows=inp.weight_rows, eps=c.eps,
+                    rope=O.ROPE_SPLIT_HALF, table=inp.table)
+    pk = O.Prologue(norm=O.NORM_ALL_HEADS, weight=inp.wk, weight_rows=inp.weight_rows, eps=c.eps,
+                    rope=O.ROPE_SPLIT_HALF, table=inp.table)
+    ql, qb = gen.LAYOUT[c.q_layout], c.q_block
+    kl, kb = gen.LAYOUT[c.k_layout], c.k_block
+    t_pro = 0.0
+    _, t = _timed(lambda: (O.mean_sq_all_heads(inp.q), O.mean_sq_all_heads(inp.k)))
+    t_pro += t
+    mu, t = _timed(lambda: O.kmean(inp.k, pk))
+    t_pro += t
+    (qc, qs), t = _timed(lambda: O.quant_qk(inp.q, pq, ql, qb, sm_scale=gen.sm_scale_q(c.D)))
+    t_pro += t
+    (kc, ks), t = _timed(lambda: O.quant_qk(inp.k, pk, kl, kb, mean=mu))
+    t_pro += t
+    (v8, vs), t = _timed(lambda: O.quant_v_fp8(inp.v))
+    t_pro += t
+    q, k = O.QK(qc, qs, ql, qb), O.QK(kc, ks, kl, kb)
+    rows = np.random.default_rng(c.seed + 1).permutation(c.Sq).astype(np.int64)
+    done, t_core, chunk = 0, 0.0, 2 * O.num_threads()
+    while t_core < args.cpu_seconds and done < c.Sq:
+        sel = np.sort(rows[done:done + chunk])
+        _, t = _timed(lambda: O.attn(q, k, v8, True, vs, kv_tile=c.kv_tile, rows=sel, want_allow=False))
+        t_core += t
+        done += sel.size
+    step_s = t_pro + t_core / done * c.Sq
+    return {"value": c.flops() / step_s / 1e12, "unit": "TFLOPS", "cores": O.num_threads(), "kind": "oracle",
+            "sample": "the benchmark's seeded inputs: norm statistics, k mean, q/k quantization and V to FP8 in full "
+                      "(%.1f s), the attention core on %d random query rows x 40 heads x 32760 keys (%.1f s); full "
+                      "step extrapolated linearly in query rows: %.0f s" % (t_pro, done, t_core, step_s),
+            "step_s_extrapolated": step_s, "prologue_s": t_pro, "core_s_per_row": t_core / done}
 
-    def timed(seconds, chunk):
-        rows_done, t_used = 0, 0.0
-        while t_used < seconds and rows_done < c.Sq:
-            rows = np.arange(rows_done, rows_done + chunk, dtype=np.int64)
-            t0 = time.perf_counter()
-            O.attn(q, k, v8, True, vs, kv_tile=c.kv_tile, rows=rows, want_allow=False)
-            t_used += time.perf_counter() - t0
-            rows_done += chunk
-        return rows_done, t_used
 
-    cores = O.num_threads()
-    rows_done, t_used = timed(args.cpu_seconds, 8)
-    O.set_num_threads(1)                      # the same oracle on one core, a shorter sample
-    rows_1, t_1 = timed(args.cpu_seconds / 3, 1)
-    O.set_num_threads(cores)
-    flops = 4.0 * rows_done * c.H * c.Sk * c.D
-    return {"value": flops / t_used / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
-            "sample": "quantized core (INT8 Q.K^T, FP32 softmax, FP8 P.V) on %d query rows x 40 heads x 32760 keys "
-                      "of the video workload, %.1f s" % (rows_done, t_used),
-            "value_1core": 4.0 * rows_1 * c.H * c.Sk * c.D / t_1 / 1e12,
-            "sample_1core": "%d query rows on one thread, %.1f s" % (rows_1, t_1)}
+def cpu_baseline_quantizer(args, c, x, w, table, runs, total_bytes):
+    """The oracle's k mean and five quantizer runs on the benchmark's own seeded tensor, in full."""
+    import gen
+    import oracle as O
+    pro = O.Prologue(norm=O.NORM_HEAD, weight=w, eps=c.eps, rope=O.ROPE_SPLIT_HALF, table=table)
+    mu, t_all = _timed(lambda: O.kmean(x, pro))
+    for _, m, sm, lay, blk in runs:
+        _, t = _timed(lambda: O.quant_qk(x, pro, lay, blk, mean=mu if m else None, sm_scale=sm, scale_eps=1e-7))
+        t_all += t
+    return {"value": total_bytes / t_all / 1e9, "unit": "GB/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": "the whole step on the benchmark's seeded %d x %d x %d x %d tensor (k mean + 5 quantizer runs), "
+                      "%.1f s" % (c.B, c.T, c.H, c.D, t_all)}
+
+
+def cpu_baseline_decode(args, c, q, kc, ks, vc, vs, bt, lens, nbytes):
+    """The oracle's binary64 paged decode on the benchmark's own seeded cache and queries, all 64 sequences."""
+    import oracle as O
+    _, t = _timed(lambda: O.paged_decode(q, kc, ks, vc, vs, bt, lens, c.scale))
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": "the whole step (%d sequences, %d cached positions, %d query heads) on the benchmark's seeded "
+                      "cache, %.1f s" % (c.N, int(lens.sum()), c.Hq, t)}
+
+
+# ---------------------------------------------------------------------------------------------- traffic
+COPY_BYTES = 1 << 30  # the copy workload: 1 GiB read and 1 GiB written
+
+
+def _per_dispatch_kib(d, counter, regex):
+    """Mean counter value (KiB) over the dispatches of kernels matching regex in a rocprofv3 -d directory."""
+    import csv
+    import re
+    with open(os.path.join(d, "run_counter_collection.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] != counter or not re.search(regex, r["Kernel_Name"]):
+            continue
+        vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        sys.exit("no %s values for /%s/ in %s" % (counter, regex, d))
+    return sum(vals.values()) / len(vals)
+
+
+def traffic_main(argv):
+    """bench.py traffic KEY KERNEL_REGEX UNITS SOURCES FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+
+    HBM bytes per launch of a benchmarked kernel from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE: KiB per
+    dispatch), each scaled by what the same counter reads for the copy workload (1 GiB read, 1 GiB written), since on
+    this GPU the counters see only part of the memory channels. Stored in profiles/traffic.json under KEY with UNITS
+    (the algorithmic flops or bytes per launch the bench line uses) and a hash of SOURCES (comma-separated names under
+    csrc/): the bench reports the figure only while those sources are unchanged."""
+    if len(argv) != 8:
+        sys.exit(traffic_main.__doc__)
+    key, regex, units, sources, fd, wd, cfd, cwd = argv
+    fetch = _per_dispatch_kib(fd, "FETCH_SIZE", regex)
+    write = _per_dispatch_kib(wd, "WRITE_SIZE", regex)
+    copy_regex = "copyBuffer|elementwise|copy"
+    f_fac = COPY_BYTES / (_per_dispatch_kib(cfd, "FETCH_SIZE", copy_regex) * 1024.0)
+    w_fac = COPY_BYTES / (_per_dispatch_kib(cwd, "WRITE_SIZE", copy_regex) * 1024.0)
+    fetch_b, write_b = fetch * 1024.0 * f_fac, write * 1024.0 * w_fac
+    files = sources.split(",")
+    entry = {"source_sha": source_sha(files), "sources": files, "units": float(units),
+             "bytes_per_launch": fetch_b + write_b, "fetch_bytes": fetch_b, "write_bytes": write_b,
+             "fetch_kib_raw": fetch, "write_kib_raw": write, "fetch_scale": f_fac, "write_scale": w_fac}
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        table = {}
+    table[key] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print("%s: fetch %.4g GB + write %.4g GB per launch (raw %.0f / %.0f KiB, scales %.3f / %.3f)"
+          % (key, fetch_b / 1e9, write_b / 1e9, fetch, write, f_fac, w_fac))
 
 
 # ---------------------------------------------------------------------------------------------- main
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "traffic":
+        traffic_main(sys.argv[2:])
+        return
     args = parse()
     if args.gpus != 1:
         sys.exit("bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus %d)" % args.gpus)
@@ -532,9 +632,6 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": line.pop("dtype"), "data": "synthetic (seeded)",
            "config": line.pop("config")}
     out.update(line)
-    if not args.no_cpu_baseline and args.workload == "video":
-        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline_video(args)
     print(json.dumps(out), flush=True)
 
 

@@ -448,8 +448,8 @@ inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
 int launch_v_transpose(const VTransposeArgs& a, void* stream) {
     dim3 grid(static_cast<unsigned>(a.Spad / 64), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
-    if (a.D == 128) hipLaunchKernelGGL(k_v_transpose<128>, grid, dim3(256), 0, S(stream), a);
-    else hipLaunchKernelGGL(k_v_transpose<64>, grid, dim3(256), 0, S(stream), a);
+    if (a.D == 128) SQ_LAUNCH(k_v_transpose<128>, grid, dim3(256), 0, S(stream), a);
+    else SQ_LAUNCH(k_v_transpose<64>, grid, dim3(256), 0, S(stream), a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_attn: V staging launch failed: %s", hipGetErrorString(e));
     return SQ_OK;
@@ -462,18 +462,18 @@ int launch_attn(const AttnArgs& a, void* stream) {
     hipStream_t s = S(stream);
     if (a.v_fp8) {
         if (a.kv_tile == 128) {
-            if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 128, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((k_attn<64, 128, true>), grid, dim3(256), 0, s, a);
+            if (a.D == 128) SQ_LAUNCH((k_attn<128, 128, true>), grid, dim3(256), 0, s, a);
+            else SQ_LAUNCH((k_attn<64, 128, true>), grid, dim3(256), 0, s, a);
         } else {
-            if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 64, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((k_attn<64, 64, true>), grid, dim3(256), 0, s, a);
+            if (a.D == 128) SQ_LAUNCH((k_attn<128, 64, true>), grid, dim3(256), 0, s, a);
+            else SQ_LAUNCH((k_attn<64, 64, true>), grid, dim3(256), 0, s, a);
         }
     } else if (a.kv_tile == 128) {
-        if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 128, false>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_attn<64, 128, false>), grid, dim3(256), 0, s, a);
+        if (a.D == 128) SQ_LAUNCH((k_attn<128, 128, false>), grid, dim3(256), 0, s, a);
+        else SQ_LAUNCH((k_attn<64, 128, false>), grid, dim3(256), 0, s, a);
     } else {
-        if (a.D == 128) hipLaunchKernelGGL((k_attn<128, 64, false>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_attn<64, 64, false>), grid, dim3(256), 0, s, a);
+        if (a.D == 128) SQ_LAUNCH((k_attn<128, 64, false>), grid, dim3(256), 0, s, a);
+        else SQ_LAUNCH((k_attn<64, 64, false>), grid, dim3(256), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_attn: kernel launch failed: %s", hipGetErrorString(e));

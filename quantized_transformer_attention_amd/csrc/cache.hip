@@ -107,11 +107,11 @@ int launch_cache_write(const CacheWriteArgs& a, bool f32, void* stream) {
     dim3 grid(static_cast<unsigned>((rows + per_wg - 1) / per_wg));
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.D == 128) {
-        if (f32) hipLaunchKernelGGL((k_q8_cache_write<128, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_q8_cache_write<128, false>), grid, dim3(256), 0, s, a);
+        if (f32) SQ_LAUNCH((k_q8_cache_write<128, true>), grid, dim3(256), 0, s, a);
+        else SQ_LAUNCH((k_q8_cache_write<128, false>), grid, dim3(256), 0, s, a);
     } else {
-        if (f32) hipLaunchKernelGGL((k_q8_cache_write<64, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_q8_cache_write<64, false>), grid, dim3(256), 0, s, a);
+        if (f32) SQ_LAUNCH((k_q8_cache_write<64, true>), grid, dim3(256), 0, s, a);
+        else SQ_LAUNCH((k_q8_cache_write<64, false>), grid, dim3(256), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_q8_cache_write: kernel launch failed: %s", hipGetErrorString(e));

@@ -411,12 +411,12 @@ void launch_decode_d(const DecodeArgs& a, hipStream_t s) {
     const int64_t chunks = static_cast<int64_t>(a.segs) * a.N;      // (sequence, segment) pairs
     dim3 g1(static_cast<unsigned>((chunks + 7) / 8 * 8 * a.Hk));
     switch (a.Hq / a.Hk) {
-    case 1: hipLaunchKernelGGL((k_decode_split<1, D>), g1, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_split<2, D>), g1, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_split<4, D>), g1, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_decode_split<8, D>), g1, dim3(256), 0, s, a); break;
+    case 1: SQ_LAUNCH((k_decode_split<1, D>), g1, dim3(256), 0, s, a); break;
+    case 2: SQ_LAUNCH((k_decode_split<2, D>), g1, dim3(256), 0, s, a); break;
+    case 4: SQ_LAUNCH((k_decode_split<4, D>), g1, dim3(256), 0, s, a); break;
+    default: SQ_LAUNCH((k_decode_split<8, D>), g1, dim3(256), 0, s, a); break;
     }
-    hipLaunchKernelGGL(k_decode_reduce<D>, dim3(static_cast<unsigned>(a.Hq), static_cast<unsigned>(a.N)), dim3(D), 0, s,
+    SQ_LAUNCH(k_decode_reduce<D>, dim3(static_cast<unsigned>(a.Hq), static_cast<unsigned>(a.N)), dim3(D), 0, s,
                        a);
 }
 }  // namespace

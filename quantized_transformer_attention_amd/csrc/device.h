@@ -5,10 +5,20 @@
 #include <cstdint>
 
 #include "../../include/sq.h"
+#include "sq_internal.h"
 
 namespace sq {
 
 constexpr int kWave = 64;
+
+// Every kernel launch of the library: with SQ_TRACE set in the environment (not "0") it is first
+// logged to stderr (kernel, grid, block, stream), then enqueued.
+#define SQ_LAUNCH(K, G, B, SH, S, ...)                                                                       \
+    do {                                                                                                     \
+        const dim3 sq_g_ = (G), sq_b_ = (B);                                                                 \
+        if (::sq::trace_enabled()) ::sq::trace_launch(#K, sq_g_.x, sq_g_.y, sq_g_.z, sq_b_.x, (SH), (S));    \
+        hipLaunchKernelGGL(K, sq_g_, sq_b_, SH, S, __VA_ARGS__);                                              \
+    } while (0)
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }

@@ -67,8 +67,8 @@ int launch_lse_merge(const MergeArgs& a, void* stream) {
     const int64_t per_wg = 4 * kRowSteps * (kWave / (a.D / 4));
     dim3 grid(static_cast<unsigned>((rows + per_wg - 1) / per_wg));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (a.D == 128) hipLaunchKernelGGL(k_lse_merge<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_lse_merge<64>, grid, dim3(256), 0, s, a);
+    if (a.D == 128) SQ_LAUNCH(k_lse_merge<128>, grid, dim3(256), 0, s, a);
+    else SQ_LAUNCH(k_lse_merge<64>, grid, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_lse_merge: kernel launch failed: %s", hipGetErrorString(e));
     return SQ_OK;

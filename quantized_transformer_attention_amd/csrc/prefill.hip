@@ -384,10 +384,10 @@ template <int D>
 void launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t s) {
     const dim3 block(64 * kPrefillWaves);
     switch (a.Hq / a.Hk) {
-        case 1: hipLaunchKernelGGL((k_paged_prefill<1, kPrefillWaves, D>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_paged_prefill<2, kPrefillWaves, D>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_paged_prefill<4, kPrefillWaves, D>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_paged_prefill<8, kPrefillWaves, D>), grid, block, 0, s, a); break;
+        case 1: SQ_LAUNCH((k_paged_prefill<1, kPrefillWaves, D>), grid, block, 0, s, a); break;
+        case 2: SQ_LAUNCH((k_paged_prefill<2, kPrefillWaves, D>), grid, block, 0, s, a); break;
+        case 4: SQ_LAUNCH((k_paged_prefill<4, kPrefillWaves, D>), grid, block, 0, s, a); break;
+        default: SQ_LAUNCH((k_paged_prefill<8, kPrefillWaves, D>), grid, block, 0, s, a); break;
     }
 }
 }  // namespace

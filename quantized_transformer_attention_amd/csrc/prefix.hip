@@ -386,11 +386,11 @@ int launch_prefix(const PrefixArgs& a, void* stream) {
     dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
     hipStream_t s = S(stream);
     if (a.kv_tile == 128) {
-        if (a.D == 128) hipLaunchKernelGGL((k_prefix<128, 128>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_prefix<64, 128>), grid, dim3(256), 0, s, a);
+        if (a.D == 128) SQ_LAUNCH((k_prefix<128, 128>), grid, dim3(256), 0, s, a);
+        else SQ_LAUNCH((k_prefix<64, 128>), grid, dim3(256), 0, s, a);
     } else {
-        if (a.D == 128) hipLaunchKernelGGL((k_prefix<128, 64>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_prefix<64, 64>), grid, dim3(256), 0, s, a);
+        if (a.D == 128) SQ_LAUNCH((k_prefix<128, 64>), grid, dim3(256), 0, s, a);
+        else SQ_LAUNCH((k_prefix<64, 64>), grid, dim3(256), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_attn_prefix_lse_merge: kernel launch failed: %s", hipGetErrorString(e));

@@ -665,8 +665,8 @@ inline int check_launch(const char* what) {
 
 template <int D, int NORM, int ROPE, bool PERTOK>
 void launch_quant_w(const QuantArgs& a, dim3 grid, hipStream_t s) {
-    if (a.r.rope_contig) hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, true, PERTOK>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_quant_qk<D, NORM, ROPE, false, PERTOK>), grid, dim3(256), 0, s, a);
+    if (a.r.rope_contig) SQ_LAUNCH((k_quant_qk<D, NORM, ROPE, true, PERTOK>), grid, dim3(256), 0, s, a);
+    else SQ_LAUNCH((k_quant_qk<D, NORM, ROPE, false, PERTOK>), grid, dim3(256), 0, s, a);
 }
 
 // per-token weight rows only matter with a norm
@@ -697,8 +697,8 @@ void launch_quant_d(const QuantArgs& a, dim3 grid, hipStream_t s) {
 
 template <int D, int NORM, int ROPE, bool PERTOK>
 void launch_kmean_w(const KmeanArgs& a, dim3 grid, hipStream_t s) {
-    if (a.r.rope_contig) hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, true, PERTOK>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_kmean_partial<D, NORM, ROPE, false, PERTOK>), grid, dim3(256), 0, s, a);
+    if (a.r.rope_contig) SQ_LAUNCH((k_kmean_partial<D, NORM, ROPE, true, PERTOK>), grid, dim3(256), 0, s, a);
+    else SQ_LAUNCH((k_kmean_partial<D, NORM, ROPE, false, PERTOK>), grid, dim3(256), 0, s, a);
 }
 
 template <int D, int NORM, int ROPE>
@@ -732,8 +732,8 @@ int launch_norm_stats(const NormStatsArgs& a, void* stream) {
     const int64_t tokens = a.B * a.T;
     if (tokens == 0) return SQ_OK;
     dim3 grid(static_cast<unsigned>((tokens + 3) / 4));
-    if (a.D == 128) hipLaunchKernelGGL(k_norm_stats<128>, grid, dim3(256), 0, S(stream), a);
-    else hipLaunchKernelGGL(k_norm_stats<64>, grid, dim3(256), 0, S(stream), a);
+    if (a.D == 128) SQ_LAUNCH(k_norm_stats<128>, grid, dim3(256), 0, S(stream), a);
+    else SQ_LAUNCH(k_norm_stats<64>, grid, dim3(256), 0, S(stream), a);
     return check_launch("sq_norm_stats");
 }
 
@@ -747,9 +747,9 @@ int launch_kmean(const KmeanArgs& a, void* stream) {
     }
     const int64_t nchunk = (a.nblk + 15) / 16, per = 256 / a.r.D;
     if (a.nblk > 0)
-        hipLaunchKernelGGL(k_kmean_chunks, dim3(static_cast<unsigned>((nchunk + per - 1) / per), static_cast<unsigned>(a.r.B * a.r.H)),
+        SQ_LAUNCH(k_kmean_chunks, dim3(static_cast<unsigned>((nchunk + per - 1) / per), static_cast<unsigned>(a.r.B * a.r.H)),
                            dim3(256), 0, S(stream), a);
-    hipLaunchKernelGGL(k_kmean_final, dim3(static_cast<unsigned>((a.r.B * a.r.H * a.r.D + 255) / 256)), dim3(256), 0,
+    SQ_LAUNCH(k_kmean_final, dim3(static_cast<unsigned>((a.r.B * a.r.H * a.r.D + 255) / 256)), dim3(256), 0,
                        S(stream), a);
     return check_launch("sq_kmean");
 }
@@ -766,15 +766,15 @@ int launch_quant_qk(const QuantArgs& a, void* stream) {
 int launch_quant_v_fp8(const QuantVArgs& a, void* stream) {
     if (a.B * a.H == 0) return SQ_OK;
     const int64_t n = a.B * a.H * a.D;
-    hipLaunchKernelGGL(k_fill_u32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, S(stream), a.amax, n, 0u);
+    SQ_LAUNCH(k_fill_u32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, S(stream), a.amax, n, 0u);
     if (a.T > 0) {
         dim3 g1(static_cast<unsigned>((a.T + 255) / 256), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
-        if (a.D == 128) hipLaunchKernelGGL(k_v_amax<128>, g1, dim3(256), 0, S(stream), a);
-        else hipLaunchKernelGGL(k_v_amax<64>, g1, dim3(256), 0, S(stream), a);
+        if (a.D == 128) SQ_LAUNCH(k_v_amax<128>, g1, dim3(256), 0, S(stream), a);
+        else SQ_LAUNCH(k_v_amax<64>, g1, dim3(256), 0, S(stream), a);
     }
     dim3 g2(static_cast<unsigned>((a.od + 127) / 128), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
-    if (a.D == 128) hipLaunchKernelGGL(k_v_fp8<128>, g2, dim3(256), 0, S(stream), a);
-    else hipLaunchKernelGGL(k_v_fp8<64>, g2, dim3(256), 0, S(stream), a);
+    if (a.D == 128) SQ_LAUNCH(k_v_fp8<128>, g2, dim3(256), 0, S(stream), a);
+    else SQ_LAUNCH(k_v_fp8<64>, g2, dim3(256), 0, S(stream), a);
     return check_launch("sq_quant_v_fp8");
 }
 

@@ -13,6 +13,11 @@ namespace sq {
 int fail(int status, const char* fmt, ...);
 void clear_error();
 
+// Launch tracing (SQ_TRACE in the environment, read once): one stderr line per kernel launch.
+bool trace_enabled();
+void trace_launch(const char* kernel, unsigned gx, unsigned gy, unsigned gz, unsigned block, size_t lds,
+                  const void* stream);
+
 // ---------------------------------------------------------------- row prologue
 // Split-half rotation over pairs < D/2 (channel p with p + pairs): an internal mode next to
 // sq_rope_mode's values, since its partner exchange needs LDS.

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 
 #include "sq_internal.h"
 
@@ -20,6 +21,20 @@ int fail(int status, const char* fmt, ...) {
 }
 
 void clear_error() { g_last_error[0] = 0; }
+
+bool trace_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("SQ_TRACE");
+        return v != nullptr && v[0] != 0 && !(v[0] == '0' && v[1] == 0);
+    }();
+    return on;
+}
+
+void trace_launch(const char* kernel, unsigned gx, unsigned gy, unsigned gz, unsigned block, size_t lds,
+                  const void* stream) {
+    std::fprintf(stderr, "sq_trace: %s grid=(%u,%u,%u) block=%u dyn_lds=%zu stream=%p\n", kernel, gx, gy, gz, block,
+                 lds, stream);
+}
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 

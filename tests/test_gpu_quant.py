@@ -169,3 +169,77 @@ def test_cfg4_quantizer_full_size_sampled_heads():
         np.testing.assert_array_equal(host(res.scales)[:, heads].view(np.uint32), scales.view(np.uint32))
         np.testing.assert_array_equal(host(res.codes)[:, :, heads], codes)
         print("cfg4 layout %d ok" % layout, flush=True)
+
+
+def test_results_do_not_depend_on_the_grid():
+    """The same rows launched as different grids: the whole (B, H) batch, one batch item at a time, and single heads
+    of a strided view (the grids of the norm statistics, k mean, quantizer and V quantizer all scale with B and H).
+    Every result is bit-identical: no kernel's arithmetic depends on which workgroup or XCD ran an item."""
+    B, T, H, D = 2, 333, 6, 128
+    x = _case(B, T, H, D, 777, outliers=3)
+    w_all = gen.uniform_bf16((1, H * D), gen.rng(8, 1))
+    w_head = gen.uniform_bf16((1, D), gen.rng(8, 2))
+    table = gen.rope_table(T, D // 2, start=2)
+    xd = dev_bf16(x)
+    # all-heads norm: full batch against one batch item at a time
+    na, r = _gpu_specs(O.NORM_ALL_HEADS, O.ROPE_SPLIT_HALF, w_all, table)
+    ms = sq.sq_norm_stats(xd)
+    mu = sq.sq_kmean(xd, na, r)
+    res = sq.sq_quant_qk(xd, na, r, mu, 1.0, 1e-7, O.LAYOUT_THREAD_K, 64)
+    v8, vs = sq.sq_quant_v_fp8(xd)
+    torch.cuda.synchronize()
+    for b in range(B):
+        xb = xd[b:b + 1]
+        ms_b = sq.sq_norm_stats(xb)
+        mu_b = sq.sq_kmean(xb, na, r)
+        res_b = sq.sq_quant_qk(xb, na, r, mu_b, 1.0, 1e-7, O.LAYOUT_THREAD_K, 64)
+        v8_b, vs_b = sq.sq_quant_v_fp8(xb)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(ms_b).view(np.uint32), host(ms)[b:b + 1].view(np.uint32))
+        np.testing.assert_array_equal(host(mu_b).view(np.uint32), host(mu)[b:b + 1].view(np.uint32))
+        np.testing.assert_array_equal(host(res_b.codes), host(res.codes)[b:b + 1])
+        np.testing.assert_array_equal(host(res_b.scales).view(np.uint32), host(res.scales)[b:b + 1].view(np.uint32))
+        np.testing.assert_array_equal(host(v8_b), host(v8)[b:b + 1])
+        np.testing.assert_array_equal(host(vs_b).view(np.uint32), host(vs)[b:b + 1].view(np.uint32))
+    # per-head norm: all heads against single heads of a strided view
+    nh, _ = _gpu_specs(O.NORM_HEAD, O.ROPE_SPLIT_HALF, w_head, table)
+    mu = sq.sq_kmean(xd, nh, r)
+    res = sq.sq_quant_qk(xd, nh, r, mu, 1.0, 1e-7, O.LAYOUT_THREAD_Q, 32)
+    torch.cuda.synchronize()
+    for h in (0, 3, 5):
+        xh = xd[:, :, h:h + 1]
+        mu_h = sq.sq_kmean(xh, nh, r)
+        res_h = sq.sq_quant_qk(xh, nh, r, mu_h, 1.0, 1e-7, O.LAYOUT_THREAD_Q, 32)
+        v8_h, vs_h = sq.sq_quant_v_fp8(xh)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(mu_h).view(np.uint32), host(mu)[:, h:h + 1].view(np.uint32))
+        np.testing.assert_array_equal(host(res_h.codes), host(res.codes)[:, :, h:h + 1])
+        np.testing.assert_array_equal(host(res_h.scales).view(np.uint32), host(res.scales)[:, h:h + 1].view(np.uint32))
+        np.testing.assert_array_equal(host(v8_h), host(v8)[:, h:h + 1])
+        np.testing.assert_array_equal(host(vs_h).view(np.uint32), host(vs)[:, h:h + 1].view(np.uint32))
+
+
+TRACE_SCRIPT = r"""
+import numpy as np, torch
+import quantized_transformer_attention_amd as sq
+x = torch.zeros((1, 300, 3, 128), dtype=torch.bfloat16, device="cuda:0")
+res = sq.sq_quant_qk(x, layout=sq.LAYOUT_PER_BLOCK, block=64)
+torch.cuda.synchronize()
+print("done", flush=True)
+"""
+
+
+def test_launch_trace_names_every_launch():
+    """SQ_TRACE=1 logs each launch (kernel, grid, block) to stderr: the quantizer of 300 tokens x 3 heads is
+    ceil(300 / 128) x 3 = 9 items on a grid rounded up to a multiple of the 8 XCDs."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ, SQ_TRACE="1")
+    r = subprocess.run([sys.executable, "-c", TRACE_SCRIPT], capture_output=True, text=True, env=env, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    print(r.stderr[-2000:])
+    assert r.returncode == 0 and "done" in r.stdout
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("sq_trace: ")]
+    assert len(lines) == 1, lines
+    assert "k_quant_qk" in lines[0] and "grid=(16,1,1)" in lines[0] and "block=256" in lines[0]
