@@ -244,7 +244,10 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
  * over kv_tile keys with Pt = bf16(p) and Vt = bf16(vc * vs16). The pass is merged
  * into (out, lse), which hold the projected pass on entry (lse base 2): top =
  * max(a, b), wa = 2^(a - top), wb = 2^(b - top), out = out wa/(wa+wb) +
- * prefix wb/(wa+wb), lse = top + log2(wa + wb). Both -inf: out 0, lse -inf. */
+ * prefix wb/(wa+wb), lse = top + log2(wa + wb). Both -inf: out 0, lse -inf.
+ * Workspace: sq_attn_prefix_lse_merge_workspace_bytes (the prefix's key tiles laid out
+ * once per call for the pass: f16 key codes, FP32 key scales, Vt; about 4 D + 16 bytes per
+ * prefix key and kv head, for either kv_tile). */
 size_t sq_attn_prefix_lse_merge_workspace_bytes(const sq_qk* q, const sq_q8prefix* prefix);
 int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const float* k_mean, int64_t mb, int64_t mh,
                              float score_scale, int kv_tile, float* out, int64_t ob, int64_t ot, int64_t oh,

@@ -280,17 +280,26 @@ int sq_attn(const sq_qk* q, const sq_qk* k, const sq_values* v, float score_scal
 // ---------------------------------------------------------------------------- C. q8 prefix pass + merge
 extern "C" {
 
+namespace {
+// The prefix pass's tile images for one kv_tile: every (prefix batch, kv head) slice in whole tiles.
+size_t prefix_ws_bytes(const sq_q8prefix& p, int kv_tile) {
+    const int64_t ntiles = (p.P + kv_tile - 1) / kv_tile;
+    return static_cast<size_t>(p.B) * static_cast<size_t>(p.Hk) * static_cast<size_t>(ntiles) *
+           prefix_image_bytes(p.D, kv_tile);
+}
+}  // namespace
+
 size_t sq_attn_prefix_lse_merge_workspace_bytes(const sq_qk* q, const sq_q8prefix* prefix) {
-    (void)q;
-    (void)prefix;
-    return 0;
+    if (!q || !prefix || prefix->B < 1 || prefix->P < 1 || prefix->Hk < 1 || (prefix->D != 64 && prefix->D != 128))
+        return 0;
+    if (q->B * q->S * q->H == 0) return 0;
+    const size_t a = prefix_ws_bytes(*prefix, 64), b = prefix_ws_bytes(*prefix, 128);
+    return round_up(a > b ? a : b);
 }
 
 int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const float* k_mean, int64_t mb, int64_t mh,
                              float score_scale, int kv_tile, float* out, int64_t ob, int64_t ot, int64_t oh,
                              float* lse, int64_t lb, int64_t lh, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     clear_error();
     const char* what = "sq_attn_prefix_lse_merge";
     int st = check_qk(q, what);
@@ -331,7 +340,18 @@ int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const fl
             2 * (rows * p.vst + groups) >= lim)
             return fail(SQ_ERR_UNSUPPORTED, "%s: one prefix slice spans 2 GiB or more", what);
     }
+    {
+        // the tile images of one (prefix batch, kv head) are addressed with 32-bit offsets
+        const int64_t ntiles = (p.P + kv_tile - 1) / kv_tile;
+        if (ntiles * static_cast<int64_t>(prefix_image_bytes(p.D, kv_tile)) >= (int64_t(1) << 31))
+            return fail(SQ_ERR_UNSUPPORTED, "%s: %lld prefix keys (the tile images of one head span 2 GiB)", what,
+                        (long long)p.P);
+        st = check_ws(ws, ws_bytes, prefix_ws_bytes(p, kv_tile), what);
+        if (st) return st;
+    }
     PrefixArgs a{};
+    a.img = static_cast<uint8_t*>(ws);
+    a.ntiles = (p.P + kv_tile - 1) / kv_tile;
     a.q = q->codes; a.B = q->B; a.Sq = q->S; a.H = q->H; a.D = q->D;
     a.qsb = q->sb; a.qst = q->st; a.qsh = q->sh;
     a.qs = q->scales; a.qssb = q->ssb; a.qssh = q->ssh; a.q_layout = q->layout; a.q_block = q->block;

@@ -59,19 +59,6 @@ struct Cfg {
     static constexpr int NG = FP8 ? 4 * NCH : 4 * NB;
 };
 
-// Key (within the tile) held in K's LDS row rho. Row rho = 32 b + r of 32-key block b with r =
-// 8 j + 4 h + i is output register 4 j + i of the lanes of half h for block b; the keys are chosen
-// so that lane half h holds, in register order, the consecutive keys its P^T operand needs:
-//   FP8 (64 keys per product): block b = 2 s + t gives keys 64 s + 32 h + 16 t + 4 j + i;
-//   bf16 (16 keys per product): block b gives keys 32 b + 16 (j >> 1) + 8 h + 4 (j & 1) + i.
-// Either way 8 consecutive registers (fixed b and j >> 1) hold 8 consecutive keys from a multiple of 8.
-template <bool FP8>
-__host__ __device__ constexpr int kappa_of_row(int rho) {
-    const int b = rho >> 5, r = rho & 31, j = r >> 3, h = (r >> 2) & 1, i = r & 3;
-    return FP8 ? 64 * (b >> 1) + 32 * h + 16 * (b & 1) + 4 * j + i
-               : 32 * b + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
-}
-
 // The k-scale group of output register 4 j + i (any block): THREAD_K group (key mod 8) / 2.
 __host__ __device__ constexpr int kgroup(int j, int i) { return 2 * (j & 1) + (i >> 1); }
 
@@ -169,11 +156,13 @@ struct WaveState {
 };
 
 // One key tile: S^T = K Q^T on INT8 MFMA, online softmax in base 2, O^T += V^T P^T.
-// tail (wave-uniform): keys are masked per query, key kappa of query ql (lane % 32) kept iff kappa <
-// min(Sk, qend0 + ql) - kbase with qend0 the key end of the wave's first query (Sk when not causal).
-// Only the masking and the exponentials branch on it: the products and the accumulator take one path.
-template <bool FP8, int NB>
-__device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, float mn, bool tail, float& lsum,
+// TAIL: keys are masked per query, key kappa of query ql (lane % 32) kept iff kappa < min(Sk, qend0 +
+// ql) - kbase with qend0 the key end of the wave's first query (Sk when not causal). It is a template
+// argument: the key loop runs the tiles that need no mask and those that do in loops of their own,
+// so the unmasked tiles carry no masking code (a run-time flag gets if-converted into per-key selects
+// on every tile).
+template <bool FP8, int NB, bool TAIL>
+__device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, float mn, float& lsum,
                                          v8i* pf8, v8bf* pbf) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -185,7 +174,7 @@ __device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, f
                 const int gi = FP8 ? 4 * (b >> 1) + kgroup(j, i) : 4 * b + kgroup(j, i);
                 const int av = s[b][4 * j + i];
                 float x = __builtin_fmaf(static_cast<float>(av), cg[gi], -mn);
-                if (tail && av == INT32_MIN) x = -__builtin_inff();   // a masked key: p = 0 exactly
+                if (TAIL && av == INT32_MIN) x = -__builtin_inff();   // a masked key: p = 0 exactly
                 const float pv = __builtin_amdgcn_exp2f(x);
                 p[i] = pv;
                 lsum += pv;
@@ -201,10 +190,10 @@ __device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, f
         }
 }
 
-template <int D, int KT, bool FP8>
+template <int D, int KT, bool FP8, bool TAIL>
 __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
                                           const uint8_t* v_lds, int kbase, const KScales<D, KT, FP8>& ks, int ql,
-                                          int h, int qend0, int layout, bool tail) {
+                                          int h, int qend0, int layout) {
     using C = Cfg<D, KT, FP8>;
     // c = RN(qs ks) per score group (times score_scale: exact for 1)
     float cg[C::NG];
@@ -228,7 +217,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
             s[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, st.qop[c], c == 0 ? v16i{} : s[b], 0, 0, 0);
         }
     }
-    if (tail) {
+    if constexpr (TAIL) {
         // keys this lane's query sees: local key < nval (a lane of half h holds the half-0 keys plus 32 h
         // (FP8 permutation) or 8 h (bf16)); opaque so that it is not computed once before the key loop
         int nval = min(static_cast<int>(a.Sk), qend0 + ql) - kbase - (FP8 ? 32 : 8) * h;
@@ -265,8 +254,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
     float lsum = 0.0f;
     v8i pf8[C::NCH];
     v8bf pbf[KT / 16];
-    if (tail) exp_pack<FP8, C::NB>(s, cg, mn, true, lsum, pf8, pbf);
-    else exp_pack<FP8, C::NB>(s, cg, mn, false, lsum, pf8, pbf);
+    exp_pack<FP8, C::NB, TAIL>(s, cg, mn, lsum, pf8, pbf);
     st.l_run = st.l_run * alpha + lsum;
 
     // Rescale the accumulator of this lane's query by alpha, unless no query of the wave moved its max
@@ -368,18 +356,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     // the key scales of tile j + 1 are fetched (before its K/V copy) while tile j is
     // processed, so no wait on them ever waits for a copy in flight
     auto kscales = [&](int j) { return load_kscales<D, KT, FP8>(ksr, j * KT, h, kl_layout, kl_shift); };
-    auto step = [&](int j, const uint8_t* buf, const KScales<D, KT, FP8>& ks) {
-        const int kbase = j * KT;
-        if (kbase >= hi_end) return;  // no query of the wave sees the tile: its state is unchanged
-        tile_step<D, KT, FP8>(a, st, buf, buf + C::KBYTES, kbase, ks, ql, h, qend0, kl_layout, kbase + KT > lo_end);
-    };
     KScales<D, KT, FP8> ks_next = kscales(0);
     copy(0, buf0);
     wait_vm();
     __syncthreads();
     // one tile per iteration, its buffer chosen at run time (wave-uniform): a loop body unrolled
     // per buffer would hold the accumulator in two register ranges and copy it between them
-    for (int j = 0; j < ntiles; ++j) {
+    auto body = [&](int j, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
         const bool odd = (j & 1) != 0;
         uint8_t* cur = odd ? buf1 : buf0;
         uint8_t* nxt = odd ? buf0 : buf1;
@@ -388,10 +372,18 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
             ks_next = kscales(j + 1);
             copy(j + 1, nxt);
         }
-        step(j, cur, ks_cur);
+        // a tile past the wave's last query's key end leaves its state unchanged
+        const int kbase = j * KT;
+        if (!TAIL || kbase < hi_end)
+            tile_step<D, KT, FP8, TAIL>(a, st, cur, cur + C::KBYTES, kbase, ks_cur, ql, h, qend0, kl_layout);
         wait_vm();
         __syncthreads();
-    }
+    };
+    // tiles [0, jm) end at or below the wave's first query's key end and need no mask; every wave
+    // runs ntiles iterations (one barrier each) over the two loops
+    const int jm = min(ntiles, lo_end / KT);
+    for (int j = 0; j < jm; ++j) body(j, std::integral_constant<bool, false>{});
+    for (int j = jm; j < ntiles; ++j) body(j, std::integral_constant<bool, true>{});
 
     // epilogue: l over the two lane halves, lse, out = acc / l (x vs / 256)
     float lt = st.l_run;

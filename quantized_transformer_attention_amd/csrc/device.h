@@ -171,6 +171,20 @@ __device__ __forceinline__ v8h_t i8x8_to_f16(uint32_t w0, uint32_t w1) {
     return __builtin_bit_cast(v8h_t, r);
 }
 
+// Key (within a key tile of the 32x32 attention kernels) held in K's LDS row rho. Row rho = 32 b + r
+// of 32-key block b with r = 8 j + 4 h + i is output register 4 j + i of the lanes of half h for
+// block b (v_mfma_*_32x32 output layout); the keys are chosen
+// so that lane half h holds, in register order, the consecutive keys its P^T operand needs:
+//   FP8 (64 keys per product): block b = 2 s + t gives keys 64 s + 32 h + 16 t + 4 j + i;
+//   bf16 (16 keys per product): block b gives keys 32 b + 16 (j >> 1) + 8 h + 4 (j & 1) + i.
+// Either way 8 consecutive registers (fixed b and j >> 1) hold 8 consecutive keys from a multiple of 8.
+template <bool FP8>
+__host__ __device__ constexpr int kappa_of_row(int rho) {
+    const int b = rho >> 5, r = rho & 31, j = r >> 3, h = (r >> 2) & 1, i = r & 3;
+    return FP8 ? 64 * (b >> 1) + 32 * h + 16 * (b & 1) + 4 * j + i
+               : 32 * b + 16 * (j >> 1) + 8 * h + 4 * (j & 1) + i;
+}
+
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
 

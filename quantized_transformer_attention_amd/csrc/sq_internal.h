@@ -139,7 +139,15 @@ struct PrefixArgs {
     int64_t ob, ot, oh;
     float* lse;
     int64_t lb, lh;
+    uint8_t* img;               // workspace: the prefix's key tiles as LDS images (k_prefix_stage)
+    int64_t ntiles;             // key tiles per (prefix batch, kv head): ceil(P / kv_tile)
 };
+
+// Bytes of one key tile's image in the prefix pass's workspace (head dim D, kv_tile 64 or 128): the
+// tile's f16 K rows, its bf16 V^T rows and its keys' FP32 group scales (padded to 1 KB).
+constexpr size_t prefix_image_bytes(int64_t D, int kv_tile) {
+    return static_cast<size_t>(kv_tile * 2 * D + D * 2 * kv_tile + (D / 32 * kv_tile * 4 + 1023) / 1024 * 1024);
+}
 
 // Positions per split-KV segment of the paged decode (one workgroup each).
 constexpr int kDecodeSeg = 256;
