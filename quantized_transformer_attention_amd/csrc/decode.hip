@@ -13,8 +13,9 @@
 // one (sequence, kv head) and serves all Hq / Hk query heads from a single read of
 // the segment's K and V; each wave takes 64 positions (4 pages). Both contractions run
 // on the f16 matrix cores (f32 accumulation), the query heads padded to 16 rows:
-//  * Q.K: K codes are loaded straight into the B operand layout (8 channels of one
-//    position per lane) and widened exactly to f16 (byte permute + packed f16 subtract);
+//  * Q.K: K rows are read whole (16 bytes a lane), put through the wave's LDS rows into the B
+//    operand layout (8 channels of one position per lane) and widened exactly to f16 (byte
+//    permute + packed f16 subtract);
 //    q (bf16 or f16) is f16 after an exact power-of-two
 //    rescale per head (the head's largest |q| lands in [2^14, 2^15), so no bf16 value
 //    overflows); one MFMA per 32-channel q8 group, whose dot then meets its FP16 key scale
@@ -115,23 +116,27 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) qraw[g] = *reinterpret_cast<const uint4*>(qp + 32 * g + 8 * j);
     }
-    // K of page t: lane (j, lc) takes position 16 t + lc, channels 32 g + 8 j .. + 7 of each group g
-    uint2 kr[4][NG];
+    // K and V rows, whole rows per load (16 bytes a lane, NV lanes a row: a load touches only full
+    // rows, which sustains a higher read rate than the 32-byte pieces of the MFMA operand layout):
+    // load r holds rows RPL r .. RPL r + RPL - 1 (lane l: row RPL r + l / NV, bytes 16 (l % NV)). K goes
+    // through the wave's LDS rows into the operand layout; V follows it there once the scores are done.
+    // The key scales of position 16 t + lc go to lane (j, lc); the value scales of row l to lane l.
+    uint4 kraw[NV], vraw[NV];
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+        const int row = RPL * r + l / NV;           // wave-local row: page row / 16, slot row % 16
+        const int64_t rb = rowbase[row >> 4] >= 0 ? rowbase[row >> 4] : hk;
+        kraw[r] = *reinterpret_cast<const uint4*>(a.kc + (rb + static_cast<int64_t>(row & 15) * a.Hk) * D + 16 * (l % NV));
+    }
     uint2 ksr[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int64_t row = (rowbase[t] >= 0 ? rowbase[t] : hk) + static_cast<int64_t>(lc) * a.Hk;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) kr[t][g] = *reinterpret_cast<const uint2*>(a.kc + row * D + 32 * g + 8 * j);
         ksr[t] = load_scale_row<D>(a.ks + row * NG);
     }
-
-    // V rows: load r holds rows RPL r .. RPL r + RPL - 1 (lane l: row RPL r + l / NV, bytes 16 (l % NV));
-    // V scales: lane l takes row l's NG FP16. Both go to LDS once the scores are done.
-    uint4 vraw[NV];
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
-        const int row = RPL * r + l / NV;           // wave-local row: page row / 16, slot row % 16
+        const int row = RPL * r + l / NV;
         const int64_t rb = rowbase[row >> 4] >= 0 ? rowbase[row >> 4] : hk;
         vraw[r] = *reinterpret_cast<const uint4*>(a.vc + (rb + static_cast<int64_t>(row & 15) * a.Hk) * D + 16 * (l % NV));
     }
@@ -165,6 +170,14 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
                 qa[g][k] = lc < G ? static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[g][k], sh)) : static_cast<_Float16>(0.0f);
     }
 
+    // ---- K rows to this wave's LDS rows: 16-byte chunk c of row rho at slot c ^ (rho mod NV), so that the
+    // operand reads below (16 rows, one chunk each) spread over the banks
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+        const int row = RPL * r + l / NV;
+        *reinterpret_cast<uint4*>(vst[w] + row * D + 16 * ((l % NV) ^ (row & (NV - 1)))) = kraw[r];
+    }
+
     // ---- pass 1: scores of the wave's 64 positions. Lane (j, lc) produces heads 4 j + i; their
     // score scale softmax_scale * log2 e * 2^-sh (a power-of-two change of a float: exact)
     float scl[4];
@@ -172,11 +185,16 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) scl[i] = __builtin_amdgcn_ldexpf(a.scale, -__shfl(sh, min(4 * j + i, 15), kWave));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+        // lane (j, lc): position 16 t + lc, channels 32 g + 8 j .. + 7 of each group g (chunk 2 g + j / 2)
+        const int krow = 16 * t + lc;
         v4f dg[NG];
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
-            dg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[g], i8x8_to_f16(kr[t][g].x, kr[t][g].y),
-                                                          v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        for (int g = 0; g < NG; ++g) {
+            const uint2 kv = *reinterpret_cast<const uint2*>(vst[w] + krow * D + 16 * ((2 * g + (j >> 1)) ^ (krow & (NV - 1))) +
+                                                             8 * (j & 1));
+            dg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[g], i8x8_to_f16(kv.x, kv.y), v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                          0, 0, 0);
+        }
         // lane (j, lc) now holds heads 4 j + i of position 16 t + lc
         const int pos = wp0 + 16 * t + lc;
         const bool ok = rowbase[t] >= 0 && pos < s1;
@@ -192,8 +210,8 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
             if (h < G) sc[h][w * kTpw + 16 * t + lc] = ok ? sv : -__builtin_inff();
         }
     }
-    // this wave's V rows and value scales to LDS (scales zero on rows past the end of the
-    // sequence or on an unread page)
+    // this wave's V rows (over its K rows, which the scores have been read from) and value scales to
+    // LDS (scales zero on rows past the end of the sequence or on an unread page)
 #pragma unroll
     for (int r = 0; r < NV; ++r) *reinterpret_cast<uint4*>(vst[w] + 1024 * r + 16 * l) = vraw[r];
     // value scales times 2^esh: the wave's largest |scale| lands in [2^14, 2^15), so the f16 weights
