@@ -242,7 +242,9 @@ def run_joint(args, torch, sq, gen, timer):
         "roofline": {"bound": "mfma", "kernel": "k_attn", "achieved": achieved, "peak": PEAK_TFLOPS_INT8,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS_INT8, "traffic": None,
                      "avg_launch_ms": attn_ms, "flops_per_launch": f_proj},
-        "prefix_pass": {"avg_ms": pre_ms, "tflops": f_pre / (pre_ms * 1e-3) / 1e12},
+        "prefix_pass": {"avg_ms": pre_ms, "tflops": f_pre / (pre_ms * 1e-3) / 1e12,
+                        "frac": f_pre / (pre_ms * 1e-3) / 1e12 / PEAK_TFLOPS_INT8,
+                        "traffic": traffic_for("k_prefix_joint", ["prefix.hip", "device.h", "sq_internal.h"], f_pre)},
         "stages_ms": {n: timer.avg_ms(n) for n in timer.pairs},
     }
     return res, line
