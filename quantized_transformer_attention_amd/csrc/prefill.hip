@@ -11,32 +11,36 @@
 //
 // Design (one workgroup = NW waves = 32 NW rows = 32 NW / G tokens x G heads of one kv head;
 // 64-key tiles = 4 pages; head dim D = 64 or 128):
-//  * K and V tiles are staged once per workgroup, key-major in LDS (2 D bytes per key, 16-byte
-//    slots XOR-swizzled): K as its int8 codes widened exactly to f16, with its FP16 group
-//    scales as FP32 beside them; V as an exact pair of f16 values per element, hi = f16(code
-//    vs) and lo = code vs - hi (one fused multiply-add: the remainder fits in f16), so that
-//    neither K nor V is rounded. The next tile's codes and scales are loaded into registers
-//    while the current tile is processed; the block-table entries of the tile after it are
-//    read (scalar) one step earlier still.
-//  * q (bf16 or f16) is carried as f16 after an exact power-of-two rescale per row (its largest |q| in
-//    [2^14, 2^15)), undone exactly in the row's score scale.
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_f16, one product per 32-channel q8 group (exact
-//    f16 products, FP32 sums) meeting its key scale in FP32: s = sum_g dot_g ks_g. K rows are
-//    permuted in LDS (key kappa = 16 G + 4 t + i to row 16 t + 4 G + i) so that lane group g
-//    ends up holding the 16 consecutive keys [16 g, 16 g + 16) of one query row: those
-//    registers, as f16, are the A operand of P.V, whose B operands (8 keys of one channel per
-//    lane, hi and lo) are read from the key-major V tiles by transposing ds_read_b64_tr_b16.
-//  * the softmax denominator is accumulated by the same matrix units from the same f16 P: one
-//    more P.V product against a column of ones, so out = acc / l is a weighted mean whose
-//    weights are exactly the P that multiplied the values (a one-key row returns its value).
-//  * causal: a workgroup reads the tiles up to its last row's end; a wave masks only the
-//    tiles that cross its rows' diagonal and skips those past its last row.
+//  * K and V tiles are staged once per workgroup, key-major in LDS (2 D bytes per key and
+//    array, 16-byte slots XOR-swizzled), each element as an exact pair of f16 values: hi =
+//    f16(code scale) and lo = code scale - hi (one fused multiply-add; an int8 code times an
+//    FP16 scale is a multiple of 2^-24 with at most 18 significant bits, so the remainder is
+//    an f16 number, subnormal or not). Neither K nor V is rounded. The next tile's codes and
+//    scales are loaded into registers while the current tile is processed; the block-table
+//    entries of the tile after it are read (scalar) one step earlier still.
+//  * q (bf16 or f16) is carried as f16 after an exact power-of-two rescale per row (its
+//    largest |q| in [2^14, 2^15)), undone exactly in the row's score scale.
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (hi and lo products of each 16-channel step into
+//    one FP32 accumulator): one query row per lane (lane % 32), 16 keys of each 32-key block
+//    per lane, the wave halves holding different keys. K rows are permuted in LDS (the 32x32
+//    attention core's key order) so that a lane's score registers are, in order, runs of 8
+//    consecutive keys: as f16 they are the B operand P^T of O^T = V^T P^T, whose A operand
+//    (8 keys of one channel per lane, hi and lo) is read from the key-major V tile by
+//    transposing ds_read_b64_tr_b16. A row's output channels stay in its lane.
+//  * the softmax denominator sums the same f16 P that multiplied the values (dot2 against
+//    ones, FP32), so out = acc / l is a weighted mean whose weights are exactly those P (a
+//    one-key row returns its value).
+//  * causal: a workgroup reads the tiles up to its last row's end; a wave runs the tiles
+//    below its first row's diagonal without masking code, masks those that cross its rows'
+//    diagonal and skips those past its last row.
 //  * the reference max of a row trails its running max by at most 8 (base 2): the
 //    accumulator is rescaled only when a tile raises some row's max beyond that, so p <= 2^8
 //    (the f16 P rounds relative to itself whatever the reference; l and acc are FP32).
 // HBM: each (sequence, kv head) key/value row is read by every q block of the sequence
 // that sees it; the q blocks of one kv head are dealt to one XCD in a row, so most of
 // those reads hit its L2.
+#include <type_traits>
+
 #include "device.h"
 #include "sq_internal.h"
 
@@ -45,57 +49,204 @@ namespace {
 
 constexpr int kBS = 16, kKT = 64;
 constexpr float kLag = 8.0f;                // how far a row's reference max may trail its max
-constexpr int kNQ = 2, kNT = kKT / 16;
-
-// LDS tile geometry of head dim D: per key one f16 row of D channels (NS 16-byte slots) in each of
-// K, V hi and V lo, then the keys' FP32 group scales.
-template <int D>
-struct PfTile {
-    static constexpr int kNC = D / 32, kNCT = D / 16, NS = D / 8;
-    static constexpr int kRowB = 2 * D;
-    static constexpr int kTileB = kKT * kRowB;                                  // 16 KB at D = 128
-    static constexpr int kVHi = kTileB, kVLo = 2 * kTileB, kKs = 3 * kTileB;   // K codes, V hi, V lo, K scales
-    static constexpr int kBufB = 3 * kTileB + kKT * kNC * 4;
-    static constexpr int KPW = kWave * 16 / D;                                  // keys a wave stages per pass
-};
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lv4s_p;
 
-// LDS row of key kappa in the K tile, and the 16-byte slot swizzles (NS slots per row): K is read as
-// 16 rows x one slot per lane group (row mod NS spreads the rows over the banks); V as 16 keys
-// 16 g + 8 u + 4 h + k (k, g = 0..3) x two slots, spread by k | g << 2 (D = 128) or k | (g & 1) << 2.
-__device__ __forceinline__ int k_row(int kappa) { return 16 * ((kappa >> 2) & 3) + 4 * (kappa >> 4) + (kappa & 3); }
+// LDS tile geometry of head dim D: per key one f16 row of D channels (NS 16-byte slots) in each of
+// K hi, K lo, V hi and V lo.
 template <int D>
-__device__ __forceinline__ int k_slot(int row, int slot) { return slot ^ (row & (D / 8 - 1)); }
-template <int D>
-__device__ __forceinline__ int v_slot(int key, int slot) { return slot ^ ((key & 3) | ((key >> 2) & (D / 8 - 4))); }
+struct PfTile {
+    static constexpr int NS = D / 8, NCS = D / 16, NCB = D / 32;   // slots per row, 16-channel steps, 32-channel blocks
+    static constexpr int kRowB = 2 * D;
+    static constexpr int kTileB = kKT * kRowB;                     // 16 KB at D = 128
+    static constexpr int kKLo = kTileB, kVHi = 2 * kTileB, kVLo = 3 * kTileB;
+    static constexpr int kBufB = 4 * kTileB;
+    static constexpr int KPW = kWave * 16 / D;                     // keys a wave stages per pass
+};
 
-// x s as an exact pair: hi = f16(x s), lo = x s - hi (x an integer code, s an f16 scale: the product
-// has at most 18 significant bits, so the remainder of its f16 rounding is an f16 number)
+// LDS row of key kappa in the K tile: the inverse of kappa_of_row<false> (32-key blocks; within a
+// block, row 8 j + 4 h + i holds key 16 (j >> 1) + 8 h + 4 (j & 1) + i).
+__host__ __device__ constexpr int k_row(int kappa) {
+    const int r = kappa & 31;
+    return (kappa & ~31) + 8 * (2 * ((r >> 4) & 1) + ((r >> 2) & 1)) + 4 * ((r >> 3) & 1) + (r & 3);
+}
+constexpr bool k_row_inverts() {
+    for (int rho = 0; rho < kKT; ++rho)
+        if (k_row(kappa_of_row<false>(rho)) != rho) return false;
+    return true;
+}
+static_assert(k_row_inverts(), "k_row inverts the key permutation");
+
+// V slot swizzle: the 4 keys of a transposing read (key mod 4 = 0..3) times 2 slots land on distinct
+// slots, and so do those of two such 16-lane blocks side by side.
+template <int D>
+__device__ __forceinline__ int v_slot(int key, int slot) { return slot ^ ((key & 3) * (D / 32)); }
+
+// x s as an exact pair: hi = f16(x s), lo = x s - hi (x an integer code, s an f16 scale).
 __device__ __forceinline__ void scale8_pair(v8h x, _Float16 s, v8h& hi, v8h& lo) {
     const v8h sv = {s, s, s, s, s, s, s, s};
     hi = x * sv;
     lo = __builtin_elementwise_fma(x, sv, -hi);
 }
 
+// Per-wave state of the key loop: this lane's row (query ql of the wave), its half h of the keys.
+template <int D>
+struct PfState {
+    v8h qop[PfTile<D>::NCS];     // B operand of S^T: channels 16 c + 8 h .. + 7 of the row
+    v16f o[PfTile<D>::NCB];      // O^T: channels 32 cb + 8 j + 4 h + i of the row
+    float cr, m_run, l;          // score scale (base 2), reference max, this half's denominator
+};
+
+// The instruction groups a scheduling region is laid out in (LLVM AMDGPU sched_group_barrier masks).
+constexpr int kSgMfma = 0x008, kSgValu = 0x002 | 0x400, kSgDsRead = 0x100;
+
+// One key tile: S^T = K Q^T, online softmax (base 2), O^T += V^T P^T. TAIL: the tile crosses some
+// row's diagonal (or L), and key kappa of this row is kept iff kappa < lim - kbase.
+//
+// Operands come from LDS two steps ahead of their products (rings of three stages), and the
+// exponentials of the next 16-key block are interleaved with the current block's P.V products, so
+// the matrix unit and the vector unit of a wave overlap.
+template <int D, bool TAIL>
+__device__ __forceinline__ void pf_tile(PfState<D>& st, const uint8_t* buf, int kbase, int lim, int ql, int h,
+                                        int l) {
+    using C = PfTile<D>;
+    constexpr int RING = 3;
+    // ---- S^T: step c takes channels 16 c .. 16 c + 15 of both 32-key blocks, hi and lo
+    v16f s[2];
+    v8h kop[RING][4];
+    auto kread = [&](int c, v8h* dst) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int row = 32 * b + ql;
+            const int off = row * C::kRowB + swz<C::NS>(row, 2 * c + h) * 16;
+            dst[2 * b] = *reinterpret_cast<const v8h*>(buf + off);
+            dst[2 * b + 1] = *reinterpret_cast<const v8h*>(buf + C::kKLo + off);
+        }
+    };
+    // A operand of P.V step t (key block u = t / NCB, channel block cb = t % NCB): lane l gets channel
+    // 32 cb + l % 32 of keys 16 u + 8 h .. + 7, two transposing reads of 4 keys x 16 channels per
+    // 16-lane block
+    const int blk = l >> 4, lj = l & 15;
+    auto vop_of = [&](const uint8_t* vt, int cb, int u) {
+        v4h half[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int key = 16 * u + 8 * (blk >> 1) + 4 * t + (lj >> 2);
+            const int slot = 4 * cb + 2 * (blk & 1) + ((lj & 3) >> 1);
+            const uint8_t* p = vt + key * C::kRowB + v_slot<D>(key, slot) * 16 + 8 * (lj & 1);
+            half[t] = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s_p)(p)));
+        }
+        return v8h{half[0][0], half[0][1], half[0][2], half[0][3], half[1][0], half[1][1], half[1][2], half[1][3]};
+    };
+    constexpr int PV_STEPS = 4 * C::NCB;
+    v8h vhi[RING], vlo[RING];
+    auto vread = [&](int t) {
+        vhi[t % RING] = vop_of(buf + C::kVHi, t % C::NCB, t / C::NCB);
+        vlo[t % RING] = vop_of(buf + C::kVLo, t % C::NCB, t / C::NCB);
+    };
+
+    kread(0, kop[0]);
+    kread(1, kop[1]);
+#pragma unroll
+    for (int c = 0; c < C::NCS; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 2 < C::NCS) kread(c + 2, kop[(c + 2) % RING]);
+        else if (c + 2 - C::NCS < 2) vread(c + 2 - C::NCS);     // the first P.V operands
+        const v8h* k = kop[c % RING];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[2 * b], st.qop[c], c == 0 ? v16f{} : s[b], 0, 0, 0);
+            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[2 * b + 1], st.qop[c], s[b], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (TAIL) {
+        // a lane of half h holds the half-0 keys plus 8 h; opaque so that it is not hoisted
+        int nval = lim - kbase - 8 * h;
+        asm volatile("" : "+v"(nval));
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (kappa_of_row<false>(32 * b + 8 * (r >> 2) + (r & 3)) >= nval) s[b][r] = -__builtin_inff();
+    }
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[b][r]);
+    {   // the other half's keys of the same row: lanes l and l ^ 32 swapped
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float ms = mt * st.cr;
+    // the reference max moves (and the row's accumulator with it) only when some row of the wave
+    // would see p > 2^kLag against it
+    if (__builtin_amdgcn_ballot_w64(ms > st.m_run + kLag) != 0) {
+        const float mo = st.m_run;
+        const float mn = fmaxf(mo, ms);
+        const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+        st.m_run = mn;
+#pragma unroll
+        for (int cb = 0; cb < C::NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.o[cb][e] *= alpha;
+        st.l *= alpha;
+    }
+    // every row sees key 0 in the first tile, so the reference is finite from there on and a masked
+    // score (-inf) gives p = 2^-inf = 0 exactly. P^T operand of keys 16 u .. 16 u + 15: this half's
+    // keys 16 u + 8 h + e, registers 4 (j & 1) + i of block u >> 1 with j >> 1 = u & 1.
+    const float mref = st.m_run;
+    auto p_of = [&](int u) {
+        v8h p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = s[u >> 1][4 * (2 * (u & 1) + (e >> 2)) + (e & 3)];
+            p[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(__builtin_fmaf(x, st.cr, -mref)));
+        }
+        return p;
+    };
+    const v2h one2 = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    v8h pf[4];
+    pf[0] = p_of(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cb = 0; cb < C::NCB; ++cb) {
+            const int t = C::NCB * u + cb;
+            if (t + 2 < PV_STEPS) vread(t + 2);
+            st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vhi[t % RING], pf[u], st.o[cb], 0, 0, 0);
+            st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vlo[t % RING], pf[u], st.o[cb], 0, 0, 0);
+        }
+        // the denominator (dot2 of the f16 P against ones) and the next block's P, between the products
+        if (u + 1 < 4) pf[u + 1] = p_of(u + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.l = __builtin_amdgcn_fdot2(v2h{pf[u][2 * e], pf[u][2 * e + 1]}, one2, st.l, false);
+#pragma unroll
+        for (int m = 0; m < 2 * C::NCB; ++m) {
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgValu, 3, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int G, int NW, int D>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a) {
     using C = PfTile<D>;
-    constexpr int kNC = C::kNC, kNCT = C::kNCT, kRowB = C::kRowB, kBufB = C::kBufB;
-    constexpr int kVHi = C::kVHi, kVLo = C::kVLo, kKs = C::kKs;
+    constexpr int kRowB = C::kRowB, kBufB = C::kBufB;
     constexpr int kRows = 32 * NW;                      // rows per workgroup
     constexpr int BQ = kRows / G;                       // query tokens per workgroup
-    // 16-byte K (and V) chunks per thread and tile; with more stagers than chunks the waves past
-    // the tile's keys stage nothing
-    constexpr int U = kKT / (NW * C::KPW) > 0 ? kKT / (NW * C::KPW) : 1;
-    static_assert(U * NW * C::KPW >= kKT, "every key of a tile has a stager");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufB];
-    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lq = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, ql = l & 31, h = l >> 5;
 
     // ---- work item: (kv head, q block); the q blocks of a kv head run on one XCD, last first
     const int64_t items = a.nqb * a.Hk;
@@ -121,8 +272,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
     const int kv_end = min(L, ctx + min(qlen, j0 + BQ));
     const int ntiles = (kv_end + kKT - 1) / kKT;
     if (ntiles <= 0) return;
-    // this wave's rows are tokens j0 + 32 w / G .. j0 + (32 w + 31) / G
-    const int lo_end = min(L, ctx + j0 + (32 * w) / G + 1);
+    // this wave's last row is token j0 + (32 w + 31) / G
     const int hi_end = min(L, ctx + j0 + (32 * w + 31) / G + 1);
     // the block table is read through the constant address space: its wave-uniform reads become scalar
     // loads, whose counter is not the one the code loads are waited on with
@@ -130,251 +280,125 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
     const cint32* bt = reinterpret_cast<const cint32*>(reinterpret_cast<uintptr_t>(a.bt + static_cast<int64_t>(seq) * a.bt_stride));
     const int last_page = (L - 1) / kBS;
 
-    // ---- q rows: row r = 32 w + 16 n + lq is token r / G, head r % G; per-row power-of-two rescale
-    v8h qop[kNQ][kNC];
-    float cr[kNQ], m_run[kNQ];
-    v4f o[kNQ][kNCT], ol[kNQ];   // ol: the denominators of the rows o holds (P against a column of ones)
+    // ---- this lane's row r = 32 w + ql: token r / G, head r % G; per-row power-of-two rescale
+    PfState<D> st;
+    const int r = 32 * w + ql;
+    const int jq = j0 + r / G, hq = hk * G + r % G;
+    const int lim = min(L, ctx + jq + 1);               // keys this row sees
+    {
+        const bool ok = jq < qlen && qs0 + jq >= 0 && qs0 + jq < a.T;
+        v4u raw[C::NCS];
+        const uint16_t* qp = a.q + static_cast<int64_t>(qs0 + (ok ? jq : 0)) * a.qt + static_cast<int64_t>(hq) * a.qh;
 #pragma unroll
-    for (int n = 0; n < kNQ; ++n) {
-        const int r = 32 * w + 16 * n + lq;
-        const int j = j0 + r / G, h = hk * G + r % G;
-        const bool ok = j < qlen && qs0 + j >= 0 && qs0 + j < a.T;
-        v4u raw[kNC];
-        const uint16_t* qp = a.q + static_cast<int64_t>(qs0 + (ok ? j : 0)) * a.qt + static_cast<int64_t>(h) * a.qh;
-#pragma unroll
-        for (int c = 0; c < kNC; ++c)
-            raw[c] = ok ? *reinterpret_cast<const v4u*>(qp + 32 * c + 8 * g) : v4u{0u, 0u, 0u, 0u};
-        float f[kNC][8];
+        for (int c = 0; c < C::NCS; ++c)
+            raw[c] = ok ? *reinterpret_cast<const v4u*>(qp + 16 * c + 8 * h) : v4u{0u, 0u, 0u, 0u};
+        float f[C::NCS][8];
         float mx = 0.0f;
 #pragma unroll
-        for (int c = 0; c < kNC; ++c) {
+        for (int c = 0; c < C::NCS; ++c) {
             const uint4 rc = make_uint4(raw[c][0], raw[c][1], raw[c][2], raw[c][3]);
             if (a.q_f16) unpack_f16x8(rc, f[c]);
             else unpack_bf16x8(rc, f[c]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[c][e]));
         }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
         const int sh = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
 #pragma unroll
-        for (int c = 0; c < kNC; ++c)
+        for (int c = 0; c < C::NCS; ++c)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qop[n][c][e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[c][e], sh));
-        cr[n] = __builtin_amdgcn_ldexpf(a.scale, -sh);
-        m_run[n] = a.sinks ? a.sinks[h] * 1.44269504f : -__builtin_inff();
+            for (int e = 0; e < 8; ++e) st.qop[c][e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[c][e], sh));
+        st.cr = __builtin_amdgcn_ldexpf(a.scale, -sh);
+        st.m_run = a.sinks ? a.sinks[hq] * 1.44269504f : -__builtin_inff();
+        // a sink is one more term 2^(sink - m) = 1 of the row's denominator, counted in half 0
+        st.l = (a.sinks && h == 0) ? 1.0f : 0.0f;
 #pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) o[n][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        // a sink is one more term 2^(sink - m) = 1 of every row's denominator (its head is a.sinks' index of
-        // row 4 g + i, whose sink starts its running max)
-        const float l0 = a.sinks ? 1.0f : 0.0f;
-        ol[n] = v4f{l0, l0, l0, l0};
+        for (int cb = 0; cb < C::NCB; ++cb) st.o[cb] = v16f{};
     }
 
-    // ---- staging: thread tid takes 16 channels (part) of keys kappa_u = tid / (D / 16) + NW KPW u of a
-    // tile; the pages of those keys are wave-uniform: tile page (KPW w + NW KPW u) / 16
+    // ---- staging: thread tid takes 16 channels (part) of key kappa = tid / (D / 16) of a tile (K and V);
+    // a wave's keys lie in one page, tile page KPW w / 16
     constexpr int PARTS = D / 16;
-    const int part = tid % PARTS, key0 = tid / PARTS;
+    static_assert(NW * C::KPW >= kKT, "one pass stages a tile");
+    const int part = tid % PARTS, kappa = tid / PARTS;
     const bool stager = C::KPW * w < kKT;               // wave-uniform
     const int64_t rowstride = a.Hk;                     // cache rows per slot
-    auto page_block = [&](int tile, int u) {
-        const int tp = stager ? (C::KPW * w + NW * C::KPW * u) / kBS : 0;
+    auto page_block = [&](int tile) {
+        const int tp = stager ? (C::KPW * w) / kBS : 0;
         const int page = __builtin_amdgcn_readfirstlane(min(tile * (kKT / kBS) + tp, last_page));
         const int b = bt[page];
         return (b >= 0 && b < a.num_blocks) ? b : 0;    // a bad entry reads block 0 (no fault)
     };
-    v4u kraw[U], vraw[U];
-    uint32_t ksr[U], vsr[U];
-    auto load_tile = [&](const int* blk) {
+    v4u kraw, vraw;
+    uint32_t ksr, vsr;
+    auto load_tile = [&](int blk) {
         if (!stager) return;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = (static_cast<int64_t>(blk[u]) * kBS + ((key0 + NW * C::KPW * u) & 15)) * rowstride + hk;
-            kraw[u] = *reinterpret_cast<const v4u*>(a.kc + row * D + 16 * part);
-            vraw[u] = *reinterpret_cast<const v4u*>(a.vc + row * D + 16 * part);
-            ksr[u] = a.ks[row * kNC + (part >> 1)];
-            vsr[u] = a.vs[row * kNC + (part >> 1)];
-        }
+        const int64_t row = (static_cast<int64_t>(blk) * kBS + (kappa & 15)) * rowstride + hk;
+        kraw = *reinterpret_cast<const v4u*>(a.kc + row * D + 16 * part);
+        vraw = *reinterpret_cast<const v4u*>(a.vc + row * D + 16 * part);
+        ksr = a.ks[row * C::NCB + (part >> 1)];
+        vsr = a.vs[row * C::NCB + (part >> 1)];
     };
     // keys at or past L (unused slots, clamped pages) get zero scales: their scores are masked and their
     // values must not carry a NaN or inf of memory nobody wrote into the P.V sums
     auto store_tile = [&](uint8_t* buf, int kbase) {
         if (!stager) return;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kappa = key0 + NW * C::KPW * u;
-            const bool live = kbase + kappa < L;
-            const float ks = live ? f16_to_f32(static_cast<uint16_t>(ksr[u])) : 0.0f;
-            const _Float16 vs = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsr[u])) : static_cast<_Float16>(0.0f);
-            const v4u kr4 = kraw[u], vr4 = vraw[u];
-            const v8h k0 = i8x8_to_f16(kr4[0], kr4[1]), k1 = i8x8_to_f16(kr4[2], kr4[3]);
-            v8h vh0, vl0, vh1, vl1;
-            scale8_pair(i8x8_to_f16(vr4[0], vr4[1]), vs, vh0, vl0);
-            scale8_pair(i8x8_to_f16(vr4[2], vr4[3]), vs, vh1, vl1);
-            const int kr = k_row(kappa);
-            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot<D>(kr, 2 * part) * 16) = k0;
-            *reinterpret_cast<v8h*>(buf + kr * kRowB + k_slot<D>(kr, 2 * part + 1) * 16) = k1;
-            // the scale of group part / 2 of key kappa (both threads of the group hold it; the even one stores)
-            if ((part & 1) == 0) reinterpret_cast<float*>(buf + kKs)[kappa * kNC + (part >> 1)] = ks;
-            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot<D>(kappa, 2 * part) * 16) = vh0;
-            *reinterpret_cast<v8h*>(buf + kVHi + kappa * kRowB + v_slot<D>(kappa, 2 * part + 1) * 16) = vh1;
-            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot<D>(kappa, 2 * part) * 16) = vl0;
-            *reinterpret_cast<v8h*>(buf + kVLo + kappa * kRowB + v_slot<D>(kappa, 2 * part + 1) * 16) = vl1;
-        }
-    };
-
-    // one tile: S^T = K Q^T, online softmax (base 2), acc += P V
-    auto tile_step = [&](const uint8_t* buf, int kbase, bool masked) {
-        v8h pf[kNQ][2];
-        int lane = l;
-#pragma unroll
-        for (int n = 0; n < kNQ; ++n) {
-            // fresh lane offsets per n: the first tile's K reads are not kept in registers for the second
-            asm volatile("" : "+v"(lane));
-            const int klq = lane & 15, kg = lane >> 4;
-            const float* ksc = reinterpret_cast<const float*>(buf + kKs);   // [key][kNC] group scales
-            v4f s[kNT];
-#pragma unroll
-            for (int t = 0; t < kNT; ++t) {
-                const int row = 16 * t + klq;
-                v4f dg[kNC];
-#pragma unroll
-                for (int c = 0; c < kNC; ++c) {
-                    const v8h kop = *reinterpret_cast<const v8h*>(buf + row * kRowB + k_slot<D>(row, 4 * c + kg) * 16);
-                    dg[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[n][c], v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                }
-                // element i is key 16 kg + 4 t + i: its group dots meet its group scales in FP32
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float* kq = ksc + (16 * kg + 4 * t + i) * kNC;
-                    float kv[kNC];
-                    if constexpr (kNC == 4) {
-                        const float4 k4 = *reinterpret_cast<const float4*>(kq);
-                        kv[0] = k4.x; kv[1] = k4.y; kv[kNC - 2] = k4.z; kv[kNC - 1] = k4.w;
-                    } else {
-                        const float2 k2 = *reinterpret_cast<const float2*>(kq);
-                        kv[0] = k2.x; kv[1] = k2.y;
-                    }
-                    float sv = dg[0][i] * kv[0];
-#pragma unroll
-                    for (int c = 1; c < kNC; ++c) sv = __builtin_fmaf(dg[c][i], kv[c], sv);
-                    s[t][i] = sv;
-                }
-            }
-            if (masked) {
-                // keys of this lane group (16 g + 4 t + i) this row sees: below min(L, ctx + j + 1)
-                const int r = 32 * w + 16 * n + lq;
-                int nval = min(L, ctx + j0 + r / G + 1) - kbase - 16 * g;
-                asm volatile("" : "+v"(nval));
-#pragma unroll
-                for (int t = 0; t < kNT; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (4 * t + i >= nval) s[t][i] = -__builtin_inff();
-            }
-            float mt = -__builtin_inff();
-#pragma unroll
-            for (int t = 0; t < kNT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[t][i]);
-            mt = fmaxf(mt, shfl_xor(mt, 16));
-            mt = fmaxf(mt, shfl_xor(mt, 32));
-            const float ms = mt * cr[n];
-            // the reference max moves (and the accumulator rows with it) only when some row of the
-            // wave would see p > 2^kLag against it
-            if (__builtin_amdgcn_ballot_w64(ms > m_run[n] + kLag) != 0) {
-                const float mo = m_run[n];
-                const float mn = fmaxf(mo, ms);
-                const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
-                m_run[n] = mn;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * g + i, kWave);
-#pragma unroll
-                    for (int ct = 0; ct < kNCT; ++ct) o[n][ct][i] *= ai;
-                    ol[n][i] *= ai;
-                }
-            }
-            // every row sees key 0 in the first tile, so mref is finite from there on and a masked
-            // score (-inf) gives p = 2^-inf = 0 exactly
-            const float mref = m_run[n];
-#pragma unroll
-            for (int t = 0; t < kNT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], cr[n], -mref));
-                    pf[n][t >> 1][4 * (t & 1) + i] = static_cast<_Float16>(p);
-                }
-        }
-        // acc += P V: B operand = keys 16 g + 8 u + 4 h + k (k = lq / 4) of channels 16 ct + 4 (lq % 4) ..
-        // + 3, transposed so that lane lq receives channel 16 ct + lq of those 4 keys
-        auto vop_of = [&](const uint8_t* vt, int ct, int u) {
-            v4h half[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int key = 16 * g + 8 * u + 4 * h + (lq >> 2), m = lq & 3;
-                const uint8_t* p = vt + key * kRowB + v_slot<D>(key, 2 * ct + (m >> 1)) * 16 + 8 * (m & 1);
-                half[h] = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lv4s_p)(p)));
-            }
-            return v8h{half[0][0], half[0][1], half[0][2], half[0][3], half[1][0], half[1][1], half[1][2], half[1][3]};
-        };
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const v8h vhi = vop_of(buf + kVHi, ct, u), vlo = vop_of(buf + kVLo, ct, u);
-#pragma unroll
-                for (int n = 0; n < kNQ; ++n) {
-                    o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], vhi, o[n][ct], 0, 0, 0);
-                    o[n][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], vlo, o[n][ct], 0, 0, 0);
-                }
-            }
-        const _Float16 one = static_cast<_Float16>(1.0f);
-        const v8h ones = {one, one, one, one, one, one, one, one};
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int n = 0; n < kNQ; ++n) ol[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf[n][u], ones, ol[n], 0, 0, 0);
+        const bool live = kbase + kappa < L;
+        const _Float16 zero = static_cast<_Float16>(0.0f);
+        const _Float16 ks = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(ksr)) : zero;
+        const _Float16 vs = live ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsr)) : zero;
+        v8h kh0, kl0, kh1, kl1, vh0, vl0, vh1, vl1;
+        scale8_pair(i8x8_to_f16(kraw[0], kraw[1]), ks, kh0, kl0);
+        scale8_pair(i8x8_to_f16(kraw[2], kraw[3]), ks, kh1, kl1);
+        scale8_pair(i8x8_to_f16(vraw[0], vraw[1]), vs, vh0, vl0);
+        scale8_pair(i8x8_to_f16(vraw[2], vraw[3]), vs, vh1, vl1);
+        const int kr = k_row(kappa);
+        const int k0 = kr * kRowB + swz<C::NS>(kr, 2 * part) * 16, k1 = kr * kRowB + swz<C::NS>(kr, 2 * part + 1) * 16;
+        *reinterpret_cast<v8h*>(buf + k0) = kh0;
+        *reinterpret_cast<v8h*>(buf + k1) = kh1;
+        *reinterpret_cast<v8h*>(buf + C::kKLo + k0) = kl0;
+        *reinterpret_cast<v8h*>(buf + C::kKLo + k1) = kl1;
+        const int v0 = kappa * kRowB + v_slot<D>(kappa, 2 * part) * 16, v1 = kappa * kRowB + v_slot<D>(kappa, 2 * part + 1) * 16;
+        *reinterpret_cast<v8h*>(buf + C::kVHi + v0) = vh0;
+        *reinterpret_cast<v8h*>(buf + C::kVHi + v1) = vh1;
+        *reinterpret_cast<v8h*>(buf + C::kVLo + v0) = vl0;
+        *reinterpret_cast<v8h*>(buf + C::kVLo + v1) = vl1;
     };
 
     // ---- key loop: tile j is processed from buffer j % 2 while tile j + 1's codes are in flight;
     // the table entries of tile j + 2 are read meanwhile
-    int nb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) nb[u] = page_block(0, u);
+    int nb = page_block(0);
     load_tile(nb);
-#pragma unroll
-    for (int u = 0; u < U; ++u) nb[u] = page_block(min(1, ntiles - 1), u);
+    nb = page_block(min(1, ntiles - 1));
     store_tile(lds, 0);
     __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
+    // tiles every row of the workgroup sees whole run without masking code; from the first row's
+    // diagonal on, a wave masks the tiles it sees and skips those past its last row
+    const int j_whole = min(ntiles, min(L, ctx + j0 + 1) / kKT);
+    auto step = [&](int j, auto tail) {
         uint8_t* cur = lds + (j & 1) * kBufB;
         uint8_t* nxt = lds + ((j + 1) & 1) * kBufB;
         load_tile(nb);                                  // tile j + 1 (the last tile again past the end)
-        const int t2 = min(j + 2, ntiles - 1);
-#pragma unroll
-        for (int u = 0; u < U; ++u) nb[u] = page_block(t2, u);
+        nb = page_block(min(j + 2, ntiles - 1));
         __builtin_amdgcn_sched_barrier(0);              // the loads go out before the tile's arithmetic
         const int kbase = j * kKT;
-        if (kbase < hi_end) tile_step(cur, kbase, kbase + kKT > lo_end);
+        if (!decltype(tail)::value || kbase < hi_end) pf_tile<D, decltype(tail)::value>(st, cur, kbase, lim, ql, h, l);
         store_tile(nxt, (j + 1) * kKT);
         __syncthreads();
-    }
+    };
+    for (int j = 0; j < j_whole; ++j) step(j, std::false_type{});
+    for (int j = j_whole; j < ntiles; ++j) step(j, std::true_type{});
 
-    // ---- epilogue: out = acc / l (l of row 4 g + i is in every lane of group g)
+    // ---- epilogue: out = acc / l, the denominator summed over both halves
+    const float lt = st.l + shfl_xor(st.l, 32);
+    if (jq >= qlen || qs0 + jq < 0 || qs0 + jq >= a.T) return;
+    const float inv = 1.0f / lt;
+    const int64_t orow = static_cast<int64_t>(qs0 + jq) * a.ot + static_cast<int64_t>(hq) * a.oh;
 #pragma unroll
-    for (int n = 0; n < kNQ; ++n) {
+    for (int cb = 0; cb < C::NCB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float inv = 1.0f / ol[n][i];
-            const int r = 32 * w + 16 * n + 4 * g + i;
-            const int j = j0 + r / G;
-            if (j >= qlen || qs0 + j < 0 || qs0 + j >= a.T) continue;
-            const int64_t orow = static_cast<int64_t>(qs0 + j) * a.ot + static_cast<int64_t>(hk * G + r % G) * a.oh;
-#pragma unroll
-            for (int ct = 0; ct < kNCT; ++ct) store_out(a.out, orow + 16 * ct + lq, o[n][ct][i] * inv, a.out_bf16 != 0);
-        }
-    }
+        for (int e = 0; e < 16; ++e)
+            store_out(a.out, orow + 32 * cb + 8 * (e >> 2) + 4 * h + (e & 3), st.o[cb][e] * inv, a.out_bf16 != 0);
 }
 
 }  // namespace
