@@ -118,9 +118,9 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buf
 }
 
 // The key scales a lane needs for one tile, raw (FP32): THREAD_K the 4 scales of each 64-key
-// chunk (key t in group (t >> 1) & 3); PER_BLOCK the scale of each 32-key block b at [b >> 1][b & 1]
-// (its keys never straddle a scale block for this lane half). Past the last scale the buffer
-// load gives 0.
+// chunk (key t in group (t >> 1) & 3); PER_BLOCK with FP8 the scale of each 64-key chunk's lane-half
+// run in all four entries, with bf16 the scale of each 32-key block b at [b >> 1][b & 1] (its keys
+// never straddle a scale block for this lane half). Past the last scale the buffer load gives 0.
 template <int D, int KT, bool FP8>
 struct KScales {
     v4f c[Cfg<D, KT, FP8>::NCH];
@@ -135,11 +135,20 @@ __device__ __forceinline__ KScales<D, KT, FP8> load_kscales(__amdgpu_buffer_rsrc
 #pragma unroll
         for (int ch = 0; ch < C::NCH; ++ch)
             k.c[ch] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * ((kbase >> 6) + ch), 0, 0));
+    } else if constexpr (FP8) {
+        // chunk ch: this lane half's 32 keys from kbase + 64 ch + 32 h lie in one scale block, whose
+        // scale stands for all four key groups (so that the products read group q's entry either way)
+#pragma unroll
+        for (int ch = 0; ch < C::NCH; ++ch) {
+            const int kmin = kbase + 64 * ch + 32 * h;
+            const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (kmin >> shift), 0, 0));
+            k.c[ch] = v4f{v, v, v, v};
+        }
     } else {
 #pragma unroll
         for (int b = 0; b < C::NB; ++b) {
             // the lowest key of this lane half in block b: its 32-key run lies in one scale block
-            const int kmin = kbase + (FP8 ? 64 * (b >> 1) + 32 * h + 16 * (b & 1) : 32 * b + 8 * h);
+            const int kmin = kbase + 32 * b + 8 * h;
             k.c[b >> 1][b & 1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (kmin >> shift), 0, 0));
         }
     }
@@ -202,8 +211,12 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
         const int q = gi & 3, blk = gi >> 2;                  // FP8: blk = 64-key chunk; bf16: 32-key block
         const int ch = FP8 ? blk : blk >> 1;
         const float tk = ks.c[ch][q];
-        const float pb = FP8 ? ks.c[ch][0] : ks.c[ch][blk & 1];
-        cg[gi] = (st.qsc * (layout == SQ_LAYOUT_THREAD_K ? tk : pb)) * a.score_scale;
+        if constexpr (FP8) {
+            cg[gi] = (st.qsc * tk) * a.score_scale;   // either layout: the loader put group q's scale at q
+        } else {
+            const float pb = ks.c[ch][blk & 1];
+            cg[gi] = (st.qsc * (layout == SQ_LAYOUT_THREAD_K ? tk : pb)) * a.score_scale;
+        }
     }
 
     // S^T of the tile: s[b][4 j + i] = dot of this lane's query with key kappa_of_row(32 b + 8 j + 4 h + i)
@@ -242,7 +255,8 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
                 if (kgroup(j, i) == q && (FP8 ? (b >> 1) == blk : b == blk)) amx = max(amx, s[b][r]);
             }
         const float mq = static_cast<float>(amx) * cg[gi];
-        mt = fmaxf(mt, amx != INT32_MIN ? mq : -__builtin_inff());
+        // only a masked tile can leave a group with no key (the int8 dots never reach INT32_MIN)
+        mt = fmaxf(mt, !TAIL || amx != INT32_MIN ? mq : -__builtin_inff());
     }
     mt = fmaxf(mt, shfl_xor(mt, 32));
     const float mo = st.m_run;
