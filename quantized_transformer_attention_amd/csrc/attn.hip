@@ -96,7 +96,9 @@ __device__ __forceinline__ DmaOffsets<D, KT, FP8> dma_lane_offsets(int kst, int 
     return r;
 }
 
-template <int D, int KT, bool FP8>
+// (TK: the kernel's key-scale layout, unused here; a specialization per kernel keeps the host pass from
+// sharing one across kernels, which it rejects)
+template <int D, int KT, bool FP8, bool TK>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int kst, int vrow,
                                          int kbase, uint8_t* kl, uint8_t* vl, int w, DmaOffsets<D, KT, FP8> off) {
     using C = Cfg<D, KT, FP8>;
@@ -117,38 +119,28 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buf
                                                  off.v + vb + (u * (4096 / C::RBV)) * vrow, 0, 0, 0);
 }
 
-// The key scales a lane needs for one tile, raw (FP32): THREAD_K the 4 scales of each 64-key
-// chunk (key t in group (t >> 1) & 3); PER_BLOCK with FP8 the scale of each 64-key chunk's lane-half
-// run in all four entries, with bf16 the scale of each 32-key block b at [b >> 1][b & 1] (its keys
-// never straddle a scale block for this lane half). Past the last scale the buffer load gives 0.
+// The key scales a lane needs for one tile, raw (FP32): THREAD_K (TK) the 4 scales of each 64-key
+// chunk (key t in group (t >> 1) & 3); PER_BLOCK the scale of each 32-key block b at [b >> 1][b & 1]
+// (its keys never straddle a scale block for this lane half). Past the last scale the buffer
+// load gives 0.
 template <int D, int KT, bool FP8>
 struct KScales {
     v4f c[Cfg<D, KT, FP8>::NCH];
 };
 
-template <int D, int KT, bool FP8>
-__device__ __forceinline__ KScales<D, KT, FP8> load_kscales(__amdgpu_buffer_rsrc_t r, int kbase, int h, int layout,
-                                                              int shift) {
+template <int D, int KT, bool FP8, bool TK>
+__device__ __forceinline__ KScales<D, KT, FP8> load_kscales(__amdgpu_buffer_rsrc_t r, int kbase, int h, int shift) {
     using C = Cfg<D, KT, FP8>;
     KScales<D, KT, FP8> k;
-    if (layout == SQ_LAYOUT_THREAD_K) {
+    if constexpr (TK) {
 #pragma unroll
         for (int ch = 0; ch < C::NCH; ++ch)
             k.c[ch] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * ((kbase >> 6) + ch), 0, 0));
-    } else if constexpr (FP8) {
-        // chunk ch: this lane half's 32 keys from kbase + 64 ch + 32 h lie in one scale block, whose
-        // scale stands for all four key groups (so that the products read group q's entry either way)
-#pragma unroll
-        for (int ch = 0; ch < C::NCH; ++ch) {
-            const int kmin = kbase + 64 * ch + 32 * h;
-            const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (kmin >> shift), 0, 0));
-            k.c[ch] = v4f{v, v, v, v};
-        }
     } else {
 #pragma unroll
         for (int b = 0; b < C::NB; ++b) {
             // the lowest key of this lane half in block b: its 32-key run lies in one scale block
-            const int kmin = kbase + 32 * b + 8 * h;
+            const int kmin = kbase + (FP8 ? 64 * (b >> 1) + 32 * h + 16 * (b & 1) : 32 * b + 8 * h);
             k.c[b >> 1][b & 1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 4 * (kmin >> shift), 0, 0));
         }
     }
@@ -199,10 +191,10 @@ __device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, f
         }
 }
 
-template <int D, int KT, bool FP8, bool TAIL>
+template <int D, int KT, bool FP8, bool TAIL, bool TK>
 __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
                                           const uint8_t* v_lds, int kbase, const KScales<D, KT, FP8>& ks, int ql,
-                                          int h, int qend0, int layout) {
+                                          int h, int qend0) {
     using C = Cfg<D, KT, FP8>;
     // c = RN(qs ks) per score group (times score_scale: exact for 1)
     float cg[C::NG];
@@ -211,12 +203,8 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
         const int q = gi & 3, blk = gi >> 2;                  // FP8: blk = 64-key chunk; bf16: 32-key block
         const int ch = FP8 ? blk : blk >> 1;
         const float tk = ks.c[ch][q];
-        if constexpr (FP8) {
-            cg[gi] = (st.qsc * tk) * a.score_scale;   // either layout: the loader put group q's scale at q
-        } else {
-            const float pb = ks.c[ch][blk & 1];
-            cg[gi] = (st.qsc * (layout == SQ_LAYOUT_THREAD_K ? tk : pb)) * a.score_scale;
-        }
+        const float pb = FP8 ? ks.c[ch][0] : ks.c[ch][blk & 1];
+        cg[gi] = (st.qsc * (TK ? tk : pb)) * a.score_scale;
     }
 
     // S^T of the tile: s[b][4 j + i] = dot of this lane's query with key kappa_of_row(32 b + 8 j + 4 h + i)
@@ -304,7 +292,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
 }
 
 
-template <int D, int KT, bool FP8>
+template <int D, int KT, bool FP8, bool TK>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     using C = Cfg<D, KT, FP8>;
     static_assert(!FP8 || KT % 64 == 0, "FP8 P.V takes 64 keys per product");
@@ -350,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const uint8_t* vb = static_cast<const uint8_t*>(a.v) + (b * a.vsb + hk * a.vsh) * C::VB;
     const float* ksp = a.ks + b * a.kssb + hk * a.kssh;
     const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ksp), 0, 4 * a.k_nscale, 0x00020000);
-    const int kl_layout = a.k_layout, kl_shift = a.k_shift;
+    const int kl_shift = a.k_shift;
     // Causal: query i sits at key position i + Sk - Sq and sees keys up to it. The workgroup
     // reads the key tiles its last query sees; a wave masks the tiles past its first query's
     // end (lo_end) and skips those past its last query's end (hi_end).
@@ -366,10 +354,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), 0, D * vrow, 0x00020000);
     const DmaOffsets<D, KT, FP8> doff = dma_lane_offsets<D, KT, FP8>(kst, vrow, w, l);
     // tile j streams into buffer j % 2 while tile j - 1 is processed from the other one
-    auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, doff); };
+    auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8, TK>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, doff); };
     // the key scales of tile j + 1 are fetched (before its K/V copy) while tile j is
     // processed, so no wait on them ever waits for a copy in flight
-    auto kscales = [&](int j) { return load_kscales<D, KT, FP8>(ksr, j * KT, h, kl_layout, kl_shift); };
+    auto kscales = [&](int j) { return load_kscales<D, KT, FP8, TK>(ksr, j * KT, h, kl_shift); };
     KScales<D, KT, FP8> ks_next = kscales(0);
     copy(0, buf0);
     wait_vm();
@@ -389,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         // a tile past the wave's last query's key end leaves its state unchanged
         const int kbase = j * KT;
         if (!TAIL || kbase < hi_end)
-            tile_step<D, KT, FP8, TAIL>(a, st, cur, cur + C::KBYTES, kbase, ks_cur, ql, h, qend0, kl_layout);
+            tile_step<D, KT, FP8, TAIL, TK>(a, st, cur, cur + C::KBYTES, kbase, ks_cur, ql, h, qend0);
         wait_vm();
         __syncthreads();
     };
@@ -461,26 +449,33 @@ int launch_v_transpose(const VTransposeArgs& a, void* stream) {
     return SQ_OK;
 }
 
+// k_attn<D, KT, FP8, TK> for the run-time head dim, key tile, P.V type and key-scale layout (written
+// out: a host template around the launches makes the host pass check the kernel bodies)
+#define SQ_ATTN_LAUNCH_DK(FP8, TK)                                                      \
+    do {                                                                                \
+        if (a.kv_tile == 128) {                                                         \
+            if (a.D == 128) SQ_LAUNCH((k_attn<128, 128, FP8, TK>), grid, dim3(256), 0, s, a); \
+            else SQ_LAUNCH((k_attn<64, 128, FP8, TK>), grid, dim3(256), 0, s, a);       \
+        } else {                                                                        \
+            if (a.D == 128) SQ_LAUNCH((k_attn<128, 64, FP8, TK>), grid, dim3(256), 0, s, a); \
+            else SQ_LAUNCH((k_attn<64, 64, FP8, TK>), grid, dim3(256), 0, s, a);        \
+        }                                                                               \
+    } while (0)
+
 int launch_attn(const AttnArgs& a, void* stream) {
     if (a.B * a.Sq * a.H == 0) return SQ_OK;
     const int64_t items = (a.Sq + 127) / 128 * a.H * a.B;
     dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));
     hipStream_t s = S(stream);
+    const bool tk = a.k_layout == SQ_LAYOUT_THREAD_K;
     if (a.v_fp8) {
-        if (a.kv_tile == 128) {
-            if (a.D == 128) SQ_LAUNCH((k_attn<128, 128, true>), grid, dim3(256), 0, s, a);
-            else SQ_LAUNCH((k_attn<64, 128, true>), grid, dim3(256), 0, s, a);
-        } else {
-            if (a.D == 128) SQ_LAUNCH((k_attn<128, 64, true>), grid, dim3(256), 0, s, a);
-            else SQ_LAUNCH((k_attn<64, 64, true>), grid, dim3(256), 0, s, a);
-        }
-    } else if (a.kv_tile == 128) {
-        if (a.D == 128) SQ_LAUNCH((k_attn<128, 128, false>), grid, dim3(256), 0, s, a);
-        else SQ_LAUNCH((k_attn<64, 128, false>), grid, dim3(256), 0, s, a);
+        if (tk) SQ_ATTN_LAUNCH_DK(true, true);
+        else SQ_ATTN_LAUNCH_DK(true, false);
     } else {
-        if (a.D == 128) SQ_LAUNCH((k_attn<128, 64, false>), grid, dim3(256), 0, s, a);
-        else SQ_LAUNCH((k_attn<64, 64, false>), grid, dim3(256), 0, s, a);
+        if (tk) SQ_ATTN_LAUNCH_DK(false, true);
+        else SQ_ATTN_LAUNCH_DK(false, false);
     }
+#undef SQ_ATTN_LAUNCH_DK
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_attn: kernel launch failed: %s", hipGetErrorString(e));
     return SQ_OK;
