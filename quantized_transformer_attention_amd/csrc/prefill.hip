@@ -30,9 +30,9 @@
 //  * the softmax denominator sums the same f16 P that multiplied the values (dot2 against
 //    ones, FP32), so out = acc / l is a weighted mean whose weights are exactly those P (a
 //    one-key row returns its value).
-//  * causal: a workgroup reads the tiles up to its last row's end; a wave runs the tiles
-//    below its first row's diagonal without masking code, masks those that cross its rows'
-//    diagonal and skips those past its last row.
+//  * causal: a workgroup reads the tiles up to its last row's end; the tiles below its first
+//    row's diagonal run in a loop without masking code, and from there on a wave masks the
+//    tiles it sees and skips those past its last row.
 //  * the reference max of a row trails its running max by at most 8 (base 2): the
 //    accumulator is rescaled only when a tile raises some row's max beyond that, so p <= 2^8
 //    (the f16 P rounds relative to itself whatever the reference; l and acc are FP32).
