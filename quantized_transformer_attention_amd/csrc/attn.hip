@@ -246,7 +246,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
         // only a masked tile can leave a group with no key (the int8 dots never reach INT32_MIN)
         mt = fmaxf(mt, !TAIL || amx != INT32_MIN ? mq : -__builtin_inff());
     }
-    mt = fmaxf(mt, shfl_xor(mt, 32));
+    mt = swap32_max(mt);
     const float mo = st.m_run;
     const float mn = fmaxf(mo, mt);
     const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
     // epilogue: l over the two lane halves, lse, out = acc / l (x vs / 256)
     float lt = st.l_run;
-    lt = lt + shfl_xor(lt, 32);
+    lt = swap32_add(lt);
     const int qi = q0i + ql;
     if (lbase && h == 0 && qi < Sq) lbase[qi] = st.m_run + log2f(lt);
     if (qi < Sq) {

@@ -160,8 +160,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(f[g][k]));
         }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx = swap32_max(swap16_max(mx));
         sh = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) + 1 : 0;
 #pragma unroll
         for (int g = 0; g < NG; ++g)
@@ -225,8 +224,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
                                       static_cast<float>(s23[1]))
                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         float mx = fmaxf(fmaxf(fabsf(sf.x), fabsf(sf.y)), fmaxf(fabsf(sf.z), fabsf(sf.w)));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+        mx = wave_max(mx);
         esh = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
         sf.x = __builtin_amdgcn_ldexpf(sf.x, esh);
         sf.y = __builtin_amdgcn_ldexpf(sf.y, esh);
@@ -241,8 +239,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float m = fmaxf(fmaxf(sc[h][l], sc[h][64 + l]), fmaxf(sc[h][128 + l], sc[h][192 + l]));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor(m, off));
+        m = wave_max(m);
         M[h] = m;
     }
 
@@ -294,8 +291,7 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
             o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pw[ct >> 1], i8x8_to_f16(raw[0], raw[1]), o[ct], 0, 0, 0);
         }
     }
-    lsum += shfl_xor(lsum, 16);
-    lsum += shfl_xor(lsum, 32);
+    lsum = swap32_add(swap16_add(lsum));
     // undo the value-scale factor (exact: a power of two on FP32)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -355,8 +351,7 @@ __global__ __launch_bounds__(D) void k_decode_reduce(DecodeArgs a) {
     const float* p = a.part + (static_cast<int64_t>(n) * a.Hq + hq) * a.segs * (D + 2);
     float mg = -__builtin_inff();
     for (int s = c; s < nseg; s += SB) mg = fmaxf(mg, p[s * (D + 2) + D]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, shfl_xor(mg, off));
+    mg = wave_max(mg);
     if ((c & 63) == 0) red[c >> 6] = mg;
     __syncthreads();
     // a sink joins as one more term of the denominator, at its logit in base 2

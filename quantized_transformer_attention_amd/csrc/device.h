@@ -106,6 +106,26 @@ __device__ __forceinline__ float row_ror(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + N, 0xf, 0xf, true));
 }
 
+// v op v' with v' the value of lane l ^ 16 (v_permlane16_swap) or l ^ 32 (v_permlane32_swap): the swap
+// hands each lane the pair (v_l, v_l') in one order or the other, and op is symmetric, so every lane
+// gets the same bits as with an LDS shuffle, without one.
+__device__ __forceinline__ float swap16_max(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float swap32_max(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float swap16_add(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float swap32_add(float v) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // Reductions over a row of LPR lanes (LPR in {8, 16}); every lane of the row gets the
 // result. The sum adds partners at lane offsets LPR/2, .., 2, 1 in that order: rotating a
 // 16-lane row by 8, 4, 2, 1 pairs each lane with the same values as xor offsets 8, 4, 2, 1
@@ -147,6 +167,16 @@ template <int LPR, int J>
 __device__ __forceinline__ float row_lane(float v) {
     constexpr int pattern = (0x1f & ~(LPR - 1)) | (J << 5);
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), pattern));
+}
+
+// Maximum over the 64 lanes of a wave (every lane gets it): DPP row rotations by 8, 4, 2, 1, then the
+// lane swaps across rows and halves.
+__device__ __forceinline__ float wave_max(float m) {
+    m = fmaxf(m, row_ror<8>(m));
+    m = fmaxf(m, row_ror<4>(m));
+    m = fmaxf(m, row_ror<2>(m));
+    m = fmaxf(m, row_ror<1>(m));
+    return swap32_max(swap16_max(m));
 }
 
 template <int NS>

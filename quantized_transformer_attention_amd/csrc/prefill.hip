@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
 #pragma unroll
             for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(f[c][e]));
         }
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx = swap32_max(mx);
         const int sh = mx > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
 #pragma unroll
         for (int c = 0; c < C::NCS; ++c)
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
     for (int j = j_whole; j < ntiles; ++j) step(j, std::true_type{});
 
     // ---- epilogue: out = acc / l, the denominator summed over both halves
-    const float lt = st.l + shfl_xor(st.l, 32);
+    const float lt = swap32_add(st.l);
     if (jq >= qlen || qs0 + jq < 0 || qs0 + jq >= a.T) return;
     const float inv = 1.0f / lt;
     const int64_t orow = static_cast<int64_t>(qs0 + jq) * a.ot + static_cast<int64_t>(hq) * a.oh;

@@ -171,7 +171,7 @@ __device__ __forceinline__ void prefix_tile(PWave<D, KT>& st, const uint8_t* img
     for (int b = 0; b < C::NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, t[b][r]);
-    mt = fmaxf(mt, shfl_xor(mt, 32));
+    mt = swap32_max(mt);
     const float ms = __builtin_fmaf(mt, st.c1, -st.c2);
     const float mo = st.m_run;
     const float mn = fmaxf(mo, ms);
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void k_prefix(PrefixArgs a) {
                                        mv[e], d);
             }
         }
-        d = d + shfl_xor(d, 32);
+        d = swap32_add(d);
         st.c1 = qsc * a.score_scale;
         st.c2 = (qsc * d) * a.score_scale;
         st.m_run = -__builtin_inff();
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void k_prefix(PrefixArgs a) {
 
     // ---- epilogue: prefix (out, lse) merged into (out, lse) in place
     float lt = st.l_run;
-    lt = lt + shfl_xor(lt, 32);
+    lt = swap32_add(lt);
     const float lse_p = st.m_run + log2f(lt);     // -inf when no key contributed
     if (!ok) return;
     float* lsep = a.lse + b * a.lb + hh * a.lh + qi;

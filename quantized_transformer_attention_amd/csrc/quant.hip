@@ -371,10 +371,16 @@ __device__ __forceinline__ void kmean_block(const KmeanArgs& a, int64_t b, int64
                 row_fetch<D, NORM, ROPE, CONTIG, PERTOK>(a.r, base, rr[i], h, lc, wrow[i], raw[i]);
         }
     }
+    // S + S' over lanes l ^ LPR, then l ^ 2 LPR (a symmetric add either way: the same bits as shuffles)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) S[k] = S[k] + shfl_xor(S[k], LPR);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) S[k] = S[k] + shfl_xor(S[k], 2 * LPR);
+    for (int k = 0; k < 8; ++k) {
+        if constexpr (LPR == 16) {
+            S[k] = swap32_add(swap16_add(S[k]));
+        } else {
+            S[k] = S[k] + row_ror<8>(S[k]);
+            S[k] = swap16_add(S[k]);
+        }
+    }
     if (r == 0) {
         float* dst = a.partial + ((b * a.r.H + h) * a.nblk + blk) * D;
         *reinterpret_cast<float4*>(dst + 4 * lc) = make_float4(S[0], S[1], S[2], S[3]);
@@ -585,9 +591,10 @@ __global__ __launch_bounds__(256) void k_v_amax(QuantVArgs a) {
         for (int k = 0; k < 8; ++k) m[k] = fmaxf(m[k], fabsf(x[k]));
     }
 #pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) m[k] = fmaxf(m[k], shfl_xor(m[k], off));
+    for (int k = 0; k < 8; ++k) {
+        if constexpr (LPR == 8) m[k] = fmaxf(m[k], row_ror<8>(m[k]));
+        m[k] = swap32_max(swap16_max(m[k]));
+    }
     if (lr == 0) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) red[w][lc * 8 + k] = m[k];
