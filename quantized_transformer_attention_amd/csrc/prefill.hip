@@ -11,18 +11,23 @@
 //
 // Design (one workgroup = NW waves = 32 NW rows = 32 NW / G tokens x G heads of one kv head;
 // 64-key tiles = 4 pages; head dim D = 64 or 128):
-//  * K and V tiles are staged once per workgroup, key-major in LDS (2 D bytes per key and
-//    array, 16-byte slots XOR-swizzled), each element as an exact pair of f16 values: hi =
+//  * K and V tiles are staged once per workgroup, key-major in LDS (16-byte slots
+//    XOR-swizzled), each element first split into an exact pair of f16 values: hi =
 //    f16(code scale) and lo = code scale - hi (one fused multiply-add; an int8 code times an
 //    FP16 scale is a multiple of 2^-24 with at most 18 significant bits, so the remainder is
-//    an f16 number, subnormal or not). Neither K nor V is rounded. The next tile's codes and
-//    scales are loaded into registers while the current tile is processed; the block-table
-//    entries of the tile after it are read (scalar) one step earlier still.
+//    an f16 number, subnormal or not). V keeps both halves (not rounded). K keeps hi as f16
+//    and lo as e4m3 of lo 2^-E with one power-of-two block scale 2^E per key and 32 channels
+//    (E = exponent of the FP16 scale - 13: lo 2^-E is a multiple of 4 of at most 256, normal
+//    in e4m3), so a key is off by at most 2^-4 |lo| <= 2^-16 |code scale|. The next tile's
+//    codes and scales are loaded into registers while the current tile is processed; the
+//    block-table entries of the tile after it are read (scalar) one step earlier still.
 //  * q (bf16 or f16) is carried as f16 after an exact power-of-two rescale per row (its
 //    largest |q| in [2^14, 2^15)), undone exactly in the row's score scale.
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_f16 (hi and lo products of each 16-channel step into
-//    one FP32 accumulator): one query row per lane (lane % 32), 16 keys of each 32-key block
-//    per lane, the wave halves holding different keys. K rows are permuted in LDS (the 32x32
+//  * S^T = K Q^T into one FP32 accumulator: the hi products on v_mfma_f32_32x32x16_f16, the
+//    lo products on v_mfma_scale_f32_32x32x64_f8f6f4 (one per 64 channels, the keys' block
+//    scales applied by the matrix unit) against an e4m3 copy of the rescaled q (q 2^-7, block
+//    scale 2^7): one query row per lane (lane % 32), 16 keys of each 32-key block per lane,
+//    the wave halves holding different keys. K rows are permuted in LDS (the 32x32
 //    attention core's key order) so that a lane's score registers are, in order, runs of 8
 //    consecutive keys: as f16 they are the B operand P^T of O^T = V^T P^T, whose A operand
 //    (8 keys of one channel per lane, hi and lo) is read from the key-major V tile by
@@ -54,21 +59,32 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lv4s_p;
 
 // LDS tile geometry of head dim D: per key one f16 row of D channels (NS 16-byte slots) in each of
-// K hi, K lo, V hi and V lo.
+// K hi, V hi and V lo; per key one row of D FP8 bytes (K lo, D / 16 16-byte slots) and 8 bytes of K lo
+// block scales.
 template <int D>
 struct PfTile {
     static constexpr int NS = D / 8, NCS = D / 16, NCB = D / 32;   // slots per row, 16-channel steps, 32-channel blocks
+    static constexpr int NCC = D / 64;                             // 64-channel steps of the FP8 products
     static constexpr int kRowB = 2 * D;
     static constexpr int kTileB = kKT * kRowB;                     // 16 KB at D = 128
-    static constexpr int kKLo = kTileB, kVHi = 2 * kTileB, kVLo = 3 * kTileB;
-    static constexpr int kBufB = 4 * kTileB;
+    static constexpr int kKLo8 = kTileB;                           // K lo as FP8: kKT rows of D bytes
+    static constexpr int kKE = kKLo8 + kKT * D;                    // K lo block scales: 8 bytes per row
+    static constexpr int kVHi = (kKE + kKT * 8 + 1023) / 1024 * 1024, kVLo = kVHi + kTileB;
+    static constexpr int kBufB = kVLo + kTileB;
     static constexpr int KPW = kWave * 16 / D;                     // keys a wave stages per pass
 };
+
+// The E8M0 block scale of the FP8 products' q operand: q (largest |q| in [2^14, 2^15)) goes to FP8 as
+// q 2^-7, so its scale is 2^7.
+constexpr int kQ8Exp = 7;
 
 // LDS row of key kappa in the K tile: the inverse of kappa_of_row<false> (32-key blocks; within a
 // block, row 8 j + 4 h + i holds key 16 (j >> 1) + 8 h + 4 (j & 1) + i).
@@ -112,22 +128,44 @@ constexpr int kSgMfma = 0x008, kSgValu = 0x002 | 0x400, kSgDsRead = 0x100;
 // Operands come from LDS two steps ahead of their products (rings of three stages), and the
 // exponentials of the next 16-key block are interleaved with the current block's P.V products, so
 // the matrix unit and the vector unit of a wave overlap.
-template <int D, bool TAIL>
-__device__ __forceinline__ void pf_tile(PfState<D>& st, const uint8_t* buf, int kbase, int lim, int ql, int h,
-                                        int l) {
+template <int D, bool TAIL, typename Mid>
+__device__ __forceinline__ void pf_tile(PfState<D>& st, const uint8_t* buf, const uint8_t* q8w, int kbase, int lim,
+                                        int ql, int h, int l, Mid mid) {
     using C = PfTile<D>;
     constexpr int RING = 3;
-    // ---- S^T: step c takes channels 16 c .. 16 c + 15 of both 32-key blocks, hi and lo
+    // ---- S^T: step c takes channels 16 c .. 16 c + 15 of K hi for both 32-key blocks (f16 products),
+    // step cc channels 64 cc .. 64 cc + 63 of K lo (FP8 products, the row's block scales applied by the
+    // matrix unit)
     v16f s[2];
-    v8h kop[RING][4];
+    v8h kop[RING][2];
     auto kread = [&](int c, v8h* dst) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int row = 32 * b + ql;
-            const int off = row * C::kRowB + swz<C::NS>(row, 2 * c + h) * 16;
-            dst[2 * b] = *reinterpret_cast<const v8h*>(buf + off);
-            dst[2 * b + 1] = *reinterpret_cast<const v8h*>(buf + C::kKLo + off);
+            dst[b] = *reinterpret_cast<const v8h*>(buf + row * C::kRowB + swz<C::NS>(row, 2 * c + h) * 16);
         }
+    };
+    // K lo of this lane's rows, in the scaled product's operand order: registers 0-3 hold channels
+    // 64 cc + 16 h .. + 15 and registers 4-7 channels 64 cc + 32 + 16 h .. + 15 (16-byte slots 4 cc + h and
+    // 4 cc + 2 + h of the D-byte row), while the block scale a lane supplies covers the 32 channels
+    // 64 cc + 32 h .. + 31, half of them held by the other half-wave (group 2 cc + h, byte cc of the row's
+    // scale word h); then this lane's FP8 q operand in the same order (the wave's LDS copy: 16-byte
+    // pieces k of step cc at (2 cc + k) KB). Step cc is read two f16 steps before its products.
+    v8i klo[2], q8;
+    uint32_t kesc[2];
+    auto loread = [&](int cc) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int row = 32 * b + ql;
+            if (cc == 0) kesc[b] = *reinterpret_cast<const uint32_t*>(buf + C::kKE + row * 8 + 4 * h);
+            const uint8_t* rb = buf + C::kKLo8 + row * D;
+            const v4i lo0 = *reinterpret_cast<const v4i*>(rb + swz<D / 16>(row, 4 * cc + h) * 16);
+            const v4i lo1 = *reinterpret_cast<const v4i*>(rb + swz<D / 16>(row, 4 * cc + 2 + h) * 16);
+            klo[b] = v8i{lo0[0], lo0[1], lo0[2], lo0[3], lo1[0], lo1[1], lo1[2], lo1[3]};
+        }
+        const v4i a0 = *reinterpret_cast<const v4i*>(q8w + (2 * cc) * 1024 + 16 * l);
+        const v4i a1 = *reinterpret_cast<const v4i*>(q8w + (2 * cc + 1) * 1024 + 16 * l);
+        q8 = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     };
     // A operand of P.V step t (key block u = t / NCB, channel block cb = t % NCB): lane l gets channel
     // 32 cb + l % 32 of keys 16 u + 8 h .. + 7, two transposing reads of 4 keys x 16 channels per
@@ -158,13 +196,23 @@ __device__ __forceinline__ void pf_tile(PfState<D>& st, const uint8_t* buf, int 
         __builtin_amdgcn_sched_barrier(0);
         if (c + 2 < C::NCS) kread(c + 2, kop[(c + 2) % RING]);
         else if (c + 2 - C::NCS < 2) vread(c + 2 - C::NCS);     // the first P.V operands
+        // the FP8 steps: step cc after f16 step (cc + 1) NCS / NCC - 1, its operands read two steps before
+        constexpr int SPC = C::NCS / C::NCC;     // f16 steps per FP8 step
+        if ((c + 3) % SPC == 0) loread((c + 3) / SPC - 1);
         const v8h* k = kop[c % RING];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[2 * b], st.qop[c], c == 0 ? v16f{} : s[b], 0, 0, 0);
-            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[2 * b + 1], st.qop[c], s[b], 0, 0, 0);
+        for (int b = 0; b < 2; ++b)
+            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k[b], st.qop[c], c == 0 ? v16f{} : s[b], 0, 0, 0);
+        if ((c + 1) % SPC == 0) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                s[b] = (c + 1) / SPC == 1
+                           ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(klo[b], q8, s[b], 0, 0, 0, kesc[b], 0, 127 + kQ8Exp)
+                           : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(klo[b], q8, s[b], 0, 0, 1, kesc[b], 0, 127 + kQ8Exp);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    mid();   // the next tile's code loads go out here, after the score products
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (TAIL) {
         // a lane of half h holds the half-0 keys plus 8 h; opaque so that it is not hoisted
@@ -246,6 +294,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
     constexpr int kRows = 32 * NW;                      // rows per workgroup
     constexpr int BQ = kRows / G;                       // query tokens per workgroup
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBufB];
+    __shared__ __attribute__((aligned(1024))) uint8_t q8s[NW * C::NCC * 2048];   // each wave's FP8 q operands
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, ql = l & 31, h = l >> 5;
 
     // ---- work item: (kv head, q block); the q blocks of a kv head run on one XCD, last first
@@ -308,6 +357,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
         for (int c = 0; c < C::NCS; ++c)
 #pragma unroll
             for (int e = 0; e < 8; ++e) st.qop[c][e] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(f[c][e], sh));
+        // the FP8 products' operand, q 2^(sh - 7) as e4m3 in the scaled product's order: channels
+        // 64 cc + 16 h .. + 15, then 64 cc + 32 + 16 h .. + 15 of the same row
+#pragma unroll
+        for (int cc = 0; cc < C::NCC; ++cc) {
+            v4u r8[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                r8[k] = ok ? *reinterpret_cast<const v4u*>(qp + 64 * cc + 32 * (k >> 1) + 16 * h + 8 * (k & 1)) : v4u{0u, 0u, 0u, 0u};
+            const float s8 = __builtin_amdgcn_ldexpf(1.0f, kQ8Exp - sh);   // the convert divides by it
+            int q8v[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float g[8];
+                const uint4 rc = make_uint4(r8[k][0], r8[k][1], r8[k][2], r8[k][3]);
+                if (a.q_f16) unpack_f16x8(rc, g);
+                else unpack_bf16x8(rc, g);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    v2s w = {};
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, g[4 * e], g[4 * e + 1], s8, false);
+                    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, g[4 * e + 2], g[4 * e + 3], s8, true);
+                    q8v[2 * k + e] = __builtin_bit_cast(int, w);
+                }
+            }
+            uint8_t* q8w = q8s + w * C::NCC * 2048;
+            *reinterpret_cast<v4i*>(q8w + (2 * cc) * 1024 + 16 * l) = v4i{q8v[0], q8v[1], q8v[2], q8v[3]};
+            *reinterpret_cast<v4i*>(q8w + (2 * cc + 1) * 1024 + 16 * l) = v4i{q8v[4], q8v[5], q8v[6], q8v[7]};
+        }
         st.cr = __builtin_amdgcn_ldexpf(a.scale, -sh);
         st.m_run = a.sinks ? a.sinks[hq] * 1.44269504f : -__builtin_inff();
         // a sink is one more term 2^(sink - m) = 1 of the row's denominator, counted in half 0
@@ -356,8 +433,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
         const int k0 = kr * kRowB + swz<C::NS>(kr, 2 * part) * 16, k1 = kr * kRowB + swz<C::NS>(kr, 2 * part + 1) * 16;
         *reinterpret_cast<v8h*>(buf + k0) = kh0;
         *reinterpret_cast<v8h*>(buf + k1) = kh1;
-        *reinterpret_cast<v8h*>(buf + C::kKLo + k0) = kl0;
-        *reinterpret_cast<v8h*>(buf + C::kKLo + k1) = kl1;
+        // K lo to FP8 as lo 2^-E, E = (exponent of ks) - 13: |lo| <= 2^-12 |code ks| keeps lo 2^-E within
+        // 256 (e4m3 holds 448), and its grain (a multiple of 2^-10 of the scale's leading bit) maps to
+        // multiples of 4, so no e4m3 subnormal arises; the products apply 2^E through the block scale
+        const int ee = __builtin_amdgcn_frexp_expf(static_cast<float>(ks)) - 13;
+        const float e2 = __builtin_amdgcn_ldexpf(1.0f, ee);
+        v4i lo8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v8h& src = q < 2 ? kl0 : kl1;
+            v2s w = {};
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, v2h{src[4 * (q & 1)], src[4 * (q & 1) + 1]}, e2, false);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, v2h{src[4 * (q & 1) + 2], src[4 * (q & 1) + 3]}, e2, true);
+            lo8[q] = __builtin_bit_cast(int, w);
+        }
+        *reinterpret_cast<v4i*>(buf + C::kKLo8 + kr * D + swz<D / 16>(kr, part) * 16) = lo8;
+        // the block scale of group part / 2 (both threads of the group compute it; the even one stores):
+        // byte 4 (g & 1) + (g >> 1) of the row's 8
+        if ((part & 1) == 0) {
+            const int g = part >> 1;
+            buf[C::kKE + kr * 8 + 4 * (g & 1) + (g >> 1)] = static_cast<uint8_t>(127 + ee);
+        }
         const int v0 = kappa * kRowB + v_slot<D>(kappa, 2 * part) * 16, v1 = kappa * kRowB + v_slot<D>(kappa, 2 * part + 1) * 16;
         *reinterpret_cast<v8h*>(buf + C::kVHi + v0) = vh0;
         *reinterpret_cast<v8h*>(buf + C::kVHi + v1) = vh1;
@@ -378,11 +474,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_paged_prefill(PrefillArgs a
     auto step = [&](int j, auto tail) {
         uint8_t* cur = lds + (j & 1) * kBufB;
         uint8_t* nxt = lds + ((j + 1) & 1) * kBufB;
-        load_tile(nb);                                  // tile j + 1 (the last tile again past the end)
-        nb = page_block(min(j + 2, ntiles - 1));
-        __builtin_amdgcn_sched_barrier(0);              // the loads go out before the tile's arithmetic
+        // tile j + 1's codes (the last tile again past the end) are loaded once this tile's scores are in
+        // flight, so their registers are not held through the score products
+        auto mid = [&]() {
+            load_tile(nb);
+            nb = page_block(min(j + 2, ntiles - 1));
+        };
         const int kbase = j * kKT;
-        if (!decltype(tail)::value || kbase < hi_end) pf_tile<D, decltype(tail)::value>(st, cur, kbase, lim, ql, h, l);
+        if (!decltype(tail)::value || kbase < hi_end)
+            pf_tile<D, decltype(tail)::value>(st, cur, q8s + w * C::NCC * 2048, kbase, lim, ql, h, l, mid);
+        else
+            mid();
         store_tile(nxt, (j + 1) * kKT);
         __syncthreads();
     };

@@ -3,10 +3,11 @@
 
 Tolerance: every element within 2e-3 rms(row) and ||gpu - ref|| <= 2e-3 ||ref|| per (token, head) row, the row
 being that query's own attention output (the rows of a batch attend 1 to thousands of keys, so their output RMS
-differs by orders of magnitude). The kernel's arithmetic: keys and values exact (codes widened to f16, key scales
-applied in FP32 per 32-channel dot, values as exact f16 pairs), P rounded once to f16 (relative <= 2^-11), its
-denominator summed from the same rounded P; a CPU emulation of that arithmetic gives at most 1.5e-3 per element
-on these inputs."""
+differs by orders of magnitude). The kernel's arithmetic: values exact (code scale as two f16 halves), keys as
+f16(code scale) plus the remainder rounded to e4m3 with a power-of-two block scale (a key off by at most 2^-16 of
+itself), q as f16 after a power-of-two rescale with an e4m3 copy for the remainder products, P rounded once to f16
+(relative <= 2^-11), its denominator summed from the same rounded P; a CPU emulation of that arithmetic gives at
+most 1.1e-3 rms(row) per element on these inputs."""
 import math
 
 import numpy as np
