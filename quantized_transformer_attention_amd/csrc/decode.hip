@@ -309,30 +309,27 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(DecodeArgs a) {
     float* lred = reinterpret_cast<float*>(vsf[w]);
     if (j == 0 && lc < G) lred[lc] = lsum;
     __syncthreads();
-    const int nseg = a.segs;
-    for (int idx = tid; idx < G * (D + 2); idx += 256) {
-        const int h = idx / (D + 2), c = idx % (D + 2);
-        float v;
-        if (c < D) {
-            const float* r0 = reinterpret_cast<const float*>(vst[0]);
-            const float* r1 = reinterpret_cast<const float*>(vst[1]);
-            const float* r2 = reinterpret_cast<const float*>(vst[2]);
-            const float* r3 = reinterpret_cast<const float*>(vst[3]);
-            v = (r0[h * D + c] + r1[h * D + c]) + (r2[h * D + c] + r3[h * D + c]);
-        } else if (c == D) {
-            float mh = -__builtin_inff();
+    // partial of head h: acc (D), max, exp-sum at part[((n Hq + hk G + h) segs + seg) (D + 2)]
+    const int64_t hstride = static_cast<int64_t>(a.segs) * (D + 2);
+    float* prow = a.part + (static_cast<int64_t>(n) * a.Hq + hk * G) * hstride + static_cast<int64_t>(seg) * (D + 2);
+    const float* r0 = reinterpret_cast<const float*>(vst[0]);
+    const float* r1 = reinterpret_cast<const float*>(vst[1]);
+    const float* r2 = reinterpret_cast<const float*>(vst[2]);
+    const float* r3 = reinterpret_cast<const float*>(vst[3]);
 #pragma unroll
-            for (int q = 0; q < G; ++q)
-                if (q == h) mh = M[q];
-            v = mh;
-        } else {
-            const float* l0 = reinterpret_cast<const float*>(vsf[0]);
-            const float* l1 = reinterpret_cast<const float*>(vsf[1]);
-            const float* l2 = reinterpret_cast<const float*>(vsf[2]);
-            const float* l3 = reinterpret_cast<const float*>(vsf[3]);
-            v = (l0[h] + l1[h]) + (l2[h] + l3[h]);
-        }
-        a.part[((static_cast<int64_t>(n) * a.Hq + hk * G + h) * nseg + seg) * (D + 2) + c] = v;
+    for (int idx = tid; idx < G * D; idx += 256)   // element h D + c of the wave rows: head h, channel c
+        prow[(idx / D) * hstride + idx % D] = (r0[idx] + r1[idx]) + (r2[idx] + r3[idx]);
+    if (tid < G) {
+        float mh = M[0];
+#pragma unroll
+        for (int q = 1; q < G; ++q)
+            if (q == tid) mh = M[q];
+        const float* l0 = reinterpret_cast<const float*>(vsf[0]);
+        const float* l1 = reinterpret_cast<const float*>(vsf[1]);
+        const float* l2 = reinterpret_cast<const float*>(vsf[2]);
+        const float* l3 = reinterpret_cast<const float*>(vsf[3]);
+        prow[tid * hstride + D] = mh;
+        prow[tid * hstride + D + 1] = (l0[tid] + l1[tid]) + (l2[tid] + l3[tid]);
     }
 }
 
