@@ -178,7 +178,8 @@ __device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, f
                 if (TAIL && av == INT32_MIN) x = -__builtin_inff();   // a masked key: p = 0 exactly
                 const float pv = __builtin_amdgcn_exp2f(x);
                 p[i] = pv;
-                lsum += pv;
+                if (b == 0 && j == 0 && i == 0) lsum = pv;   // the first term starts the sum (no 0 + p)
+                else lsum += pv;
             }
             if constexpr (FP8) {
                 // keys 64 (b >> 1) + 32 h + 16 (b & 1) + 4 j + i: dword 4 (b & 1) + j of chunk b >> 1
@@ -191,12 +192,12 @@ __device__ __forceinline__ void exp_pack(const v16i (&s)[NB], const float* cg, f
         }
 }
 
-template <int D, int KT, bool FP8, bool TAIL, bool TK>
+template <int D, int KT, bool FP8, bool TAIL, bool TK, bool SS>
 __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP8>& st, const uint8_t* k_lds,
                                           const uint8_t* v_lds, int kbase, const KScales<D, KT, FP8>& ks, int ql,
                                           int h, int qend0) {
     using C = Cfg<D, KT, FP8>;
-    // c = RN(qs ks) per score group (times score_scale: exact for 1)
+    // c = RN(qs ks) per score group, times score_scale when it is not 1 (SS)
     float cg[C::NG];
 #pragma unroll
     for (int gi = 0; gi < C::NG; ++gi) {
@@ -204,7 +205,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
         const int ch = FP8 ? blk : blk >> 1;
         const float tk = ks.c[ch][q];
         const float pb = FP8 ? ks.c[ch][0] : ks.c[ch][blk & 1];
-        cg[gi] = (st.qsc * (TK ? tk : pb)) * a.score_scale;
+        cg[gi] = SS ? (st.qsc * (TK ? tk : pb)) * a.score_scale : st.qsc * (TK ? tk : pb);
     }
 
     // S^T of the tile: s[b][4 j + i] = dot of this lane's query with key kappa_of_row(32 b + 8 j + 4 h + i)
@@ -249,7 +250,9 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
     mt = swap32_max(mt);
     const float mo = st.m_run;
     const float mn = fmaxf(mo, mt);
-    const float alpha = (mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+    // alpha = 0 while m is -inf: exp2(-inf - m') is 0 when m' is finite, which every tile without
+    // masked keys makes it; only a masked tile can leave m' at -inf (and -inf - -inf undefined)
+    const float alpha = (TAIL && mo == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
     st.m_run = mn;
 
     // p = 2^(a c - m'), l += p, P^T operands
@@ -257,7 +260,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
     v8i pf8[C::NCH];
     v8bf pbf[KT / 16];
     exp_pack<FP8, C::NB, TAIL>(s, cg, mn, lsum, pf8, pbf);
-    st.l_run = st.l_run * alpha + lsum;
+    st.l_run = __builtin_fmaf(st.l_run, alpha, lsum);
 
     // Rescale the accumulator of this lane's query by alpha, unless no query of the wave moved its max
     // (alpha is then exactly 1 everywhere and the products would change nothing). The products are
@@ -292,7 +295,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs& a, WaveState<D, KT, FP
 }
 
 
-template <int D, int KT, bool FP8, bool TK>
+template <int D, int KT, bool FP8, bool TK, bool SS>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     using C = Cfg<D, KT, FP8>;
     static_assert(!FP8 || KT % 64 == 0, "FP8 P.V takes 64 keys per product");
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         // a tile past the wave's last query's key end leaves its state unchanged
         const int kbase = j * KT;
         if (!TAIL || kbase < hi_end)
-            tile_step<D, KT, FP8, TAIL, TK>(a, st, cur, cur + C::KBYTES, kbase, ks_cur, ql, h, qend0);
+            tile_step<D, KT, FP8, TAIL, TK, SS>(a, st, cur, cur + C::KBYTES, kbase, ks_cur, ql, h, qend0);
         wait_vm();
         __syncthreads();
     };
@@ -449,17 +452,23 @@ int launch_v_transpose(const VTransposeArgs& a, void* stream) {
     return SQ_OK;
 }
 
-// k_attn<D, KT, FP8, TK> for the run-time head dim, key tile, P.V type and key-scale layout (written
-// out: a host template around the launches makes the host pass check the kernel bodies)
-#define SQ_ATTN_LAUNCH_DK(FP8, TK)                                                      \
-    do {                                                                                \
-        if (a.kv_tile == 128) {                                                         \
-            if (a.D == 128) SQ_LAUNCH((k_attn<128, 128, FP8, TK>), grid, dim3(256), 0, s, a); \
-            else SQ_LAUNCH((k_attn<64, 128, FP8, TK>), grid, dim3(256), 0, s, a);       \
-        } else {                                                                        \
-            if (a.D == 128) SQ_LAUNCH((k_attn<128, 64, FP8, TK>), grid, dim3(256), 0, s, a); \
-            else SQ_LAUNCH((k_attn<64, 64, FP8, TK>), grid, dim3(256), 0, s, a);        \
-        }                                                                               \
+// k_attn<D, KT, FP8, TK, SS> for the run-time head dim, key tile, P.V type, key-scale layout and score
+// scale (SS: not 1) (written out: a host template around the launches makes the host pass check the
+// kernel bodies)
+#define SQ_ATTN_LAUNCH_DK(FP8, TK, SS)                                                       \
+    do {                                                                                     \
+        if (a.kv_tile == 128) {                                                              \
+            if (a.D == 128) SQ_LAUNCH((k_attn<128, 128, FP8, TK, SS>), grid, dim3(256), 0, s, a); \
+            else SQ_LAUNCH((k_attn<64, 128, FP8, TK, SS>), grid, dim3(256), 0, s, a);        \
+        } else {                                                                             \
+            if (a.D == 128) SQ_LAUNCH((k_attn<128, 64, FP8, TK, SS>), grid, dim3(256), 0, s, a); \
+            else SQ_LAUNCH((k_attn<64, 64, FP8, TK, SS>), grid, dim3(256), 0, s, a);         \
+        }                                                                                    \
+    } while (0)
+#define SQ_ATTN_LAUNCH_SS(FP8, TK)                            \
+    do {                                                      \
+        if (a.score_scale != 1.0f) SQ_ATTN_LAUNCH_DK(FP8, TK, true); \
+        else SQ_ATTN_LAUNCH_DK(FP8, TK, false);               \
     } while (0)
 
 int launch_attn(const AttnArgs& a, void* stream) {
@@ -469,12 +478,13 @@ int launch_attn(const AttnArgs& a, void* stream) {
     hipStream_t s = S(stream);
     const bool tk = a.k_layout == SQ_LAYOUT_THREAD_K;
     if (a.v_fp8) {
-        if (tk) SQ_ATTN_LAUNCH_DK(true, true);
-        else SQ_ATTN_LAUNCH_DK(true, false);
+        if (tk) SQ_ATTN_LAUNCH_SS(true, true);
+        else SQ_ATTN_LAUNCH_SS(true, false);
     } else {
-        if (tk) SQ_ATTN_LAUNCH_DK(false, true);
-        else SQ_ATTN_LAUNCH_DK(false, false);
+        if (tk) SQ_ATTN_LAUNCH_SS(false, true);
+        else SQ_ATTN_LAUNCH_SS(false, false);
     }
+#undef SQ_ATTN_LAUNCH_SS
 #undef SQ_ATTN_LAUNCH_DK
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SQ_ERR_HIP, "sq_attn: kernel launch failed: %s", hipGetErrorString(e));
