@@ -96,9 +96,9 @@ __device__ __forceinline__ DmaOffsets<D, KT, FP8> dma_lane_offsets(int kst, int 
     return r;
 }
 
-// (TK: the kernel's key-scale layout, unused here; a specialization per kernel keeps the host pass from
-// sharing one across kernels, which it rejects)
-template <int D, int KT, bool FP8, bool TK>
+// (TK, SS: the kernel's key-scale layout and score-scale flag, unused here; a specialization per kernel
+// keeps the host pass from sharing one across kernels, which it rejects)
+template <int D, int KT, bool FP8, bool TK, bool SS>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int kst, int vrow,
                                          int kbase, uint8_t* kl, uint8_t* vl, int w, DmaOffsets<D, KT, FP8> off) {
     using C = Cfg<D, KT, FP8>;
@@ -128,7 +128,8 @@ struct KScales {
     v4f c[Cfg<D, KT, FP8>::NCH];
 };
 
-template <int D, int KT, bool FP8, bool TK>
+// (SS: one specialization per kernel, as for dma_tile)
+template <int D, int KT, bool FP8, bool TK, bool SS>
 __device__ __forceinline__ KScales<D, KT, FP8> load_kscales(__amdgpu_buffer_rsrc_t r, int kbase, int h, int shift) {
     using C = Cfg<D, KT, FP8>;
     KScales<D, KT, FP8> k;
@@ -357,10 +358,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vb), 0, D * vrow, 0x00020000);
     const DmaOffsets<D, KT, FP8> doff = dma_lane_offsets<D, KT, FP8>(kst, vrow, w, l);
     // tile j streams into buffer j % 2 while tile j - 1 is processed from the other one
-    auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8, TK>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, doff); };
+    auto copy = [&](int j, uint8_t* buf) { dma_tile<D, KT, FP8, TK, SS>(krs, vrs, kst, vrow, j * KT, buf, buf + C::KBYTES, w, doff); };
     // the key scales of tile j + 1 are fetched (before its K/V copy) while tile j is
     // processed, so no wait on them ever waits for a copy in flight
-    auto kscales = [&](int j) { return load_kscales<D, KT, FP8, TK>(ksr, j * KT, h, kl_shift); };
+    auto kscales = [&](int j) { return load_kscales<D, KT, FP8, TK, SS>(ksr, j * KT, h, kl_shift); };
     KScales<D, KT, FP8> ks_next = kscales(0);
     copy(0, buf0);
     wait_vm();
