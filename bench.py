@@ -240,7 +240,8 @@ def run_joint(args, torch, sq, gen, timer):
                                "H=24 d=128, bf16 P.V", "B": c.B, "H": c.H, "Sq": c.Sq, "Sk": c.Sk, "prefix": c.prefix,
                    "head_dim": c.D, "kv_tile": c.kv_tile},
         "roofline": {"bound": "mfma", "kernel": "k_attn", "achieved": achieved, "peak": PEAK_TFLOPS_INT8,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS_INT8, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS_INT8,
+                     "traffic": traffic_for("k_attn_joint", ["attn.hip", "device.h", "sq_internal.h"], f_proj),
                      "avg_launch_ms": attn_ms, "flops_per_launch": f_proj},
         "prefix_pass": {"avg_ms": pre_ms, "tflops": f_pre / (pre_ms * 1e-3) / 1e12,
                         "frac": f_pre / (pre_ms * 1e-3) / 1e12 / PEAK_TFLOPS_INT8,
