@@ -104,6 +104,49 @@ def test_paged_prefill_head_dims_and_q_dtypes(D, q_f16):
         check_rows(got, ref, "prefill D %d" % D)
 
 
+def _case_spread(seed, ctx, qlen, Hq, Hk, D=128, bs=16, extra=3, k_spread=6, v_spread=2):
+    """Varlen batch whose cached rows carry a power of two per (key, 32-channel group): 2^U{-k_spread..k_spread}
+    for keys, 2^U{-v_spread..v_spread} for values, so the FP16 group scales of a key (and of neighbouring keys)
+    differ by up to 2^(2 spread); q ~ N(0, 1/64) keeps the scores moderate."""
+    g = np.random.default_rng(seed)
+    lens = np.array(ctx, np.int32) + np.array(qlen, np.int32)
+    pages = [(int(L) + bs - 1) // bs for L in lens]
+    NB = sum(pages) + extra
+
+    def rows(spread):
+        x = g.standard_normal((NB, bs, Hk, D // 32, 32))
+        x *= np.exp2(g.integers(-spread, spread + 1, size=(NB, bs, Hk, D // 32, 1)))
+        return O.q8_quantize(x.reshape(NB, bs, Hk, D).astype(np.float32))
+
+    kc, ks = rows(k_spread)
+    vc, vs = rows(v_spread)
+    perm = g.permutation(NB)
+    bt = np.full((len(lens), max(pages) + 2), -1, np.int32)
+    o = 0
+    for n, p in enumerate(pages):
+        bt[n, :p] = perm[o:o + p]
+        o += p
+    qs = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    q = gen.normal_bf16((int(qs[-1]), 1, Hq, D), g).reshape(-1, Hq, D)
+    q = gen.to_bf16_bits(gen.from_bf16_bits(q) * 0.125)
+    return q, kc, ks, vc, vs, bt, lens, qs
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_paged_prefill_scale_exponents_spread(D):
+    """Group scales whose exponents differ across the groups of a key and across keys (keys by up to 2^12, values
+    by up to 2^4): the keys' FP8 remainders take one power-of-two block scale per (key, group), so a scale applied
+    to the wrong group or key shows here as errors far above the bound. (Values spread much wider would test the
+    f16 rounding of P against the per-element bound rather than the scales.)"""
+    for ctx, qlen, Hq, Hk in (((0, 300), (130, 70), 8, 2), ((77,), (200,), 4, 4)):
+        print("prefill spread D %d" % D, ctx, qlen, Hq, Hk, flush=True)
+        q, kc, ks, vc, vs, bt, lens, qs = _case_spread(6300 + D + sum(ctx) + Hq, ctx, qlen, Hq, Hk, D=D)
+        scale = 1 / math.sqrt(D)
+        ref = O.paged_prefill(q, kc, ks, vc, vs, bt, lens, qs, scale)
+        got = _gpu(q, kc, ks, vc, vs, bt, lens, qs, scale)
+        check_rows(got, ref, "prefill spread D %d" % D)
+
+
 def test_paged_prefill_sinks_and_max_len_bound():
     """Per-head sinks (one dominant, one -inf), and a max_seq_len host bound above every length."""
     Hq, Hk = 8, 2
