@@ -446,7 +446,9 @@ def run_merge(args, torch, sq, gen, timer):
         "config": {"workload": "merge of two attention outputs B=1 Sq=32760 H=40 d=128 FP32", "B": B, "Sq": S, "H": H,
                    "head_dim": D},
         "roofline": {"bound": "hbm", "kernel": "k_lse_merge", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "avg_launch_ms": ms, "bytes_per_launch": nbytes},
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic_for("k_lse_merge_merge", ["merge.hip", "device.h", "sq_internal.h"], nbytes),
+                     "avg_launch_ms": ms, "bytes_per_launch": nbytes},
     }
     return res, line
 
