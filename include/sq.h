@@ -325,11 +325,12 @@ int sq_paged_decode_noalloc(const void* q, sq_dtype q_dtype, int64_t qn, int64_t
  * and attends positions 0 .. L - q_len + j. Caches, scales, block table and softmax_scale
  * as sq_paged_decode (block_size 16, D 64 or 128, Hq / Hk in {1, 2, 4, 8}; scales 2-byte
  * aligned); sinks NULL or FP32 (Hq,). out (num_tokens, Hq, D) at out[t*ot + h*oh + c] in
- * elements of out_dtype (SQ_F32, or SQ_BF16 rounded to nearest even, as sq_attn). Both
- * products run on f16 matrix units with FP32 accumulation: q as f16 after an exact
- * power-of-two rescale per (token, head); key codes widened exactly to f16, each 32-channel
- * dot meeting its FP16 key scale in FP32; each value code * scale held exactly as a pair of
- * f16 (cached values must stay below 65504 in magnitude); P as f16 (relative rounding
+ * elements of out_dtype (SQ_F32, or SQ_BF16 rounded to nearest even, as sq_attn). The
+ * products accumulate in FP32 on the matrix units: q as f16 after an exact power-of-two
+ * rescale per (token, head); each key code * scale as f16(code * scale) plus the remainder in
+ * e4m3 under a power-of-two scale per (key, 32 channels), multiplied by an e4m3 copy of q (a
+ * key off by at most 2^-16 of itself); each value code * scale held exactly as a pair of f16
+ * (cached values must stay below 65504 in magnitude); P as f16 (relative rounding
  * <= 2^-11), the denominator summed from the same f16 P. A block-table entry outside
  * [0, num_blocks) is read as block 0 (no fault; that sequence's rows are then undefined).
  * No workspace; only enqueues. */
