@@ -138,7 +138,7 @@ def test_cfg3_joint_with_q8_prefix_full_size():
 
 
 # ------------------------------------------------------------------------------------------------ paged decode
-def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3, v_sigma=1.0, q_f16=False):
+def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3, v_sigma=1.0, q_f16=False, k_spread=0, v_spread=0):
     g = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int32)
     pages = (lens + bs - 1) // bs
@@ -152,6 +152,9 @@ def _decode_case(lens, Hq, Hk, seed, D=128, bs=16, extra_blocks=3, v_sigma=1.0, 
         o += p
     kx = g.standard_normal(size=(NB, bs, Hk, D), dtype=np.float32)
     vx = g.standard_normal(size=(NB, bs, Hk, D), dtype=np.float32) * np.float32(v_sigma)
+    if k_spread or v_spread:   # a power of two per (slot, head, 32-channel group)
+        kx *= np.repeat(np.exp2(g.integers(-k_spread, k_spread + 1, size=(NB, bs, Hk, D // 32))), 32, axis=-1).astype(np.float32)
+        vx *= np.repeat(np.exp2(g.integers(-v_spread, v_spread + 1, size=(NB, bs, Hk, D // 32))), 32, axis=-1).astype(np.float32)
     kc, ks = _q8(kx)
     vc, vs = _q8(vx)
     if q_f16:   # binary16 queries, spread over f16's range
@@ -209,6 +212,21 @@ def test_paged_decode_small_values(v_sigma):
     ref = O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale)
     got = _gpu_decode(q, kc, ks, vc, vs, bt, lens, scale)
     check_float(got, ref, None, what="decode out sigma %g" % v_sigma)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_paged_decode_scale_exponents_spread(D):
+    """Group scales whose exponents differ across the groups of a slot and across slots (keys by up to 2^12, values
+    by up to 2^4): each group's dot meets its own key scale and each value group its own weight, so a scale taken
+    from the wrong group or slot shows far above the bound."""
+    lens = [1, 17, 300, 1100]
+    print("decode spread D %d" % D, flush=True)
+    q, kc, ks, vc, vs, bt, lens = _decode_case(lens, 8, 2, 3200 + D, D=D, k_spread=6, v_spread=2)
+    q = gen.to_bf16_bits(gen.from_bf16_bits(q) * 0.125)   # moderate scores against the spread keys
+    scale = 1.0 / np.sqrt(float(D))
+    ref = O.paged_decode(q, kc, ks, vc, vs, bt, lens, scale)
+    got = _gpu_decode(q, kc, ks, vc, vs, bt, lens, scale)
+    check_float(got, ref, None, what="decode spread D %d out" % D)
 
 
 def test_paged_decode_block_permutation_is_bit_identical():
