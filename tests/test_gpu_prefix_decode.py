@@ -64,6 +64,30 @@ def test_prefix_merge_parity_ragged(case):
     np.testing.assert_allclose(host(lse), rlse, rtol=0, atol=1e-4)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefix_merge_scale_exponents_spread(D):
+    """Prefix keys and values whose FP16 group scales differ by up to 2^8 across the groups of a token and across
+    tokens: each group's integer dot meets its own key scale and each value its own group scale, so a scale read
+    from the wrong group or token shows far above the bound."""
+    g = np.random.default_rng(2400 + D)
+    B, H, Hk, Sq, P, (ql, qb), kvt = 1, 4, 2, 150, 300, (0, 64), 64
+    qc, qs = _rand_codes(g, B, Sq, H, D, ql, qb, 0.01, 0.02)
+    spread = lambda: np.repeat(np.exp2(g.integers(-4, 5, size=(1, P, Hk, D // 32))), 32, axis=-1).astype(np.float32)
+    kc, ks = _q8(g.standard_normal(size=(1, P, Hk, D), dtype=np.float32) * spread())
+    vc, vs = _q8(g.standard_normal(size=(1, P, Hk, D), dtype=np.float32) * spread())
+    mu = (g.standard_normal(size=(B, Hk, D)) * 0.3).astype(np.float32)
+    out_in = g.standard_normal(size=(B, Sq, H, D)).astype(np.float32)
+    lse_in = (g.standard_normal(size=(B, H, Sq)) * 3 + 5).astype(np.float32)
+    ref, rlse, allow = O.prefix_merge(O.QK(qc, qs, ql, qb), O.Q8Prefix(kc, ks, vc, vs), mu, out_in, lse_in,
+                                      kv_tile=kvt)
+    out, lse = dev(out_in.copy()), dev(lse_in.copy())
+    sq.sq_attn_prefix_lse_merge(sq.QK(dev(qc), dev(qs), ql, qb), _dev_prefix(kc, ks, vc, vs), dev(mu), out, lse, 1.0,
+                                kvt)
+    torch.cuda.synchronize()
+    check_float(host(out), ref, allow, what="merged out, spread D %d" % D)
+    np.testing.assert_allclose(host(lse), rlse, rtol=0, atol=1e-4)
+
+
 def test_prefix_merge_empty_prefix_keeps_projected_pass():
     g = np.random.default_rng(7)
     qc, qs = _rand_codes(g, 1, 40, 2, 128, 0, 64)
