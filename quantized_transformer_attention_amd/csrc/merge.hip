@@ -6,8 +6,11 @@
 //
 // A row (b, i, h) of D floats is D/4 lanes with one 16-byte load of each input per lane;
 // each lane reads its row's two log-sum-exps itself (the same address across the row's
-// lanes is one request). Every load of a wave's rows goes out before the arithmetic.
-// HBM-bound: 12 D bytes per row plus 12 bytes of log-sum-exps.
+// lanes is one request). A workgroup takes RB consecutive queries i of one (b, h), so the
+// log-sum-exps it reads and writes ((B, H, S) arrays) are whole lines; the workgroups go
+// head-fastest, so those running together cover whole stretches of out rows (b, i, 0..H-1).
+// Every load of a wave's rows goes out before the arithmetic. HBM-bound: 12 D bytes per row
+// plus 12 bytes of log-sum-exps.
 #include "device.h"
 #include "sq_internal.h"
 
@@ -18,19 +21,19 @@ constexpr int kRowSteps = 4;
 
 template <int D>
 __global__ __launch_bounds__(256) void k_lse_merge(MergeArgs a) {
-    constexpr int LPR = D / 4, RPW = kWave / LPR;
+    constexpr int LPR = D / 4, RPW = kWave / LPR, RB = 4 * kRowSteps * RPW;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lc = lane % LPR, lr = lane / LPR;
-    const int64_t rows = a.B * a.S * a.H;
-    const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * (kRowSteps * RPW);
-    if (r0 >= rows) return;  // wave-uniform
+    const int64_t nib = (a.S + RB - 1) / RB;
+    const int64_t h = blockIdx.x % a.H, ib = (blockIdx.x / a.H) % nib, b = blockIdx.x / (a.H * nib);
+    const int64_t i0 = ib * RB + w * (kRowSteps * RPW);
+    if (b >= a.B || i0 >= a.S) return;  // wave-uniform
     float4 x[kRowSteps], y[kRowSteps];
     float la[kRowSteps], lb[kRowSteps];
     int64_t obase[kRowSteps], lbase[kRowSteps];
 #pragma unroll
     for (int s = 0; s < kRowSteps; ++s) {
-        int64_t r = r0 + s * RPW + lr;
-        if (r >= rows) r = rows - 1;   // rows past the end recompute the last row and store nothing
-        const int64_t h = r % a.H, i = (r / a.H) % a.S, b = r / (a.H * a.S);
+        int64_t i = i0 + s * RPW + lr;
+        if (i >= a.S) i = a.S - 1;   // queries past the end recompute the last one and store nothing
         obase[s] = b * a.ob + i * a.ot + h * a.oh;
         lbase[s] = b * a.lb + h * a.lh + i;
         x[s] = *reinterpret_cast<const float4*>(a.out + obase[s] + 4 * lc);
@@ -51,8 +54,7 @@ __global__ __launch_bounds__(256) void k_lse_merge(MergeArgs a) {
                             x[s].w * fa + y[s].w * fb);
             l = top + __builtin_log2f(tot);
         }
-        const int64_t r = r0 + s * RPW + lr;
-        if (r < rows) {
+        if (i0 + s * RPW + lr < a.S) {
             *reinterpret_cast<float4*>(a.out + obase[s] + 4 * lc) = o;
             if (lc == 0) a.lse[lbase[s]] = l;
         }
@@ -62,10 +64,11 @@ __global__ __launch_bounds__(256) void k_lse_merge(MergeArgs a) {
 }  // namespace
 
 int launch_lse_merge(const MergeArgs& a, void* stream) {
-    const int64_t rows = a.B * a.S * a.H;
-    if (rows == 0) return SQ_OK;
-    const int64_t per_wg = 4 * kRowSteps * (kWave / (a.D / 4));
-    dim3 grid(static_cast<unsigned>((rows + per_wg - 1) / per_wg));
+    if (a.B * a.S * a.H == 0) return SQ_OK;
+    const int64_t rb = 4 * kRowSteps * (kWave / (a.D / 4));   // queries per workgroup
+    const int64_t wgs = a.B * a.H * ((a.S + rb - 1) / rb);
+    if (wgs >= (int64_t(1) << 31)) return fail(SQ_ERR_UNSUPPORTED, "sq_lse_merge: too many rows (%lld workgroups)", (long long)wgs);
+    dim3 grid(static_cast<unsigned>(wgs));
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.D == 128) SQ_LAUNCH(k_lse_merge<128>, grid, dim3(256), 0, s, a);
     else SQ_LAUNCH(k_lse_merge<64>, grid, dim3(256), 0, s, a);
