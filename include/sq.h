@@ -263,7 +263,9 @@ int sq_attn_prefix_lse_merge(const sq_qk* q, const sq_q8prefix* prefix, const fl
  * (other_lse with qb, qh): the layouts sq_attn writes. A native prefix: k mean of the
  * prefix keys (sq_kmean), prefix keys quantized with it (sq_quant_qk), prefix values to
  * FP8 (sq_quant_v_fp8), the projected keys quantized with the same mean, one sq_attn pass
- * per key set, then this merge. D 64 or 128; out/other rows 16-byte aligned. */
+ * per key set, then this merge. D 64 or 128; out/other rows 16-byte aligned; B H S below
+ * 2^36 (one workgroup per 32 queries of a (b, h) at D 128, 64 at D 64, at most 2^31 of them:
+ * SQ_ERR_UNSUPPORTED beyond). */
 int sq_lse_merge(float* out, int64_t ob, int64_t ot, int64_t oh, float* lse, int64_t lb, int64_t lh, const float* other,
                  int64_t pb, int64_t pt, int64_t ph, const float* other_lse, int64_t qb, int64_t qh, int64_t B, int64_t S,
                  int64_t H, int64_t D, void* stream);
